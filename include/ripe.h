@@ -1,0 +1,217 @@
+/*
+ * ripe.h -- C ABI of the RIPE self-speculative verification library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * A looped (depth-recurrent) language model runs one block of layers R times
+ * per token, so each recurrent layer's KV cache holds R planes, one per loop;
+ * self-speculative decoding drafts with a few loops and verifies a draft
+ * block with all R loops, reading every plane (RIPE abstract, zhuanzhiai.com
+ * paper page, opening sentence).  Three cache layouts are supported:
+ *
+ *   FULL     every plane at every position; depth r reads plane r;
+ *   DEEPEST  only the deepest plane R ("one shared plane"); every depth
+ *            reads plane R;
+ *   RIPE     plane R at every position plus planes 1..R-1 for a window of
+ *            the W most recent committed positions; depth r reads plane r
+ *            inside the window and plane R before it (RIPE abstract,
+ *            sentence introducing RIPE).
+ *
+ * Depths are 1-based; plane R is the deepest.  Several draft groups (draft
+ * blocks of different sequences, or LoopSpec-style branches of one sequence
+ * at different depths) are verified in one call (LoopSpec summary on
+ * rit.work: branches at different recurrent depths in one batched call).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory owned by the caller;
+ *    pointers marked "host" are read (or, for seq_len in ripe_commit,
+ *    updated) before the call returns.  The library allocates nothing and
+ *    keeps no state between calls; calls are asynchronous on `stream`
+ *    (0 = the null stream) and never synchronise the host.
+ *  - Every argument is validated on the host before any HIP call.  On an
+ *    error nothing is launched and no output (device or host) is modified.
+ *  - Device pointers must be 16-byte aligned (workspace: 256-byte aligned).
+ *  - Input values must be finite.
+ */
+#ifndef RIPE_H_
+#define RIPE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RIPE_LAYOUT_FULL = 0,
+  RIPE_LAYOUT_DEEPEST = 1,
+  RIPE_LAYOUT_RIPE = 2
+} ripe_layout_t;
+
+/* Element type shared by the cache, q, kv_new and out. */
+typedef enum { RIPE_F32 = 0, RIPE_BF16 = 1 } ripe_dtype_t;
+
+typedef enum {
+  RIPE_OK = 0,
+  RIPE_EINVAL = -1,        /* malformed argument (null, negative, misaligned) */
+  RIPE_ERANGE = -2,        /* a depth, sequence, length or row index out of range */
+  RIPE_ECAPACITY = -3,     /* commit would grow a sequence past t_max */
+  RIPE_EUNSUPPORTED = -4,  /* well-formed but not supported (head_dim, window width, limits) */
+  RIPE_EWORKSPACE = -5,    /* workspace missing or too small */
+  RIPE_EHIP = -6           /* a HIP launch failed */
+} ripe_status_t;
+
+typedef enum { RIPE_BYTES_CACHE = 0, RIPE_BYTES_WORKSPACE = 1 } ripe_bytes_kind_t;
+
+/*
+ * One recurrent layer's cache (callers allocate one buffer per layer).
+ *
+ *  layout      ripe_layout_t
+ *  dtype       ripe_dtype_t
+ *  R           loops = planes, 1..127
+ *  W           RIPE window in positions, >= 0 (ignored by FULL / DEEPEST).
+ *              With We = min(W, t_max): We must be 0, 8, 16, 24 or a
+ *              multiple of 32.  W = 0 keeps only plane R; W >= t_max keeps
+ *              every plane everywhere.
+ *  batch       sequences B >= 1
+ *  t_max       capacity per sequence, a positive multiple of 32
+ *  n_kv_heads  Hkv >= 1
+ *  head_dim    D, 64 or 128
+ *  n_q_heads   Hq, a multiple of Hkv (query head h reads KV head h / (Hq/Hkv))
+ *  max_rows    upper bound on n_rows of a verify call   (workspace sizing)
+ *  max_groups  upper bound on n_groups of a verify call (workspace sizing)
+ *  split_len   prefix positions per split-K work item: 0 selects the
+ *              library default, otherwise a positive multiple of 32.  The
+ *              split plan of a sequence depends only on this descriptor and
+ *              on that sequence's own groups and length, never on the other
+ *              sequences of the call, so a group's results are bit-identical
+ *              whether it is verified alone or batched.
+ */
+typedef struct ripe_desc {
+  int32_t layout;
+  int32_t dtype;
+  int32_t R;
+  int32_t W;
+  int32_t batch;
+  int32_t t_max;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_q_heads;
+  int32_t max_rows;
+  int32_t max_groups;
+  int32_t split_len;
+} ripe_desc_t;
+
+/*
+ * A draft group: rows [row_start, row_start + n_rows) of q / kv_new / out,
+ * belonging to sequence `seq`, verified at loop depth `depth` (1..R).  Row i
+ * of a group attends to the sequence's committed prefix (planes per layout)
+ * and to rows 0..i of its own group at depth `depth`; it never attends to
+ * another group's rows.  Row ranges of the groups of one call must not
+ * overlap.
+ */
+typedef struct ripe_group {
+  int32_t seq;
+  int32_t depth;
+  int32_t row_start;
+  int32_t n_rows;
+} ripe_group_t;
+
+/*
+ * Byte layout of one recurrent layer's cache (E = 4 for F32, 2 for BF16;
+ * T = t_max; We = min(W, T); BW = min(32, We)).  The K region comes first,
+ * then the V region, with no padding:
+ *
+ *   FULL     K [B][R][Hkv][T][D]            V [B][R][Hkv][T/32][D][32]
+ *   DEEPEST  K [B][Hkv][T][D]               V [B][Hkv][T/32][D][32]
+ *   RIPE     K deep [B][Hkv][T][D]          V deep [B][Hkv][T/32][D][32]
+ *            then K ring [B][R-1][Hkv][We][D], V ring [B][R-1][Hkv][We/BW][D][BW]
+ *
+ * Plane p lives at index p-1.  V is stored transposed in blocks of 32
+ * positions so that each head dimension's 32 values are contiguous.  RIPE
+ * keeps planes 1..R-1 of position j in ring slot j mod We; the deep region
+ * holds plane R of every position.  Hence the cache costs
+ *   FULL    2*B*Hkv*D*E * R*T
+ *   DEEPEST 2*B*Hkv*D*E * T
+ *   RIPE    2*B*Hkv*D*E * (T + We*(R-1))
+ * bytes: one plane plus W*(R-1) window slots per sequence (RIPE abstract,
+ * memory statement).
+ *
+ * kind = RIPE_BYTES_CACHE returns the cache size above; kind =
+ * RIPE_BYTES_WORKSPACE returns a workspace size sufficient for any verify
+ * call within the descriptor's max_rows / max_groups bounds.  Returns a
+ * negative ripe_status_t on an invalid descriptor or kind.
+ */
+int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind);
+
+/*
+ * Verification attention for one recurrent layer (RIPE abstract: the verify
+ * pass reads the planes the layout keeps; LoopSpec summary: branches at
+ * several depths in one batched call).
+ *
+ *  desc          cache descriptor (host)
+ *  cache         device, ripe_layout_bytes(desc, RIPE_BYTES_CACHE) bytes,
+ *                laid out as above
+ *  seq_len       host [batch]: committed prefix length T_b, 0 <= T_b <= t_max
+ *  groups        host [n_groups] (n_groups == 0 is a no-op)
+ *  n_rows        rows of q / kv_new / out (>= every group's row_start+n_rows)
+ *  softmax_scale scores are softmax_scale * <q, k>
+ *  q             device [n_rows][Hq][D]
+ *  kv_new        device [2][R][n_rows][Hkv][D]: K then V of every draft row
+ *                at every depth; a group at depth r reads slice [.][r-1]
+ *  out           device [n_rows][Hq][D]; written for the rows of the groups
+ *  lse           device float [n_rows][Hq], natural-log log-sum-exp of each
+ *                row's visible scores; may be NULL
+ *  plane_sel     device int8 [n_groups][t_max]: plane (1..R) read by group
+ *                g at prefix position j, written for j < T_seq; may be NULL
+ *  workspace     device scratch of workspace_bytes bytes (256-byte aligned;
+ *                ripe_layout_bytes(desc, RIPE_BYTES_WORKSPACE) suffices);
+ *                its contents need no initialisation and are clobbered
+ *  stream        hipStream_t (as void*) the kernels are launched on
+ *
+ * Calls that share a workspace must be ordered on one stream.
+ */
+ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                               const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                               float softmax_scale, const void* q, const void* kv_new, void* out,
+                               float* lse, int8_t* plane_sel, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Commit accepted draft rows (RIPE abstract: the window of recent positions
+ * is kept at full depth, older positions collapse to the deepest plane;
+ * LoopSpec summary: rejected continuations are dropped and decoding resumes
+ * from the confirmed prefix).
+ *
+ * For every sequence b with n_accept[b] > 0, draft rows src_row[b] ..
+ * src_row[b] + n_accept[b] - 1 of kv_new become positions T_b ..
+ * T_b + n_accept[b] - 1, where T_b = seq_len[b]:
+ *   FULL     planes 1..R are written;
+ *   DEEPEST  plane R is written;
+ *   RIPE     plane R is written to the deep region, and planes 1..R-1 of the
+ *            positions that are within the new window (j >= T_b + n - We)
+ *            are written to ring slot j mod We.  A position leaving the
+ *            window needs no copy: its plane R is already in the deep region
+ *            and its ring slot is taken over by the position W later.
+ * Then seq_len[b] += n_accept[b] (host).  n_accept[b] == 0 leaves sequence b
+ * untouched (rollback to the confirmed prefix).
+ *
+ *  desc       cache descriptor (host)
+ *  cache      device, laid out as above (written)
+ *  seq_len    host [batch], in/out; T_b + n_accept[b] <= t_max or RIPE_ECAPACITY
+ *  n_accept   host [batch], >= 0
+ *  src_row    host [batch]; rows src_row[b] + n_accept[b] <= n_rows (ignored
+ *             when n_accept[b] == 0)
+ *  kv_new     device [2][R][n_rows][Hkv][D] (same layout as for verify)
+ *  n_rows     rows of kv_new
+ *  stream     hipStream_t (as void*)
+ */
+ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,
+                          const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
+                          int32_t n_rows, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIPE_H_ */

@@ -50,88 +50,88 @@ def layout_bytes(layout, dtype: str, R: int, W: int, B: int, t_max: int, Hkv: in
     return layout_elements(layout, R, W, B, t_max, Hkv, D) * ELEM_BYTES[dtype]
 
 
-def _to_bytes(x: np.ndarray, dtype: str) -> np.ndarray:
+def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, Hkv: int,
+                  D: int):
+    """Named array views of a flat element buffer: K and V of the main region
+    (FULL planes or the deep plane) and, for RIPE, of the ring.  V views are
+    blocked: [..., n/width, D, width]."""
+    layout = layout_code(layout)
+    T = t_max
+    if layout == FULL:
+        main = (B, R, Hkv, T, D)
+    else:
+        main = (B, Hkv, T, D)
+    We = ring_width(W, T) if layout == RIPE else 0
+    parts = [("main", main, 32)]
+    if We > 0:
+        parts.append(("ring", (B, R - 1, Hkv, We, D), min(32, We)))
+    views = {}
+    off = 0
+    for kind in ("K", "V"):
+        for name, shp, w in parts:
+            n = int(np.prod(shp))
+            flat = buf_elems[off:off + n]
+            if kind == "K":
+                views[(kind, name)] = flat.reshape(shp)
+            else:
+                *lead, nn, dd = shp
+                views[(kind, name)] = flat.reshape(*lead, nn // w, dd, w)
+            off += n
+    assert off == buf_elems.size
+    return views
+
+
+def _bits(x: np.ndarray, dtype: str) -> np.ndarray:
     x32 = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "f32":
-        return x32.reshape(-1).view(np.uint8)
-    bits = x32.reshape(-1).view(np.uint32)
-    finite = ~np.isnan(x32.reshape(-1))
+        return x32.view(np.uint32)
+    bits = x32.view(np.uint32)
+    finite = ~np.isnan(x32)
     if np.any(bits[finite] & 0xFFFF):
         raise ValueError("value not representable in bf16")
-    return (bits >> 16).astype(np.uint16).view(np.uint8)
-
-
-def _from_bytes(buf: np.ndarray, dtype: str, n: int) -> np.ndarray:
-    if dtype == "f32":
-        return buf[: 4 * n].view(np.float32).astype(np.float64)
-    u16 = buf[: 2 * n].view(np.uint16).astype(np.uint32)
-    return (u16 << 16).view(np.float32).astype(np.float64)
-
-
-def _blocked_v(v: np.ndarray, width: int) -> np.ndarray:
-    """[..., n, D] -> [..., n/width, D, width]."""
-    *lead, n, D = v.shape
-    v = v.reshape(*lead, n // width, width, D)
-    return np.swapaxes(v, -1, -2)
-
-
-def _unblocked_v(v: np.ndarray) -> np.ndarray:
-    """[..., n/width, D, width] -> [..., n, D]."""
-    *lead, nb, D, width = v.shape
-    return np.swapaxes(v, -1, -2).reshape(*lead, nb * width, D)
-
-
-def _logical_arrays(cache: LogicalCache):
-    """Dense float64 arrays of what each region holds (NaN where nothing)."""
-    B, R, T, H, D = cache.B, cache.R, cache.t_max, cache.Hkv, cache.D
-    if cache.layout == FULL:
-        K = np.full((B, R, H, T, D), np.nan)
-        V = np.full((B, R, H, T, D), np.nan)
-        for b in range(B):
-            for p in range(1, R + 1):
-                k, v = cache.dense_plane(b, p)
-                K[b, p - 1] = np.moveaxis(k, 0, 1)
-                V[b, p - 1] = np.moveaxis(v, 0, 1)
-        return [(K, V, 32)]
-    deepK = np.full((B, H, T, D), np.nan)
-    deepV = np.full((B, H, T, D), np.nan)
-    for b in range(B):
-        k, v = cache.dense_plane(b, R)
-        deepK[b] = np.moveaxis(k, 0, 1)
-        deepV[b] = np.moveaxis(v, 0, 1)
-    regions = [(deepK, deepV, 32)]
-    if cache.layout == RIPE:
-        We = ring_width(cache.W, T)
-        if We > 0:
-            ringK = np.full((B, R - 1, H, We, D), np.nan)
-            ringV = np.full((B, R - 1, H, We, D), np.nan)
-            filled = np.zeros((B, R - 1, We), dtype=bool)
-            for b in range(B):
-                for p in range(1, R):
-                    for j in cache.held_positions(b, p):
-                        s = j % We
-                        if filled[b, p - 1, s]:
-                            raise ValueError("two held positions share a ring slot")
-                        filled[b, p - 1, s] = True
-                        k, v = cache.get(b, p, j, j + 1)
-                        ringK[b, p - 1, :, s] = k[0]
-                        ringV[b, p - 1, :, s] = v[0]
-            regions.append((ringK, ringV, min(32, We)))
-    return regions
+    return (bits >> 16).astype(np.uint16)
 
 
 def encode(cache: LogicalCache) -> np.ndarray:
     """The cache's bytes in the ABI layout (uint8 array).  Slots the layout
     does not currently hold are filled with a quiet NaN, so a kernel that
     reads them produces NaN."""
-    regions = _logical_arrays(cache)
-    k_parts = [_to_bytes(K, cache.dtype) for K, _, _ in regions]
-    v_parts = [_to_bytes(_blocked_v(V, w), cache.dtype) for _, V, w in regions]
-    out = np.concatenate(k_parts + v_parts)
-    expect = layout_bytes(cache.layout, cache.dtype, cache.R, cache.W, cache.B, cache.t_max,
-                          cache.Hkv, cache.D)
-    assert out.size == expect
-    return out
+    B, R, T, H, D = cache.B, cache.R, cache.t_max, cache.Hkv, cache.D
+    n = layout_elements(cache.layout, R, cache.W, B, T, H, D)
+    if cache.dtype == "f32":
+        buf = np.full(n, 0x7FC00000, dtype=np.uint32)
+    else:
+        buf = np.full(n, 0x7FC0, dtype=np.uint16)
+    views = _region_views(buf, cache.layout, R, cache.W, B, T, H, D)
+    kmain, vmain = views[("K", "main")], views[("V", "main")]
+    main_planes = range(1, R + 1) if cache.layout == FULL else [R]
+    for b in range(B):
+        for p in main_planes:
+            if (b, p) not in cache._dense:
+                continue
+            k, v, held = cache._dense[(b, p)]
+            kt = np.moveaxis(k, 0, 1)          # [H, T, D]
+            vt = np.moveaxis(v, 0, 1)
+            kd = kmain[b, p - 1] if cache.layout == FULL else kmain[b]
+            vd = vmain[b, p - 1] if cache.layout == FULL else vmain[b]
+            kd[:, held] = _bits(kt[:, held], cache.dtype)
+            vblk = _bits(np.swapaxes(vt.reshape(H, T // 32, 32, D), -1, -2), cache.dtype)
+            hb = held.reshape(T // 32, 32)
+            vd[...] = np.where(hb[None, :, None, :], vblk, vd)
+    if cache.layout == RIPE and ("K", "ring") in views:
+        We = ring_width(cache.W, T)
+        BW = min(32, We)
+        kring, vring = views[("K", "ring")], views[("V", "ring")]
+        filled = np.zeros((B, R - 1, We), dtype=bool)
+        for (b, p), store in cache._sparse.items():
+            for j, (k, v) in store.items():
+                s = j % We
+                if filled[b, p - 1, s]:
+                    raise ValueError("two held positions share a ring slot")
+                filled[b, p - 1, s] = True
+                kring[b, p - 1, :, s] = _bits(k, cache.dtype)
+                vring[b, p - 1, :, s // BW, :, s % BW] = _bits(v, cache.dtype)
+    return buf.view(np.uint8)
 
 
 def decode(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: int, Hkv: int,
@@ -139,44 +139,35 @@ def decode(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: i
     """Inverse of ``encode`` for the positions the layout holds given the
     committed lengths ``seq_len``."""
     layout = layout_code(layout)
-    E = ELEM_BYTES[dtype]
     cache = LogicalCache(layout, dtype, R, W, B, t_max, Hkv, D)
-    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    raw = np.ascontiguousarray(buf, dtype=np.uint8)
+    elems = raw.view(np.uint32 if dtype == "f32" else np.uint16)
+    views = _region_views(elems, layout, R, W, B, t_max, Hkv, D)
+
+    def val(x):
+        if dtype == "f32":
+            return np.ascontiguousarray(x).view(np.float32).astype(np.float64)
+        return (np.asarray(x, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
     T = t_max
-    We = ring_width(W, T) if layout == RIPE else 0
-    if layout == FULL:
-        shapes = [((B, R, Hkv, T, D), 32)]
-    else:
-        shapes = [((B, Hkv, T, D), 32)]
-        if We > 0:
-            shapes.append(((B, R - 1, Hkv, We, D), min(32, We)))
-    arrays_k, arrays_v = [], []
-    off = 0
-    for shp, _ in shapes:
-        n = int(np.prod(shp))
-        arrays_k.append(_from_bytes(buf[off:off + n * E], dtype, n).reshape(shp))
-        off += n * E
-    for shp, w in shapes:
-        n = int(np.prod(shp))
-        *lead, nn, dd = shp
-        blocked = _from_bytes(buf[off:off + n * E], dtype, n).reshape(*lead, nn // w, dd, w)
-        arrays_v.append(_unblocked_v(blocked))
-        off += n * E
+    kmain, vmain = views[("K", "main")], views[("V", "main")]
     for b in range(B):
         Tb = int(seq_len[b])
         cache.seq_len[b] = Tb
-        if layout == FULL:
-            K, V = arrays_k[0], arrays_v[0]
-            for p in range(1, R + 1):
-                cache.put_range(b, p, 0, np.moveaxis(K[b, p - 1, :, :Tb], 0, 1),
-                                np.moveaxis(V[b, p - 1, :, :Tb], 0, 1))
-            continue
-        K, V = arrays_k[0], arrays_v[0]
-        cache.put_range(b, R, 0, np.moveaxis(K[b, :, :Tb], 0, 1), np.moveaxis(V[b, :, :Tb], 0, 1))
-        if layout == RIPE and We > 0:
-            rK, rV = arrays_k[1], arrays_v[1]
+        planes = range(1, R + 1) if layout == FULL else [R]
+        for p in planes:
+            kd = kmain[b, p - 1] if layout == FULL else kmain[b]          # [H, T, D]
+            vd = vmain[b, p - 1] if layout == FULL else vmain[b]          # [H, T/32, D, 32]
+            k = np.moveaxis(val(kd[:, :Tb]), 0, 1)
+            v = np.moveaxis(np.swapaxes(val(vd), -1, -2).reshape(Hkv, T, D)[:, :Tb], 0, 1)
+            cache.put_range(b, p, 0, k, v)
+        if layout == RIPE and ("K", "ring") in views:
+            We = ring_width(W, T)
+            BW = min(32, We)
+            kring, vring = views[("K", "ring")], views[("V", "ring")]
             for p in range(1, R):
                 for j in range(max(0, Tb - W), Tb):
                     s = j % We
-                    cache.put(b, p, j, rK[b, p - 1, :, s], rV[b, p - 1, :, s])
+                    cache.put(b, p, j, val(kring[b, p - 1, :, s]),
+                              val(vring[b, p - 1, :, s // BW, :, s % BW]))
     return cache

@@ -1,0 +1,151 @@
+"""Thin ctypes binding of libripe.so (the C ABI in include/ripe.h).
+
+Argument marshalling only: device buffers are torch tensors on the GPU (or
+raw device addresses), host arrays are NumPy / Python sequences, and every
+step of the computation runs in the library's HIP kernels.  If the library
+is missing, importing this module raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("RIPE_LIB", os.path.join(_PKG, "libripe.so"))
+
+RIPE_LAYOUT_FULL, RIPE_LAYOUT_DEEPEST, RIPE_LAYOUT_RIPE = 0, 1, 2
+RIPE_F32, RIPE_BF16 = 0, 1
+RIPE_BYTES_CACHE, RIPE_BYTES_WORKSPACE = 0, 1
+STATUS = {0: "RIPE_OK", -1: "RIPE_EINVAL", -2: "RIPE_ERANGE", -3: "RIPE_ECAPACITY",
+          -4: "RIPE_EUNSUPPORTED", -5: "RIPE_EWORKSPACE", -6: "RIPE_EHIP"}
+LAYOUTS = {"full": RIPE_LAYOUT_FULL, "deepest": RIPE_LAYOUT_DEEPEST, "ripe": RIPE_LAYOUT_RIPE}
+DTYPES = {"f32": RIPE_F32, "bf16": RIPE_BF16}
+
+
+class RipeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class ripe_desc_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layout", "dtype", "R", "W", "batch", "t_max", "n_kv_heads", "head_dim", "n_q_heads",
+        "max_rows", "max_groups", "split_len")]
+
+
+class ripe_group_t(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("depth", ctypes.c_int32), ("row_start", ctypes.c_int32),
+                ("n_rows", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libripe.so not built ({LIB_PATH}); run "
+                          "python -m self_speculative_verify_ripe_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.ripe_layout_bytes.argtypes = [ctypes.POINTER(ripe_desc_t), ctypes.c_int32]
+    lib.ripe_layout_bytes.restype = ctypes.c_int64
+    lib.ripe_verify_attn.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ripe_verify_attn.restype = ctypes.c_int
+    lib.ripe_commit.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), P,
+                                ctypes.c_int32, P]
+    lib.ripe_commit.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def make_desc(layout, dtype, R, W, batch, t_max, n_kv_heads, head_dim, n_q_heads,
+              max_rows=0, max_groups=0, split_len=0) -> ripe_desc_t:
+    layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return ripe_desc_t(layout, dtype, R, W, batch, t_max, n_kv_heads, head_dim, n_q_heads,
+                       max_rows, max_groups, split_len)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _i32(a, n: Optional[int] = None):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if n is not None and arr.size != n:
+        raise ValueError(f"expected {n} entries, got {arr.size}")
+    return arr
+
+
+def _groups(groups: Iterable) -> ctypes.Array:
+    gl = list(groups)
+    arr = (ripe_group_t * max(len(gl), 1))()
+    for i, g in enumerate(gl):
+        if isinstance(g, tuple):
+            seq, depth, row_start, n_rows = g
+        else:
+            seq, depth, row_start, n_rows = g.seq, g.depth, g.row_start, g.n_rows
+        arr[i] = ripe_group_t(int(seq), int(depth), int(row_start), int(n_rows))
+    return arr, len(gl)
+
+
+def ripe_layout_bytes(desc: ripe_desc_t, kind: int = RIPE_BYTES_CACHE) -> int:
+    n = int(lib.ripe_layout_bytes(ctypes.byref(desc), int(kind)))
+    if n < 0:
+        raise RipeError(n, "ripe_layout_bytes")
+    return n
+
+
+def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
+                     n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
+                     workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """Launch verification attention (asynchronous on ``stream``)."""
+    sl = _i32(seq_len, desc.batch)
+    garr, ng = _groups(groups)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ripe_verify_attn(ctypes.byref(desc), _ptr(cache),
+                              sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr, ng,
+                              int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
+                              _ptr(lse), _ptr(plane_sel), _ptr(workspace), int(workspace_bytes),
+                              _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_verify_attn")
+
+
+def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],
+                src_row: Sequence[int], kv_new, n_rows: int, stream=None) -> np.ndarray:
+    """Commit accepted rows; returns the updated committed lengths (an int32
+    array; ``seq_len`` is updated in place when it is an int32 NumPy array)."""
+    inplace = isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32 and \
+        seq_len.flags["C_CONTIGUOUS"]
+    sl = seq_len if inplace else _i32(seq_len, desc.batch).copy()
+    na = _i32(n_accept, desc.batch)
+    sr = _i32(src_row, desc.batch)
+    st = lib.ripe_commit(ctypes.byref(desc), _ptr(cache),
+                         sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         na.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         sr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(kv_new),
+                         int(n_rows), _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_commit")
+    return sl

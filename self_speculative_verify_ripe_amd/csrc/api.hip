@@ -1,0 +1,361 @@
+// api.hip -- host side of the C ABI declared in include/ripe.h: argument
+// validation, the memory model, the split-K work plan and kernel launches.
+//
+// Every check runs before the first HIP call, so an invalid call launches
+// nothing and modifies nothing.  The plan of a call is packed into the kernel
+// arguments (no host-to-device copies); calls with more than 64 sequences or
+// 128 groups are cut into several launches that reuse the workspace in
+// stream order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "plan.h"
+#include "ripe.h"
+
+namespace ripe {
+hipError_t launch_verify(const VerifyParams& p, int dtype, int D, int NB, hipStream_t stream);
+hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream);
+}  // namespace ripe
+
+namespace {
+
+using namespace ripe;
+
+constexpr int64_t kMaxBytes = int64_t(1) << 50;   // sanity bound on any buffer size
+constexpr int64_t kMaxItems = int64_t(1) << 30;   // commit work items per launch
+constexpr int kMaxCQ = 32;                        // query columns per verify work-group
+
+int elem_bytes(int dtype) { return dtype == RIPE_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ring_width(const ripe_desc_t& d) {
+  if (d.layout != RIPE_LAYOUT_RIPE) return 0;
+  return d.W < d.t_max ? d.W : d.t_max;
+}
+
+int split_len(const ripe_desc_t& d) {
+  if (d.split_len > 0) return d.split_len;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  // Few query columns per KV head -> small partials -> shorter splits for
+  // more parallelism; many columns -> longer splits to amortise the partial.
+  return G >= 4 ? 1024 : (G >= 2 ? 512 : 256);
+}
+
+// Elements of one region (K or V) of the cache, or -1 on overflow.
+int64_t region_elems(const ripe_desc_t& d) {
+  const long double per_seq =
+      d.layout == RIPE_LAYOUT_FULL ? (long double)d.R * d.t_max
+      : d.layout == RIPE_LAYOUT_DEEPEST ? (long double)d.t_max
+                                        : (long double)d.t_max + (long double)ring_width(d) * (d.R - 1);
+  const long double n = per_seq * d.batch * d.n_kv_heads * d.head_dim;
+  if (n * 2 * elem_bytes(d.dtype) > (long double)kMaxBytes) return -1;
+  return int64_t(n);
+}
+
+ripe_status_t check_desc(const ripe_desc_t* d) {
+  if (d == nullptr) return RIPE_EINVAL;
+  if (d->layout < RIPE_LAYOUT_FULL || d->layout > RIPE_LAYOUT_RIPE) return RIPE_EINVAL;
+  if (d->dtype != RIPE_F32 && d->dtype != RIPE_BF16) return RIPE_EINVAL;
+  if (d->R < 1 || d->W < 0 || d->batch < 1 || d->t_max < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->n_q_heads < 1 || d->max_rows < 0 || d->max_groups < 0 || d->split_len < 0)
+    return RIPE_EINVAL;
+  if (d->n_q_heads % d->n_kv_heads != 0) return RIPE_EINVAL;
+  if (d->R > 127 || d->batch > 65535) return RIPE_EUNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return RIPE_EUNSUPPORTED;
+  if (d->t_max % 32 != 0 || d->split_len % 32 != 0) return RIPE_EUNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > 65535) return RIPE_EUNSUPPORTED;
+  const int We = ring_width(*d);
+  if (!(We == 0 || (We < 32 && We % 8 == 0) || We % 32 == 0)) return RIPE_EUNSUPPORTED;
+  if (region_elems(*d) < 0) return RIPE_EUNSUPPORTED;
+  return RIPE_OK;
+}
+
+// Upper bound on split partial slots of any verify call within the
+// descriptor's max_rows / max_groups bounds.
+int64_t workspace_bound(const ripe_desc_t& d) {
+  const int64_t S = split_len(d);
+  const int64_t G = d.n_q_heads / d.n_kv_heads;
+  const int64_t We = ring_width(d);
+  const int64_t groups = std::max<int64_t>(d.max_groups, 1);
+  const int64_t rows = std::max<int64_t>(d.max_rows, groups);
+  const int64_t nseq = std::min<int64_t>(d.batch, groups);
+  const int64_t tchunks = (int64_t(d.t_max) + S - 1) / S;
+  int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tchunks;
+  if (d.layout == RIPE_LAYOUT_RIPE) per_seq += std::min<int64_t>(groups, d.R - 1) * ((We + S - 1) / S);
+  per_seq += groups + (rows + S - 1) / S;
+  const int64_t col_chunks = (rows * G + 15) / 16 + nseq;
+  const long double slots = (long double)d.n_kv_heads * col_chunks * per_seq;
+  const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4;
+  if (bytes > (long double)kMaxBytes) return -1;
+  return int64_t(bytes) + 256;
+}
+
+struct LaunchPlan {
+  VerifyParams p;
+  int NB;
+  int64_t ws_bytes;
+};
+
+}  // namespace
+
+extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
+  const ripe_status_t st = check_desc(desc);
+  if (st != RIPE_OK) return st;
+  if (kind == RIPE_BYTES_CACHE) return 2 * region_elems(*desc) * elem_bytes(desc->dtype);
+  if (kind == RIPE_BYTES_WORKSPACE) {
+    const int64_t b = workspace_bound(*desc);
+    return b < 0 ? int64_t(RIPE_EUNSUPPORTED) : b;
+  }
+  return RIPE_EINVAL;
+}
+
+extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                          const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                                          float softmax_scale, const void* q, const void* kv_new, void* out,
+                                          float* lse, int8_t* plane_sel, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  ripe_status_t st = check_desc(desc);
+  if (st != RIPE_OK) return st;
+  const ripe_desc_t& d = *desc;
+  if (n_groups < 0) return RIPE_EINVAL;
+  if (n_groups == 0) return RIPE_OK;
+  if (groups == nullptr || seq_len == nullptr || n_rows < 1) return RIPE_EINVAL;
+  if (n_groups > 65535) return RIPE_EUNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return RIPE_EINVAL;
+  if (cache == nullptr || q == nullptr || kv_new == nullptr || out == nullptr) return RIPE_EINVAL;
+  if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(kv_new, 16) || !aligned(out, 16)) return RIPE_EINVAL;
+  if ((lse && !aligned(lse, 4)) || (plane_sel && !aligned(plane_sel, 16))) return RIPE_EINVAL;
+  if (workspace && !aligned(workspace, 256)) return RIPE_EINVAL;
+  for (int b = 0; b < d.batch; ++b)
+    if (seq_len[b] < 0 || seq_len[b] > d.t_max) return RIPE_ERANGE;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  std::vector<std::pair<int, int>> spans;  // (row_start, n_rows) for the overlap check
+  spans.reserve(n_groups);
+  for (int i = 0; i < n_groups; ++i) {
+    const ripe_group_t& g = groups[i];
+    if (g.n_rows < 1) return RIPE_EINVAL;
+    if (g.seq < 0 || g.seq >= d.batch || g.depth < 1 || g.depth > d.R || g.row_start < 0 ||
+        int64_t(g.row_start) + g.n_rows > n_rows)
+      return RIPE_ERANGE;
+    if (g.n_rows > 65535) return RIPE_EUNSUPPORTED;
+    spans.emplace_back(g.row_start, g.n_rows);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i - 1].first + spans[i - 1].second > spans[i].first) return RIPE_EINVAL;
+
+  // groups of each sequence, in the caller's order
+  std::vector<std::vector<int>> by_seq(d.batch);
+  for (int i = 0; i < n_groups; ++i) by_seq[groups[i].seq].push_back(i);
+  for (int b = 0; b < d.batch; ++b) {
+    if (by_seq[b].size() > size_t(kMaxGroups)) return RIPE_EUNSUPPORTED;
+    int64_t nq = 0;
+    for (int i : by_seq[b]) nq += int64_t(groups[i].n_rows) * G;
+    if (nq > 65535) return RIPE_EUNSUPPORTED;
+  }
+
+  const int D = d.head_dim;
+  const int We = ring_width(d);
+  const int S = split_len(d);
+  const size_t E = elem_bytes(d.dtype);
+  const int64_t reg = region_elems(d);
+  const char* cache_k = static_cast<const char*>(cache);
+  const char* cache_v = cache_k + size_t(reg) * E;
+
+  std::vector<LaunchPlan> plans;
+  int b = 0;
+  while (b < d.batch) {
+    LaunchPlan lp;
+    std::memset(&lp.p, 0, sizeof(lp.p));
+    VerifyParams& p = lp.p;
+    p.cache_k = cache_k;
+    p.cache_v = cache_v;
+    p.q = q;
+    p.kv_new = kv_new;
+    p.out = out;
+    p.lse = lse;
+    p.plane_sel = plane_sel;
+    p.ws = static_cast<float*>(workspace);
+    p.ring_off = uint64_t(d.batch) * d.n_kv_heads * uint64_t(d.t_max) * D;
+    p.layout = d.layout;
+    p.R = d.R;
+    p.We = We;
+    p.BW = We < 32 ? We : 32;
+    p.t_max = d.t_max;
+    p.H = d.n_kv_heads;
+    p.Hq = d.n_q_heads;
+    p.G = G;
+    p.n_rows = n_rows;
+    p.S = S;
+    p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
+    int n_seq = 0, n_grp = 0;
+    bool wide = false;
+    for (; b < d.batch; ++b) {
+      const int cnt = int(by_seq[b].size());
+      if (cnt == 0) continue;
+      if (n_seq == kMaxSeq || n_grp + cnt > kMaxGroups) break;
+      SeqRec& sr = p.seq[n_seq];
+      sr.T = seq_len[b];
+      sr.b = uint16_t(b);
+      sr.g_begin = uint8_t(n_grp);
+      sr.g_count = uint8_t(cnt);
+      int nq = 0;
+      for (int i : by_seq[b]) {
+        GroupRec& gr = p.grp[n_grp];
+        gr.row_start = groups[i].row_start;
+        gr.n_rows = uint16_t(groups[i].n_rows);
+        gr.depth = uint8_t(groups[i].depth);
+        gr.seq = uint8_t(n_seq);
+        p.gorig[n_grp] = uint16_t(i);
+        nq += groups[i].n_rows * G;
+        ++n_grp;
+      }
+      sr.nq = uint16_t(nq);
+      wide |= nq > 16;
+      ++n_seq;
+    }
+    if (n_seq == 0) break;
+    p.n_seq = n_seq;
+    p.n_grp = n_grp;
+    lp.NB = wide ? 2 : 1;
+    const int CQ = 16 * lp.NB;
+    int64_t wg = 0, parts = 0, mwg = 0;
+    for (int s = 0; s < n_seq; ++s) {
+      SeqRec& sr = p.seq[s];
+      int64_t n_pre = 0, n_split = 0;
+      enumerate_segments(d.layout, d.R, We, sr.T, p.grp, sr.g_begin, sr.g_count, [&](const Seg& sg) {
+        const int64_t nch = (int64_t(sg.len) + S - 1) / S;
+        if (sg.kind == kSegPlane) n_pre += nch;
+        n_split += nch;
+        return false;
+      });
+      const int n_cc = (sr.nq + CQ - 1) / CQ;
+      sr.n_cc = uint16_t(n_cc);
+      sr.n_pre = int32_t(n_pre);
+      sr.n_split = int32_t(n_split);
+      sr.wg0 = int32_t(wg);
+      sr.part0 = int32_t(parts);
+      sr.mwg0 = int32_t(mwg);
+      wg += n_split * d.n_kv_heads * n_cc;
+      parts += n_split * d.n_kv_heads * n_cc;
+      mwg += int64_t(d.n_kv_heads) * n_cc;
+      if (wg > INT32_MAX || parts > INT32_MAX) return RIPE_EUNSUPPORTED;
+    }
+    p.n_wg = int32_t(wg);
+    p.n_mwg = int32_t(mwg);
+    lp.ws_bytes = parts * CQ * (D + 2) * 4;
+    plans.push_back(lp);
+  }
+  for (const LaunchPlan& lp : plans) {
+    if (lp.ws_bytes > 0 && (workspace == nullptr || size_t(lp.ws_bytes) > workspace_bytes))
+      return RIPE_EWORKSPACE;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (const LaunchPlan& lp : plans) {
+    if (launch_verify(lp.p, d.dtype, D, lp.NB, hs) != hipSuccess) return RIPE_EHIP;
+  }
+  return RIPE_OK;
+}
+
+extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,
+                                     const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
+                                     int32_t n_rows, void* stream) {
+  ripe_status_t st = check_desc(desc);
+  if (st != RIPE_OK) return st;
+  const ripe_desc_t& d = *desc;
+  if (seq_len == nullptr || n_accept == nullptr || src_row == nullptr || n_rows < 0) return RIPE_EINVAL;
+  bool any = false;
+  for (int b = 0; b < d.batch; ++b) {
+    if (seq_len[b] < 0 || seq_len[b] > d.t_max) return RIPE_ERANGE;
+    const int n = n_accept[b];
+    if (n < 0) return RIPE_EINVAL;
+    if (n == 0) continue;
+    any = true;
+    if (src_row[b] < 0 || int64_t(src_row[b]) + n > n_rows) return RIPE_ERANGE;
+    if (int64_t(seq_len[b]) + n > d.t_max) return RIPE_ECAPACITY;
+  }
+  if (!any) return RIPE_OK;
+  if (cache == nullptr || kv_new == nullptr || !aligned(cache, 16) || !aligned(kv_new, 16)) return RIPE_EINVAL;
+
+  const int D = d.head_dim;
+  const int We = ring_width(d);
+  const size_t E = elem_bytes(d.dtype);
+  const int64_t reg = region_elems(d);
+  const int64_t per_row_plane = int64_t(d.n_kv_heads) * (D / 8);  // items per (row, plane)
+
+  struct Job {
+    int b, j0, src0, n, plane_lo, n_planes;
+  };
+  std::vector<Job> jobs;
+  auto add = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes) {
+    // cut rows so that no job exceeds the per-launch item budget
+    const int64_t per_row = per_row_plane * n_planes;
+    const int max_rows = int(std::max<int64_t>(1, kMaxItems / per_row));
+    for (int r0 = 0; r0 < n; r0 += max_rows) {
+      const int cnt = std::min(max_rows, n - r0);
+      jobs.push_back(Job{b, j0 + r0, src0 + r0, cnt, plane_lo, n_planes});
+    }
+  };
+  for (int b = 0; b < d.batch; ++b) {
+    const int n = n_accept[b];
+    if (n == 0) continue;
+    const int T = seq_len[b];
+    const int s = src_row[b];
+    if (d.layout == RIPE_LAYOUT_FULL) {
+      add(b, T, s, n, 1, d.R);
+    } else {
+      add(b, T, s, n, d.R, 1);
+      if (d.layout == RIPE_LAYOUT_RIPE && We > 0 && d.R > 1) {
+        const int k0 = n > We ? n - We : 0;  // rows that end inside the window
+        add(b, T + k0, s + k0, n - k0, 1, d.R - 1);
+      }
+    }
+  }
+  std::vector<CommitParams> launches;
+  size_t i = 0;
+  while (i < jobs.size()) {
+    CommitParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.cache_k = cache;
+    p.cache_v = static_cast<char*>(cache) + size_t(reg) * E;
+    p.kv_new = kv_new;
+    p.ring_off = uint64_t(d.batch) * d.n_kv_heads * uint64_t(d.t_max) * D;
+    p.layout = d.layout;
+    p.R = d.R;
+    p.We = We;
+    p.BW = We < 32 ? We : 32;
+    p.t_max = d.t_max;
+    p.H = d.n_kv_heads;
+    p.n_rows = n_rows;
+    int64_t items = 0;
+    int nj = 0;
+    for (; i < jobs.size() && nj < kMaxJobs; ++i) {
+      const Job& jb = jobs[i];
+      const int64_t cnt = int64_t(jb.n) * jb.n_planes * per_row_plane;
+      if (nj > 0 && items + cnt > kMaxItems) break;
+      CommitJob& cj = p.job[nj++];
+      cj.item0 = int32_t(items);
+      cj.j0 = jb.j0;
+      cj.src0 = jb.src0;
+      cj.n_rows = jb.n;
+      cj.b = uint16_t(jb.b);
+      cj.plane_lo = uint8_t(jb.plane_lo);
+      cj.n_planes = uint8_t(jb.n_planes);
+      items += cnt;
+    }
+    p.n_jobs = nj;
+    p.n_items = int32_t(items);
+    launches.push_back(p);
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (const CommitParams& p : launches)
+    if (launch_commit(p, d.dtype, D, hs) != hipSuccess) return RIPE_EHIP;
+  for (int b = 0; b < d.batch; ++b) seq_len[b] += n_accept[b];
+  return RIPE_OK;
+}

@@ -1,0 +1,149 @@
+// plan.h -- work plan shared by the host planner and the gfx950 kernels.
+//
+// A verify call is split, per sequence, into segments that each read one
+// source of keys and values:
+//   kind 0  a prefix plane read in position order (FULL: plane r of each
+//           distinct depth; DEEPEST: plane R; RIPE: the deep region, plane R,
+//           over [0, T - Wb), or over [0, T) when a group sits at depth R);
+//   kind 1  a RIPE window ring for each distinct depth r < R, read in ring
+//           slot order (slot s holds the one window position j = s mod We);
+//   kind 2  one group's own draft rows at its depth (causal within the group).
+// Segments are cut into chunks of at most S positions; a chunk is one split-K
+// work item of one work-group.  The plan of a sequence depends only on the
+// descriptor, its committed length and its own groups, so a group's result is
+// bit-identical whether it is verified alone or batched with other sequences.
+// Groups of one sequence share its prefix chunks; a chunk that does not apply
+// to a group is masked for that group's query columns, which leaves its
+// running softmax state bit-identical (factor 1, zero added).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define RIPE_HD __host__ __device__
+#else
+#define RIPE_HD
+#endif
+
+namespace ripe {
+
+constexpr int kStep = 32;        // key positions per wavefront step
+constexpr int kWaves = 4;        // wavefronts per verify work-group
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSeq = 64;      // sequences per launch
+constexpr int kMaxGroups = 128;  // groups per launch
+constexpr int kMaxJobs = 128;    // commit jobs per launch
+
+enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
+
+struct SeqRec {        // one sequence of a launch (32 bytes)
+  int32_t T;           // committed prefix length
+  int32_t wg0;         // first verify work-group
+  int32_t part0;       // first split partial slot
+  int32_t mwg0;        // first merge work-group
+  int32_t n_pre;       // chunks of kind-0 segments
+  int32_t n_split;     // chunks of all segments
+  uint16_t b;          // sequence index within the cache
+  uint16_t n_cc;       // query-column chunks
+  uint8_t g_begin;     // first group record of this sequence
+  uint8_t g_count;     // its number of groups
+  uint16_t nq;         // query columns = sum(rows) * (Hq / Hkv)
+};
+
+struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
+  int32_t row_start;
+  uint16_t n_rows;
+  uint8_t depth;
+  uint8_t seq;         // launch-local sequence index
+};
+
+struct Seg {
+  int kind;
+  int depth;  // plane read (kind 0), depth r (kinds 1 and 2)
+  int gidx;   // group record (kind 2)
+  int len;    // positions (kind 0), slots (kind 1) or rows (kind 2)
+};
+
+struct VerifyParams {
+  const void* cache_k;   // K region of the cache
+  const void* cache_v;   // V region of the cache
+  const void* q;
+  const void* kv_new;
+  void* out;
+  float* lse;
+  int8_t* plane_sel;
+  float* ws;
+  uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
+  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, S, n_seq, n_wg, n_mwg, n_grp;
+  float scale_log2;      // softmax scale * log2(e)
+  SeqRec seq[kMaxSeq];
+  GroupRec grp[kMaxGroups];
+  uint16_t gorig[kMaxGroups];  // index of each group in the caller's array
+};
+
+struct CommitJob {     // rows of one sequence written to one region (20 bytes)
+  int32_t item0;       // first work item
+  int32_t j0;          // destination position of the job's first row
+  int32_t src0;        // kv_new row of the job's first row
+  int32_t n_rows;
+  uint16_t b;
+  uint8_t plane_lo;    // first plane written (1-based)
+  uint8_t n_planes;
+};
+
+struct CommitParams {
+  void* cache_k;
+  void* cache_v;
+  const void* kv_new;
+  uint64_t ring_off;
+  int32_t layout, R, We, BW, t_max, H, n_rows, n_jobs, n_items;
+  CommitJob job[kMaxJobs];  // a RIPE job with plane_lo < R writes the ring
+};
+
+RIPE_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Visit the segments of one sequence in canonical order (kind 0, then kind 1,
+// then kind 2); `visit` returns true to stop.  Distinct depths are visited in
+// ascending order.
+template <class Visit>
+RIPE_HD inline void enumerate_segments(int layout, int R, int We, int T, const GroupRec* g, int g_begin,
+                                       int g_count, Visit&& visit) {
+  const int Wb = We < T ? We : T;
+  bool anyR = false;
+  for (int i = 0; i < g_count; ++i) anyR |= (g[g_begin + i].depth == R);
+  if (layout == 0) {  // FULL: one plane segment per distinct depth
+    int cur = 0;
+    while (T > 0) {
+      int nxt = 1 << 30;
+      for (int i = 0; i < g_count; ++i) {
+        const int d = g[g_begin + i].depth;
+        if (d > cur && d < nxt) nxt = d;
+      }
+      if (nxt == (1 << 30)) break;
+      if (visit(Seg{kSegPlane, nxt, -1, T})) return;
+      cur = nxt;
+    }
+  } else if (layout == 1) {  // DEEPEST
+    if (T > 0 && visit(Seg{kSegPlane, R, -1, T})) return;
+  } else {  // RIPE
+    const int deep = anyR ? T : T - Wb;
+    if (deep > 0 && visit(Seg{kSegPlane, R, -1, deep})) return;
+    int cur = 0;
+    while (Wb > 0) {
+      int nxt = 1 << 30;
+      for (int i = 0; i < g_count; ++i) {
+        const int d = g[g_begin + i].depth;
+        if (d > cur && d < R && d < nxt) nxt = d;
+      }
+      if (nxt == (1 << 30)) break;
+      if (visit(Seg{kSegRing, nxt, -1, Wb})) return;
+      cur = nxt;
+    }
+  }
+  for (int i = 0; i < g_count; ++i) {
+    const GroupRec& gr = g[g_begin + i];
+    if (visit(Seg{kSegDraft, gr.depth, g_begin + i, gr.n_rows})) return;
+  }
+}
+
+}  // namespace ripe

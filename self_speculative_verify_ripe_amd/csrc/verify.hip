@@ -1,0 +1,647 @@
+// verify.hip -- RIPE verification attention kernels for gfx950 (CDNA4).
+//
+// What is computed (RIPE abstract, zhuanzhiai.com paper page; LoopSpec
+// summary, rit.work): for every draft group g (sequence b, depth r, rows
+// i < k) and query head h, softmax attention of q[row, h] over
+//   * the committed prefix j < T_b, each position read from the plane its
+//     layout selects (FULL: r; DEEPEST: R; RIPE: r inside the window of the
+//     last W positions, R before it), and
+//   * the group's own draft rows 0..i at depth r,
+// with KV head h / (Hq / Hkv).
+//
+// How (split-K / flash-decoding):
+//   verify_partial  one work-group (4 wavefronts) per (sequence, KV head,
+//                   query-column chunk, chunk of <= S key positions of one
+//                   segment).  Each wavefront streams 32-position steps
+//                   straight from HBM into VGPRs in MFMA operand order:
+//                   K rows (row-major [pos][D]) feed the A operand of
+//                   S^T = K Q^T, and the V blocks (stored transposed,
+//                   [D][32] per 32 positions) feed the A operand of
+//                   O^T += V^T P^T, so no LDS staging or shuffles are needed
+//                   on the hot loop.  The next step's K/V loads are issued
+//                   before the current step's MFMAs.  Online softmax in the
+//                   log2 domain with one max reduction per step.  The four
+//                   wavefronts' (m, l, O) are merged through LDS and written
+//                   as one fp32 partial per work-item.
+//   verify_merge    one work-group per (sequence, KV head, column chunk)
+//                   merges the partials in split order, normalises, writes
+//                   out (storage dtype, round-to-nearest-even) and the
+//                   natural-log LSE; extra work-groups write plane_sel.
+//
+// MFMA shapes: bf16 v_mfma_f32_16x16x32_bf16 (8 bf16 per lane per operand);
+// fp32 v_mfma_f32_16x16x4_f32 (no reduced-precision path).  For the
+// 16x16 MFMAs, lane l holds A row / B column l%16 and the k-slots of lane
+// group l/16; the accumulator lane l holds column l%16, rows 4*(l/16)+j.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "plan.h"
+
+namespace ripe {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Op;
+
+// bf16: one 16-byte chunk = 8 elements = one MFMA k-block of 32.
+template <>
+struct Op<__bf16> {
+  static constexpr int VEC = 8;
+  static constexpr int VCH = 1;  // 16-byte chunks per lane per V fragment
+  typedef bf16x8 P;              // probability fragment (B operand of P.V)
+  __device__ static inline floatx4 mma_k(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline floatx4 mma_v(const u32x4 (&v)[VCH], const P& p, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[0]), p, c, 0, 0, 0);
+  }
+  // round p to the MFMA operand precision; the softmax denominator keeps the
+  // unrounded value so that the log-sum-exp is not biased by the rounding
+  __device__ static inline void pack(P& dst, int e, float x) { dst[e] = static_cast<__bf16>(x); }
+  __device__ static inline void zero_tail(u32x4 (&v)[VCH], int nval) {
+    // keep elements e < nval of the 8 bf16 values
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int e0 = 2 * w;
+      uint32_t m = 0;
+      if (e0 < nval) m |= 0x0000FFFFu;
+      if (e0 + 1 < nval) m |= 0xFFFF0000u;
+      v[0][w] &= m;
+    }
+  }
+  __device__ static inline void store(void* dst, const float* x, int n) {
+    __bf16* d = static_cast<__bf16*>(dst);
+    for (int i = 0; i < n; ++i) d[i] = static_cast<__bf16>(x[i]);
+  }
+  __device__ static inline float ld_elem(const void* base, size_t idx) {
+    return static_cast<float>(static_cast<const __bf16*>(base)[idx]);
+  }
+  __device__ static inline void put_elem(u32x4 (&v)[VCH], int e, const void* base, size_t idx) {
+    const uint16_t bits = static_cast<const uint16_t*>(base)[idx];
+    const int w = e >> 1;
+    if (e & 1)
+      v[0][w] = (v[0][w] & 0x0000FFFFu) | (uint32_t(bits) << 16);
+    else
+      v[0][w] = (v[0][w] & 0xFFFF0000u) | uint32_t(bits);
+  }
+};
+
+// fp32: one 16-byte chunk = 4 elements = four 16x16x4 MFMAs.
+template <>
+struct Op<float> {
+  static constexpr int VEC = 4;
+  static constexpr int VCH = 2;
+  struct P {
+    float v[8];
+  };
+  __device__ static inline floatx4 mma_k(u32x4 a, u32x4 b, floatx4 c) {
+    const floatx4 fa = __builtin_bit_cast(floatx4, a);
+    const floatx4 fb = __builtin_bit_cast(floatx4, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], fb[e], c, 0, 0, 0);
+    return c;
+  }
+  __device__ static inline floatx4 mma_v(const u32x4 (&v)[VCH], const P& p, floatx4 c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const floatx4 fv = __builtin_bit_cast(floatx4, v[h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(fv[e], p.v[4 * h + e], c, 0, 0, 0);
+    }
+    return c;
+  }
+  __device__ static inline void pack(P& dst, int e, float x) { dst.v[e] = x; }
+  __device__ static inline void zero_tail(u32x4 (&v)[VCH], int nval) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= nval) v[e >> 2][e & 3] = 0u;
+  }
+  __device__ static inline void store(void* dst, const float* x, int n) {
+    float* d = static_cast<float*>(dst);
+    for (int i = 0; i < n; ++i) d[i] = x[i];
+  }
+  __device__ static inline float ld_elem(const void* base, size_t idx) {
+    return static_cast<const float*>(base)[idx];
+  }
+  __device__ static inline void put_elem(u32x4 (&v)[VCH], int e, const void* base, size_t idx) {
+    v[e >> 2][e & 3] = static_cast<const uint32_t*>(base)[idx];
+  }
+};
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline float wave_max_lanegroups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ inline float wave_sum_lanegroups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ inline int find_seq_by(const VerifyParams& p, int idx, bool merge) {
+  int lo = 0, hi = p.n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int start = merge ? p.seq[mid].mwg0 : p.seq[mid].wg0;
+    if (start <= idx)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Locate the group, row and head-in-group of query column `col` of sequence
+// record `sr`.  Returns the group record index, or -1 for a padding column.
+__device__ inline int column_group(const VerifyParams& p, const SeqRec& sr, int col, int& row, int& hh) {
+  if (col >= sr.nq) return -1;
+  int off = 0;
+  for (int i = 0; i < sr.g_count; ++i) {
+    const GroupRec& g = p.grp[sr.g_begin + i];
+    const int nc = g.n_rows * p.G;
+    if (col < off + nc) {
+      row = (col - off) / p.G;
+      hh = (col - off) % p.G;
+      return sr.g_begin + i;
+    }
+    off += nc;
+  }
+  return -1;
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0,
+// which masks key rows past a segment's end without per-lane branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ inline size_t uniform_u64(size_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
+  return (size_t(hi) << 32) | lo;
+}
+
+__device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Running softmax state of one wavefront for its NB 16-column blocks.  The
+// reference maximum m only moves when a step's maximum exceeds it by more than
+// kLazy (log2 units) -- probabilities stay <= 2^kLazy -- so the accumulator
+// rescale is rare; the decision is wave-uniform.
+constexpr float kLazy = 8.0f;
+
+template <typename T, int D, int NB>
+struct Softmax {
+  using O = Op<T>;
+  static constexpr int DB = D / 16;
+  float m[NB], l[NB];
+  floatx4 acc[DB][NB];
+
+  __device__ inline void init() {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m[nb] = -INFINITY;
+      l[nb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // scores of one 32-position step: sacc[mb][nb][j] is position 8*lg+4*mb+j
+  // of column ln+16*nb; positions >= lim[nb] (step-local) are invisible.
+  __device__ inline void update(const floatx4 (&sacc)[2][NB], const int (&lim)[NB], float sl2,
+                                typename O::P (&pf)[NB]) {
+    const int lg = (threadIdx.x & 63) >> 4;
+    float x[NB][8];
+    bool grow = false;
+    float mref[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * mb + j;
+          const float v = (8 * lg + e < lim[nb]) ? sacc[mb][nb][j] * sl2 : -INFINITY;
+          x[nb][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = wave_max_lanegroups(mx);
+      const bool g = (mx > m[nb] + kLazy) || (m[nb] == -INFINITY && mx != -INFINITY);
+      mref[nb] = g ? mx : m[nb];
+      grow |= g;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float alpha = (mref[nb] == m[nb]) ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mref[nb]);
+        l[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][nb] *= alpha;
+        m[nb] = mref[nb];
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float mu = (m[nb] == -INFINITY) ? 0.f : m[nb];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[nb][e] - mu);
+        O::pack(pf[nb], e, pe);
+        ps += pe;
+      }
+      l[nb] += ps;
+    }
+  }
+
+  template <int VCH>
+  __device__ inline void pv(const u32x4 (&vf)[DB][VCH], const typename O::P (&pf)[NB]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[db][nb] = O::mma_v(vf[db], pf[nb], acc[db][nb]);
+  }
+};
+
+template <typename T, int D, int NB>
+__device__ inline void qk(const u32x4 (&kf)[2][D / (4 * Op<T>::VEC)],
+                          const u32x4 (&qf)[NB][D / (4 * Op<T>::VEC)], floatx4 (&sacc)[2][NB]) {
+  constexpr int KC = D / (4 * Op<T>::VEC);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) a = Op<T>::mma_k(kf[mb][c], qf[nb][c], a);
+      sacc[mb][nb] = a;
+    }
+}
+
+template <typename T, int D, int NB>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void verify_partial(const VerifyParams p) {
+  using O = Op<T>;
+  constexpr int VEC = O::VEC;
+  constexpr int VCH = O::VCH;
+  constexpr int KC = D / (4 * VEC);  // 16-byte K/Q chunks per lane per 16-row MFMA block
+  constexpr int DB = D / 16;         // 16-wide head-dim blocks of the output
+  constexpr int CQ = 16 * NB;        // query columns per work-group
+  constexpr int E = sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+
+  // ---- which work item -------------------------------------------------
+  const int s = find_seq_by(p, blockIdx.x, false);
+  const SeqRec& sr = p.seq[s];
+  int local = blockIdx.x - sr.wg0;
+  const int n_cc = sr.n_cc;
+  const int cc = local % n_cc;
+  local /= n_cc;
+  const int h = local % p.H;
+  const int chunk = local / p.H;
+
+  Seg seg{0, 0, -1, 0};
+  int chunk_in = 0;
+  {
+    int acc = 0;
+    const int S = p.S;
+    enumerate_segments(p.layout, p.R, p.We, sr.T, p.grp, sr.g_begin, sr.g_count, [&](const Seg& sg) {
+      const int nch = ceil_div(sg.len, S);
+      if (chunk < acc + nch) {
+        seg = sg;
+        chunk_in = chunk - acc;
+        return true;
+      }
+      acc += nch;
+      return false;
+    });
+  }
+  // every quantity below is wave-uniform; say so, so that buffer
+  // descriptors and loop bounds live in scalar registers
+  seg.kind = __builtin_amdgcn_readfirstlane(seg.kind);
+  seg.depth = __builtin_amdgcn_readfirstlane(seg.depth);
+  seg.gidx = __builtin_amdgcn_readfirstlane(seg.gidx);
+  seg.len = __builtin_amdgcn_readfirstlane(seg.len);
+  chunk_in = __builtin_amdgcn_readfirstlane(chunk_in);
+  const int c0 = chunk_in * p.S;
+  const int clen = min(p.S, seg.len - c0);
+  const int nsteps = ceil_div(clen, kStep);
+  const int seg_len = seg.len;
+
+  // ---- query columns of this lane ---------------------------------------
+  int hi[NB];  // visible segment-local positions are < hi
+  u32x4 qf[NB][KC];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = cc * CQ + ln + 16 * nb;
+    int row = 0, hh = 0;
+    const int gi = column_group(p, sr, col, row, hh);
+    hi[nb] = 0;
+    if (gi >= 0) {
+      const GroupRec& g = p.grp[gi];
+      const T* qp = static_cast<const T*>(p.q) +
+                    (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qf[nb][c] = ld16(qp + c * 4 * VEC + lg * VEC);
+      const int Wb = min(p.We, sr.T);
+      if (seg.kind == kSegPlane) {
+        if (p.layout == 0)
+          hi[nb] = (g.depth == seg.depth) ? sr.T : 0;
+        else if (p.layout == 1)
+          hi[nb] = sr.T;
+        else
+          hi[nb] = (g.depth == p.R) ? sr.T : sr.T - Wb;
+      } else if (seg.kind == kSegRing) {
+        hi[nb] = (g.depth == seg.depth) ? Wb : 0;
+      } else {
+        hi[nb] = (gi == seg.gidx) ? row + 1 : 0;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qf[nb][c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  Softmax<T, D, NB> sm;
+  sm.init();
+  const float sl2 = p.scale_log2;
+
+  if (seg.kind != kSegDraft) {
+    // ---- prefix plane or window ring: streamed with buffer loads ----------
+    size_t off;
+    int bw = kStep;
+    if (seg.kind == kSegPlane) {
+      if (p.layout == 0)
+        off = ((size_t(sr.b) * p.R + (seg.depth - 1)) * p.H + h) * size_t(p.t_max) * D;
+      else
+        off = (size_t(sr.b) * p.H + h) * size_t(p.t_max) * D;
+    } else {
+      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (seg.depth - 1)) * p.H + h) * size_t(p.We) * D;
+      bw = p.BW;
+    }
+    off = uniform_u64(off);
+    bw = __builtin_amdgcn_readfirstlane(bw);
+    const T* kb = static_cast<const T*>(p.cache_k) + off;
+    const T* vb = static_cast<const T*>(p.cache_v) + off;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, uint32_t(seg_len) * D * E);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, uint32_t(ceil_div(seg_len, bw)) * bw * D * E);
+    // lane-constant parts of the byte offsets
+    const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
+    const uint32_t koff = (krow * D + lg * VEC) * E;
+    auto load_k = [&](int st, u32x4 (&kf)[2][KC]) {
+      const uint32_t base = uint32_t(c0 + st * kStep) * D * E + koff;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kf[mb][c] = bload16(krs, base + (4 * mb * D + c * 4 * VEC) * E);
+    };
+    auto load_v = [&](int st, u32x4 (&vf)[DB][VCH]) {
+      const int slot0 = c0 + st * kStep + 8 * lg;
+      const int blk = slot0 / bw;
+      const uint32_t base = uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < VCH; ++v) vf[db][v] = bload16(vrs, base + (16 * db * bw + v * VEC) * E);
+      const int nval = seg_len - slot0;
+      if (nval < 8) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
+      }
+    };
+    if (wave < nsteps) {
+      u32x4 kf[2][KC], vf[DB][VCH];
+      load_k(wave, kf);
+      load_v(wave, vf);
+      for (int st = wave; st < nsteps; st += kWaves) {
+        const bool more = st + kWaves < nsteps;
+        floatx4 sacc[2][NB];
+        qk<T, D, NB>(kf, qf, sacc);
+        if (more) load_k(st + kWaves, kf);
+        int lim[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - (c0 + st * kStep);
+        typename O::P pf[NB];
+        sm.update(sacc, lim, sl2, pf);
+        sm.pv(vf, pf);
+        if (more) load_v(st + kWaves, vf);
+      }
+    }
+  } else {
+    // ---- a group's own draft rows: gathered from kv_new -------------------
+    const GroupRec& g = p.grp[seg.gidx];
+    const int Hd = p.H * D;
+    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(seg.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    const T* vb = static_cast<const T*>(p.kv_new) +
+                  (size_t(p.R + seg.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    for (int st = wave; st < nsteps; st += kWaves) {
+      u32x4 kf[2][KC], vf[DB][VCH];
+      const int base = c0 + st * kStep;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int pos = base + 8 * (ln >> 2) + 4 * mb + (ln & 3);
+        const T* rp = kb + size_t(pos) * Hd + lg * VEC;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kf[mb][c] = pos < seg_len ? ld16(rp + c * 4 * VEC) : u32x4{0u, 0u, 0u, 0u};
+      }
+      const int slot0 = base + 8 * lg;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int v = 0; v < VCH; ++v) vf[db][v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (slot0 + e < seg_len) O::put_elem(vf[db], e, vb, size_t(slot0 + e) * Hd + 16 * db + ln);
+      }
+      floatx4 sacc[2][NB];
+      qk<T, D, NB>(kf, qf, sacc);
+      int lim[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - base;
+      typename O::P pf[NB];
+      sm.update(sacc, lim, sl2, pf);
+      sm.pv(vf, pf);
+    }
+  }
+
+  // ---- merge the four wavefronts through LDS, write one partial ----------
+  __shared__ float lds_o[kWaves][CQ][D + 4];
+  __shared__ float lds_m[kWaves][CQ];
+  __shared__ float lds_l[kWaves][CQ];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = wave_sum_lanegroups(sm.l[nb]);
+    const int col = ln + 16 * nb;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<floatx4*>(&lds_o[wave][col][16 * db + 4 * lg]) = sm.acc[db][nb];
+    if (lg == 0) {
+      lds_m[wave][col] = sm.m[nb];
+      lds_l[wave][col] = lt;
+    }
+  }
+  __syncthreads();
+  constexpr int TPC = kThreads / CQ;  // threads per column
+  constexpr int DPT = D / TPC;        // head-dim values per thread
+  const int col = threadIdx.x / TPC;
+  const int d0 = (threadIdx.x % TPC) * DPT;
+  if (cc * CQ + col >= sr.nq) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][col]);
+  float f[kWaves];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = lds_m[w][col];
+    f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L += f[w] * lds_l[w][col];
+  }
+  const size_t stride = size_t(CQ) * (D + 2);
+  float* part = p.ws + (size_t(sr.part0) + (size_t(h) * n_cc + cc) * sr.n_split + chunk) * stride;
+#pragma unroll
+  for (int d = 0; d < DPT; d += 4) {
+    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) o += f[w] * *reinterpret_cast<const floatx4*>(&lds_o[w][col][d0 + d]);
+    *reinterpret_cast<floatx4*>(part + size_t(col) * D + d0 + d) = o;
+  }
+  if (d0 == 0) {
+    part[size_t(CQ) * D + col] = M;
+    part[size_t(CQ) * D + CQ + col] = L;
+  }
+}
+
+template <typename T, int D, int NB>
+__global__ __launch_bounds__(kThreads) void verify_merge(const VerifyParams p) {
+  using O = Op<T>;
+  constexpr int CQ = 16 * NB;
+  constexpr int TPC = kThreads / CQ;
+  constexpr int DPT = D / TPC;
+  if (int(blockIdx.x) >= p.n_mwg) {
+    // plane_sel of one group: plane read at each committed position
+    const int gi = blockIdx.x - p.n_mwg;
+    if (p.plane_sel == nullptr || gi >= p.n_grp) return;
+    const GroupRec& g = p.grp[gi];
+    const int Tl = p.seq[g.seq].T;
+    const int Wb = min(p.We, Tl);
+    int8_t* row = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
+    const int r = g.depth;
+    for (int j0 = threadIdx.x * 16; j0 < Tl; j0 += kThreads * 16) {
+      int8_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
+        int pl;
+        if (p.layout == 0)
+          pl = r;
+        else if (p.layout == 1)
+          pl = p.R;
+        else
+          pl = (j >= Tl - Wb) ? r : p.R;
+        v[e] = int8_t(pl);
+      }
+      if (j0 + 16 <= Tl) {
+        *reinterpret_cast<u32x4*>(row + j0) = *reinterpret_cast<const u32x4*>(v);
+      } else {
+        for (int e = 0; j0 + e < Tl; ++e) row[j0 + e] = v[e];
+      }
+    }
+    return;
+  }
+  const int s = find_seq_by(p, blockIdx.x, true);
+  const SeqRec& sr = p.seq[s];
+  const int local = blockIdx.x - sr.mwg0;
+  const int n_cc = sr.n_cc;
+  const int cc = local % n_cc;
+  const int h = local / n_cc;
+  const int col = threadIdx.x / TPC;
+  const int d0 = (threadIdx.x % TPC) * DPT;
+  int row = 0, hh = 0;
+  const int gi = column_group(p, sr, cc * CQ + col, row, hh);
+  if (gi < 0) return;
+  const size_t stride = size_t(CQ) * (D + 2);
+  const float* base = p.ws + (size_t(sr.part0) + (size_t(h) * n_cc + cc) * sr.n_split) * stride;
+  const int ns = sr.n_split;
+  constexpr int U = 4;  // splits whose loads are issued together
+  float M = -INFINITY;
+  for (int sp = 0; sp < ns; sp += U) {
+    float mm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      mm[u] = (sp + u < ns) ? base[size_t(sp + u) * stride + size_t(CQ) * D + col] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
+  }
+  float L = 0.f;
+  float o[DPT];
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) o[d] = 0.f;
+  for (int sp = 0; sp < ns; sp += U) {
+    float ms[U], ls[U];
+    floatx4 ov[U][DPT / 4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = sp + u < ns;
+      const float* part = base + size_t(ok ? sp + u : 0) * stride;
+      ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
+      ls[u] = part[size_t(CQ) * D + CQ + col];
+#pragma unroll
+      for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+      L += f * ls[u];
+#pragma unroll
+      for (int d = 0; d < DPT; d += 4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[d + e] += f * ov[u][d / 4][e];
+    }
+  }
+  const GroupRec& g = p.grp[gi];
+  const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
+  float res[DPT];
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
+  O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
+  if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NB>
+static hipError_t launch_verify_t(const VerifyParams& p, hipStream_t stream) {
+  if (p.n_wg > 0)
+    hipLaunchKernelGGL((verify_partial<T, D, NB>), dim3(p.n_wg), dim3(kThreads), 0, stream, p);
+  const int n2 = p.n_mwg + (p.plane_sel ? p.n_grp : 0);
+  if (n2 > 0) hipLaunchKernelGGL((verify_merge<T, D, NB>), dim3(n2), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyParams& p, int dtype, int D, int NB, hipStream_t stream) {
+  if (dtype == 1) {
+    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, stream) : launch_verify_t<__bf16, 128, 2>(p, stream);
+    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, stream) : launch_verify_t<__bf16, 64, 2>(p, stream);
+  }
+  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, stream) : launch_verify_t<float, 128, 2>(p, stream);
+  return NB == 1 ? launch_verify_t<float, 64, 1>(p, stream) : launch_verify_t<float, 64, 2>(p, stream);
+}
+
+}  // namespace ripe

@@ -1,0 +1,164 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, sizes caches by the closed-form memory model, and rejects
+invalid arguments on the host before any HIP call (no compute call is made
+here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import self_speculative_verify_ripe_amd as rp
+from self_speculative_verify_ripe_amd import binding
+from oracle import layout as oracle_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ripe.h")
+
+FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on error paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ripe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert names == ["ripe_commit", "ripe_layout_bytes", "ripe_verify_attn"]
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(rp.ripe_desc_t) == 12 * 4
+    assert ctypes.sizeof(rp.ripe_group_t) == 16
+
+
+@pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [0, 8, 16, 24, 32, 64, 96, 4096, 100000])
+def test_cache_bytes_closed_form(layout, dtype, W):
+    R, B, T, H, D = 32, 3, 1024, 8, 128
+    d = rp.make_desc(layout, dtype, R, W, B, T, H, D, 32)
+    got = rp.ripe_layout_bytes(d)
+    assert got == oracle_layout.layout_bytes(layout, dtype, R, W, B, T, H, D)
+    E = 4 if dtype == "f32" else 2
+    per_seq = {"full": R * T, "deepest": T, "ripe": T + min(W, T) * (R - 1)}[layout]
+    assert got == 2 * B * H * D * E * per_seq
+
+
+def test_memory_identities():
+    R, B, T, H, D = 32, 2, 1024, 8, 128
+    full = rp.ripe_layout_bytes(rp.make_desc("full", "bf16", R, 64, B, T, H, D, 32))
+    deep = rp.ripe_layout_bytes(rp.make_desc("deepest", "bf16", R, 64, B, T, H, D, 32))
+    assert rp.ripe_layout_bytes(rp.make_desc("ripe", "bf16", R, 0, B, T, H, D, 32)) == deep
+    assert rp.ripe_layout_bytes(rp.make_desc("ripe", "bf16", R, T, B, T, H, D, 32)) == full
+    ripe = rp.ripe_layout_bytes(rp.make_desc("ripe", "bf16", R, 64, B, T, H, D, 32))
+    assert ripe * 32768 == full * 3008  # T + W(R-1) over R*T at T=1024, W=64, R=32
+
+
+def test_workspace_bound_positive():
+    d = rp.make_desc("ripe", "bf16", 32, 64, 16, 4128, 8, 128, 32, max_rows=128, max_groups=16)
+    assert rp.ripe_layout_bytes(d, rp.RIPE_BYTES_WORKSPACE) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("layout", 3, -1), ("dtype", 7, -1), ("R", 0, -1), ("W", -1, -1), ("batch", 0, -1),
+    ("t_max", 0, -1), ("n_kv_heads", 0, -1), ("n_q_heads", 12, -1), ("head_dim", 96, -4),
+    ("t_max", 100, -4), ("W", 40, -4), ("R", 200, -4), ("split_len", 48, -4),
+    ("split_len", -32, -1),
+])
+def test_bad_descriptor(field, value, status):
+    d = rp.make_desc("ripe", "bf16", 32, 64, 2, 1024, 8, 128, 32)
+    setattr(d, field, value)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) == status
+
+
+def test_bad_kind():
+    d = rp.make_desc("ripe", "bf16", 32, 64, 2, 1024, 8, 128, 32)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 9) == -1
+    assert binding.lib.ripe_layout_bytes(None, 0) == -1
+
+
+def call_verify(desc, seq_len, groups, n_rows=16, scale=1.0, cache=FAKE, q=FAKE, kv=FAKE,
+                out=FAKE, lse=None, ps=None, ws=FAKE, ws_bytes=1 << 40):
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    garr, ng = binding._groups(groups)
+    return binding.lib.ripe_verify_attn(
+        ctypes.byref(desc), cache, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr, ng,
+        n_rows, scale, q, kv, out, lse, ps, ws, ws_bytes, None)
+
+
+def desc2():
+    return rp.make_desc("ripe", "bf16", 4, 8, 2, 64, 2, 64, 4, max_rows=16, max_groups=4)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(seq_len=[10, 65]), -2),                       # T > t_max
+    (dict(seq_len=[-1, 3]), -2),
+    (dict(groups=[(2, 1, 0, 4)]), -2),                  # sequence out of range
+    (dict(groups=[(0, 0, 0, 4)]), -2),                  # depth 0
+    (dict(groups=[(0, 5, 0, 4)]), -2),                  # depth > R
+    (dict(groups=[(0, 1, 14, 4)]), -2),                 # rows past n_rows
+    (dict(groups=[(0, 1, 0, 0)]), -1),                  # empty group
+    (dict(groups=[(0, 1, 0, 4), (1, 1, 3, 4)]), -1),    # overlapping rows
+    (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(q=0), -1), (dict(cache=0), -1), (dict(out=0), -1), (dict(kv=0), -1),
+    (dict(q=FAKE + 2), -1),                             # misaligned
+    (dict(ws=FAKE + 16), -1),                           # workspace not 256-aligned
+    (dict(ws_bytes=16), -5),                            # workspace too small
+    (dict(ws=0, ws_bytes=0), -5),
+    (dict(n_rows=0), -1),
+])
+def test_verify_rejects(case, status):
+    args = dict(seq_len=[10, 20], groups=[(0, 1, 0, 4), (1, 2, 4, 4)])
+    args.update(case)
+    assert call_verify(desc2(), **args) == status
+
+
+def test_verify_no_groups_is_noop():
+    assert call_verify(desc2(), [10, 20], []) == 0
+
+
+def test_verify_too_many_columns():
+    d = rp.make_desc("ripe", "bf16", 4, 8, 1, 64, 1, 64, 64, max_rows=2048, max_groups=4)
+    assert call_verify(d, [10], [(0, 1, 0, 1100)], n_rows=2048) == -4  # 1100 * 64 columns
+
+
+def call_commit(desc, seq_len, n_accept, src_row, n_rows=8, cache=FAKE, kv=FAKE):
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    na = np.ascontiguousarray(np.asarray(n_accept, dtype=np.int32))
+    sr = np.ascontiguousarray(np.asarray(src_row, dtype=np.int32))
+    st = binding.lib.ripe_commit(ctypes.byref(desc), cache,
+                                 sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 na.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 sr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), kv, n_rows, None)
+    return st, sl
+
+
+@pytest.mark.parametrize("args,status", [
+    (([60, 0], [5, 0], [0, 0]), -3),     # capacity
+    (([0, 0], [-1, 0], [0, 0]), -1),     # negative count
+    (([0, 0], [4, 0], [6, 0]), -2),      # source rows past n_rows
+    (([0, 0], [2, 0], [-1, 0]), -2),
+    (([65, 0], [0, 0], [0, 0]), -2),     # committed length past t_max
+])
+def test_commit_rejects_and_leaves_seq_len(args, status):
+    st, sl = call_commit(desc2(), *args)
+    assert st == status
+    assert sl.tolist() == list(args[0])
+
+
+def test_commit_nothing_accepted_is_noop():
+    st, sl = call_commit(desc2(), [7, 9], [0, 0], [3, 3], cache=0, kv=0)
+    assert st == 0 and sl.tolist() == [7, 9]
+
+
+def test_commit_null_buffers():
+    st, sl = call_commit(desc2(), [7, 9], [1, 0], [0, 0], cache=0)
+    assert st == -1 and sl.tolist() == [7, 9]

@@ -1,0 +1,215 @@
+"""GPU parity of ripe_verify_attn and ripe_commit against the float64 oracle.
+
+Every call goes through the C ABI (libripe.so).  The device cache bytes are
+produced by the oracle's own layout encoder from seeded workloads; unheld
+slots are NaN so any wrong read shows up.  Tolerances: plane_sel and cache
+bytes bit-exact; out max-abs <= 2e-2 (bf16) / 1e-5 (fp32); lse <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import self_speculative_verify_ripe_amd as rp
+from oracle import layout as olay
+from oracle import ripe_oracle as ro
+from workloads import Group, make_case
+
+from gpu_util import (DEV, Device, check, gpu_verify, make_desc, oracle_cache, to_dev,
+                      upload)
+
+pytestmark = pytest.mark.gpu
+LAYOUTS = ("full", "deepest", "ripe")
+
+
+def oracle_verify(cache, case, groups):
+    return ro.verify(cache, groups, case.q, case.kv_new, case.scale, case.Hq)
+
+
+def run_case(case, layout, groups, W=None, split_len=0, planes=None, tag=""):
+    print(f"[case] {tag} {case.name} {layout} W={W} split={split_len} groups={len(groups)}",
+          flush=True)
+    oc = oracle_cache(case, layout, W=W, planes=planes)
+    dev = Device(case)
+    cache = upload(olay.encode(oc))
+    desc = make_desc(case, layout, W=W, split_len=split_len)
+    gpu = gpu_verify(desc, cache, case, dev, groups)
+    ref = oracle_verify(oc, case, groups)
+    return check(case, groups, gpu, ref, tag=f"{tag} {layout}"), gpu
+
+
+# ---------------------------------------------------------------------------
+# c1: fp32, R=4, Hq=Hkv=4, D=64, T=128, k=4, W=8, all depths and layouts
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("split_len", [0, 32])
+def test_c1_all_depths(layout, split_len):
+    case = make_case("c1")
+    for r in case.depths:
+        run_case(case, layout, case.groups_at(r), split_len=split_len, tag=f"c1 r={r}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_c1_four_depths_in_one_call(layout):
+    case = make_case("c1", k=16)
+    groups = [Group(0, r, 4 * (r - 1), 4) for r in (1, 2, 3, 4)]
+    run_case(case, layout, groups, tag="c1 mixed")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_c1_commit_then_verify(layout):
+    case = make_case("c1")
+    print(f"[case] c1 commit {layout}", flush=True)
+    oc = oracle_cache(case, layout)
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, layout)
+    sl = case.seq_len.astype(np.int32).copy()
+    rp.ripe_commit(desc, cache, sl, case.n_accept, case.src_row, dev.kv_new, case.n_rows)
+    torch.cuda.synchronize()
+    ro.commit(oc, case.n_accept, case.src_row, case.kv_new)
+    assert sl.tolist() == oc.seq_len.tolist() == [131]
+    assert np.array_equal(cache.cpu().numpy(), olay.encode(oc)), "cache bytes differ after commit"
+    for r in case.depths:
+        groups = case.groups_at(r)
+        gpu = gpu_verify(desc, cache, case, dev, groups, seq_len=sl)
+        ref = ro.verify(oc, groups, case.q, case.kv_new, case.scale, case.Hq)
+        check(case, groups, gpu, ref, seq_len=sl, tag=f"c1 after commit r={r}")
+
+
+# ---------------------------------------------------------------------------
+# c2 at full size: bf16, R=32, 40/40 heads, D=128, T=1024, k=8, W=64
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_c2_full_size(layout):
+    case = make_case("c2")
+    for r in case.depths:
+        run_case(case, layout, case.groups_at(r), planes={r, case.R} if layout == "full" else None,
+                 tag=f"c2 r={r}")
+
+
+# ---------------------------------------------------------------------------
+# c3-shaped, reduced lengths: 4 sequences, T in [300, 700], GQA 32/8
+# ---------------------------------------------------------------------------
+def small_c3(**kw):
+    args = dict(B=4, T_range=(300, 700))
+    args.update(kw)
+    return make_case("c3", **args)
+
+
+@pytest.mark.parametrize("split_len", [0, 128, 32])
+def test_c3_reduced_all_layouts(split_len):
+    case = small_c3()
+    for layout in LAYOUTS:
+        for r in (1, 17, 32):
+            run_case(case, layout, case.groups_at(r), split_len=split_len,
+                     planes={r} if layout == "full" else None, tag=f"c3s r={r}")
+
+
+def test_c3_batched_equals_alone_bitexact():
+    case = small_c3(B=5)
+    oc = oracle_cache(case, "ripe")
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, "ripe", split_len=128)
+    for r in (3, 32):
+        groups = case.groups_at(r)
+        out, lse, ps = gpu_verify(desc, cache, case, dev, groups)
+        check(case, groups, (out, lse, ps), oracle_verify(oc, case, groups), tag=f"batched r={r}")
+        for gi, g in enumerate(groups):
+            o1, l1, p1 = gpu_verify(desc, cache, case, dev, [g])
+            rows = slice(g.row_start, g.row_start + g.n_rows)
+            assert torch.equal(out[rows], o1[rows]), f"out differs alone vs batched, group {gi}"
+            assert torch.equal(lse[rows], l1[rows]), f"lse differs alone vs batched, group {gi}"
+            assert torch.equal(ps[gi], p1[0])
+
+
+def test_c4_branches_alone_equal_batched_bitexact():
+    case = make_case("c4", T_range=(400, 700))
+    oc = oracle_cache(case, "ripe")
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, "ripe", split_len=128)
+    groups = case.groups()
+    out, lse, ps = gpu_verify(desc, cache, case, dev, groups)
+    check(case, groups, (out, lse, ps), oracle_verify(oc, case, groups), tag="c4 batched")
+    for g in groups:
+        o1, l1, _ = gpu_verify(desc, cache, case, dev, [g])
+        rows = slice(g.row_start, g.row_start + g.n_rows)
+        assert torch.equal(out[rows], o1[rows]) and torch.equal(lse[rows], l1[rows])
+
+
+# ---------------------------------------------------------------------------
+# the layout identities on the GPU, bit-exact
+# ---------------------------------------------------------------------------
+def test_ripe_wide_window_equals_full_and_zero_window_equals_deepest():
+    case = small_c3(B=3)
+    dev = Device(case)
+    for r in (2, 32):
+        groups = case.groups_at(r)
+        res = {}
+        for name, layout, W in (("full", "full", case.W), ("deepest", "deepest", case.W),
+                                ("wide", "ripe", case.t_max), ("zero", "ripe", 0)):
+            oc = oracle_cache(case, layout, W=W)
+            desc = make_desc(case, layout, W=W, split_len=64)
+            res[name] = gpu_verify(desc, upload(olay.encode(oc)), case, dev, groups)
+            check(case, groups, res[name], oracle_verify(oc, case, groups), tag=f"{name} r={r}")
+        for a, b in (("wide", "full"), ("zero", "deepest")):
+            assert torch.equal(res[a][0], res[b][0]) and torch.equal(res[a][1], res[b][1]), (a, b)
+            assert torch.equal(res[a][2], res[b][2])
+        if r == case.R:
+            assert torch.equal(res["full"][0], res["deepest"][0])
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_empty_prefix_and_ragged_lengths():
+    case = make_case("c3", B=5, T_range=(0, 90), R=8)
+    case.seq_len[:] = [0, 1, 31, 33, 90]
+    for layout in LAYOUTS:
+        run_case(case, layout, case.groups_at(3), split_len=32, tag="ragged")
+
+
+def test_long_draft_block_spans_steps():
+    case = make_case("c3", B=2, T_range=(100, 200), k=40, R=6)
+    for layout in LAYOUTS:
+        run_case(case, layout, case.groups_at(2), tag="k=40")
+
+
+def test_many_query_columns_per_kv_head():
+    # GQA 32/1 with 8 rows: 256 columns per KV head -> eight column chunks
+    case = make_case("c3", B=2, T_range=(150, 260), Hkv=1, Hq=32, R=5)
+    for layout in LAYOUTS:
+        run_case(case, layout, case.groups_at(4), tag="G=32")
+
+
+@pytest.mark.parametrize("W", [8, 16, 24, 32, 96])
+def test_ring_widths(W):
+    case = make_case("c3", B=3, T_range=(60, 150), R=5, W=W)
+    for r in (1, 4, 5):
+        run_case(case, "ripe", case.groups_at(r), split_len=64, tag=f"W={W} r={r}")
+
+
+def test_head_dim_64_bf16_and_fp32_d128():
+    for kw in (dict(D=64), dict(dtype="f32", D=128)):
+        case = make_case("c3", B=3, T_range=(70, 200), R=4, **kw)
+        for layout in LAYOUTS:
+            run_case(case, layout, case.groups_at(2), tag=f"{kw}")
+
+
+def test_more_sequences_than_one_launch():
+    case = make_case("c3", B=70, T_range=(10, 60), R=3, Hkv=2, Hq=4, D=64)
+    run_case(case, "ripe", case.groups_at(2), tag="B=70")
+
+
+def test_optional_outputs_and_determinism():
+    case = small_c3(B=2)
+    oc = oracle_cache(case, "ripe")
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, "ripe")
+    groups = case.groups_at(5)
+    a = gpu_verify(desc, cache, case, dev, groups)
+    b = gpu_verify(desc, cache, case, dev, groups, with_ps=False, with_lse=False)
+    c = gpu_verify(desc, cache, case, dev, groups)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
