@@ -43,6 +43,10 @@ class ripe_group_t(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime under the same soname as /opt/rocm's.
+    # Load torch first so that libripe.so binds to the runtime torch already
+    # uses: one process, one HIP runtime.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libripe.so not built ({LIB_PATH}); run "
                           "python -m self_speculative_verify_ripe_amd.build")

@@ -11,6 +11,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -31,6 +33,15 @@ constexpr int64_t kMaxItems = int64_t(1) << 30;   // commit work items per launc
 constexpr int kMaxCQ = 32;                        // query columns per verify work-group
 
 int elem_bytes(int dtype) { return dtype == RIPE_F32 ? 4 : 2; }
+
+// A failed launch is reported as RIPE_EHIP; with RIPE_DEBUG set in the
+// environment the HIP error string is also printed to stderr.
+ripe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RIPE_OK;
+  if (std::getenv("RIPE_DEBUG") != nullptr)
+    std::fprintf(stderr, "[ripe] %s: HIP error %d (%s)\n", what, int(e), hipGetErrorString(e));
+  return RIPE_EHIP;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -258,7 +269,8 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (const LaunchPlan& lp : plans) {
-    if (launch_verify(lp.p, d.dtype, D, lp.NB, hs) != hipSuccess) return RIPE_EHIP;
+    const ripe_status_t st2 = hip_status(launch_verify(lp.p, d.dtype, D, lp.NB, hs), "ripe_verify_attn");
+    if (st2 != RIPE_OK) return st2;
   }
   return RIPE_OK;
 }
@@ -355,7 +367,7 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (const CommitParams& p : launches)
-    if (launch_commit(p, d.dtype, D, hs) != hipSuccess) return RIPE_EHIP;
+    if (hip_status(launch_commit(p, d.dtype, D, hs), "ripe_commit") != RIPE_OK) return RIPE_EHIP;
   for (int b = 0; b < d.batch; ++b) seq_len[b] += n_accept[b];
   return RIPE_OK;
 }

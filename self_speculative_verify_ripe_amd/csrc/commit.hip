@@ -82,8 +82,10 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
 template <typename T, int D>
 static hipError_t launch_commit_t(const CommitParams& p, hipStream_t stream) {
   const int blocks = (p.n_items + 255) / 256;
-  if (blocks > 0) hipLaunchKernelGGL((commit_rows<T, D>), dim3(blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (blocks == 0) return hipSuccess;
+  void* args[] = {const_cast<CommitParams*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&commit_rows<T, D>), dim3(blocks), dim3(256),
+                         args, 0, stream);
 }
 
 hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream) {

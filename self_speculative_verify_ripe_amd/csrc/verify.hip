@@ -290,8 +290,20 @@ __device__ inline void qk(const u32x4 (&kf)[2][D / (4 * Op<T>::VEC)],
     }
 }
 
+#ifndef RIPE_FP32_WAVES
+#define RIPE_FP32_WAVES 2
+#endif
+// Wavefronts per SIMD the register allocation targets: two for bf16 (the
+// streaming configuration); fp32 with D = 128 and 32 columns needs more
+// registers than two wavefronts allow.
 template <typename T, int D, int NB>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+constexpr int waves_per_simd() {
+  return (sizeof(T) == 4 && D == 128 && NB == 2) ? RIPE_FP32_WAVES : 2;
+}
+
+template <typename T, int D, int NB>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
 void verify_partial(const VerifyParams p) {
   using O = Op<T>;
   constexpr int VEC = O::VEC;
@@ -344,37 +356,33 @@ void verify_partial(const VerifyParams p) {
   const int seg_len = seg.len;
 
   // ---- query columns of this lane ---------------------------------------
+  // Straight-line on purpose: every lane loads from a valid address and
+  // padding columns are zeroed by selects, with no loads under divergent
+  // control flow.
   int hi[NB];  // visible segment-local positions are < hi
   u32x4 qf[NB][KC];
+  const int Wb = min(p.We, sr.T);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int col = cc * CQ + ln + 16 * nb;
     int row = 0, hh = 0;
     const int gi = column_group(p, sr, col, row, hh);
-    hi[nb] = 0;
-    if (gi >= 0) {
-      const GroupRec& g = p.grp[gi];
-      const T* qp = static_cast<const T*>(p.q) +
-                    (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
+    const bool valid = gi >= 0;
+    const GroupRec& g = p.grp[valid ? gi : sr.g_begin];
+    const T* qp = static_cast<const T*>(p.q) + (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) qf[nb][c] = ld16(qp + c * 4 * VEC + lg * VEC);
-      const int Wb = min(p.We, sr.T);
-      if (seg.kind == kSegPlane) {
-        if (p.layout == 0)
-          hi[nb] = (g.depth == seg.depth) ? sr.T : 0;
-        else if (p.layout == 1)
-          hi[nb] = sr.T;
-        else
-          hi[nb] = (g.depth == p.R) ? sr.T : sr.T - Wb;
-      } else if (seg.kind == kSegRing) {
-        hi[nb] = (g.depth == seg.depth) ? Wb : 0;
-      } else {
-        hi[nb] = (gi == seg.gidx) ? row + 1 : 0;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < KC; ++c) qf[nb][c] = u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 v = ld16(qp + c * 4 * VEC + lg * VEC);
+      qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
     }
+    const int gd = g.depth;
+    const int h_plane = (p.layout == 0) ? (gd == seg.depth ? sr.T : 0)
+                        : (p.layout == 1) ? sr.T
+                                          : (gd == p.R ? sr.T : sr.T - Wb);
+    const int h_ring = (gd == seg.depth) ? Wb : 0;
+    const int h_draft = (gi == seg.gidx) ? row + 1 : 0;
+    const int hv = (seg.kind == kSegPlane) ? h_plane : (seg.kind == kSegRing) ? h_ring : h_draft;
+    hi[nb] = valid ? hv : 0;
   }
 
   Softmax<T, D, NB> sm;
@@ -403,43 +411,49 @@ void verify_partial(const VerifyParams p) {
     // lane-constant parts of the byte offsets
     const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
     const uint32_t koff = (krow * D + lg * VEC) * E;
-    auto load_k = [&](int st, u32x4 (&kf)[2][KC]) {
-      const uint32_t base = uint32_t(c0 + st * kStep) * D * E + koff;
+    // A step index past the chunk maps to an offset beyond the buffer's
+    // range: those loads return zeros without touching memory, so the
+    // prefetch below is unconditional and the wait counts stay exact.
+    constexpr uint32_t kOutOfRange = 0x80000000u;
+    auto load_k = [&](int st, bool live, u32x4 (&kf)[2][KC]) {
+      const uint32_t base = live ? uint32_t(c0 + st * kStep) * D * E + koff : kOutOfRange;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int c = 0; c < KC; ++c) kf[mb][c] = bload16(krs, base + (4 * mb * D + c * 4 * VEC) * E);
     };
-    auto load_v = [&](int st, u32x4 (&vf)[DB][VCH]) {
+    auto load_v = [&](int st, bool live, u32x4 (&vf)[DB][VCH]) {
       const int slot0 = c0 + st * kStep + 8 * lg;
       const int blk = slot0 / bw;
-      const uint32_t base = uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E;
+      const uint32_t base = live ? uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E : kOutOfRange;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < VCH; ++v) vf[db][v] = bload16(vrs, base + (16 * db * bw + v * VEC) * E);
-      const int nval = seg_len - slot0;
-      if (nval < 8) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
-      }
     };
     if (wave < nsteps) {
       u32x4 kf[2][KC], vf[DB][VCH];
-      load_k(wave, kf);
-      load_v(wave, vf);
+      load_k(wave, true, kf);
+      load_v(wave, true, vf);
       for (int st = wave; st < nsteps; st += kWaves) {
         const bool more = st + kWaves < nsteps;
         floatx4 sacc[2][NB];
         qk<T, D, NB>(kf, qf, sacc);
-        if (more) load_k(st + kWaves, kf);
+        load_k(st + kWaves, more, kf);
         int lim[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - (c0 + st * kStep);
         typename O::P pf[NB];
         sm.update(sacc, lim, sl2, pf);
+        // a step reaching past the segment's end: zero the V values of the
+        // missing positions (they may hold anything, even NaN)
+        if (c0 + (st + 1) * kStep > seg_len) {
+          const int nval = seg_len - (c0 + st * kStep + 8 * lg);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
+        }
         sm.pv(vf, pf);
-        if (more) load_v(st + kWaves, vf);
+        load_v(st + kWaves, more, vf);
       }
     }
   } else {
@@ -628,11 +642,17 @@ __global__ __launch_bounds__(kThreads) void verify_merge(const VerifyParams p) {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NB>
 static hipError_t launch_verify_t(const VerifyParams& p, hipStream_t stream) {
-  if (p.n_wg > 0)
-    hipLaunchKernelGGL((verify_partial<T, D, NB>), dim3(p.n_wg), dim3(kThreads), 0, stream, p);
+  void* args[] = {const_cast<VerifyParams*>(&p)};
+  if (p.n_wg > 0) {
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_partial<T, D, NB>),
+                                         dim3(p.n_wg), dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   const int n2 = p.n_mwg + (p.plane_sel ? p.n_grp : 0);
-  if (n2 > 0) hipLaunchKernelGGL((verify_merge<T, D, NB>), dim3(n2), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  if (n2 > 0)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge<T, D, NB>), dim3(n2),
+                           dim3(kThreads), args, 0, stream);
+  return hipSuccess;
 }
 
 hipError_t launch_verify(const VerifyParams& p, int dtype, int D, int NB, hipStream_t stream) {
