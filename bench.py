@@ -161,6 +161,7 @@ def main():
     else:
         group_sets = [[(b, r, case.blocks[b][0], case.blocks[b][1]) for b in range(B)]
                       for r in depths]
+    packed_sets = [rp.pack_groups(gs) for gs in group_sets]
     n_rows = case.n_rows
     desc = rp.make_desc(layout, case.dtype, R, W, B, t_max, Hkv, D, Hq, max_rows=n_rows,
                         max_groups=2 * B, split_len=args.split_len)
@@ -205,45 +206,61 @@ def main():
     src_row = case.src_row.astype(np.int32)
 
     seq_len = seq_len0.copy()
-    ev_pairs = []
+    n_calls = len(group_sets) * L
 
-    def one_step(record):
+    def step_bytes(sl):
+        """Per-call algorithmic bytes (KV read; all incl. q/out/lse) for the
+        current committed lengths."""
+        kv = [kv_read_bytes(layout, R, W, sl, gs, Hkv, D, elem) for gs in group_sets]
+        io = [io_bytes(gs, Hq, D, elem) for gs in group_sets]
+        return kv, io
+
+    def one_step(events, ev0):
         nonlocal seq_len
-        for gs in group_sets:
+        i = ev0
+        for gi in range(len(group_sets)):
+            gs = packed_sets[gi]
             for layer in range(L):
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                if events is not None:
+                    events[i][0].record(stream)
                 rp.ripe_verify_attn(desc, caches[layer], seq_len, gs, n_rows, 1.0, q, kv_new, out,
                                     lse, None, ws, ws_bytes, stream)
-                if record:
-                    e1.record(stream)
-                    ev_pairs.append((e0, e1, kv_read_bytes(layout, R, W, seq_len, gs, Hkv, D, elem)
-                                     + io_bytes(gs, Hq, D, elem)))
-        step_bytes = sum(kv_read_bytes(layout, R, W, seq_len, gs, Hkv, D, elem) for gs in group_sets) * L
+                if events is not None:
+                    events[i][1].record(stream)
+                i += 1
+        sl = seq_len
         for layer in range(L):
             sl = seq_len.copy()
             rp.ripe_commit(desc, caches[layer], sl, n_accept, src_row, kv_new, n_rows, stream)
         seq_len = sl
-        return step_bytes
 
     for _ in range(args.warmup):
-        one_step(False)
+        one_step(None, 0)
     torch.cuda.synchronize()
-    total_kv = 0
+    # byte counts of every timed call, computed before timing starts
+    per_step = []
+    sl = seq_len.copy()
+    for _ in range(args.steps):
+        kv, io = step_bytes(sl)
+        per_step.append((kv, io))
+        sl = sl + n_accept
+    total_kv = sum(sum(kv) * L for kv, _ in per_step)
+    call_bytes = np.array([kv[gi] + io[gi] for kv, io in per_step for gi in range(len(group_sets))
+                           for _ in range(L)], dtype=np.float64)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_calls * args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        total_kv += one_step(True)
+    for k in range(args.steps):
+        one_step(events, k * n_calls)
+    host_s = time.perf_counter() - wall0
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed = t0.elapsed_time(t1) / 1e3
-    call_s = np.array([a.elapsed_time(b) / 1e3 for a, b, _ in ev_pairs])
-    call_bytes = np.array([x for _, _, x in ev_pairs], dtype=np.float64)
+    call_s = np.array([a.elapsed_time(b) / 1e3 for a, b in events])
     calls_per_step = len(group_sets) * L
     rows_per_step = sum(g[3] for g in group_sets[0])
     verified_tok_s = rows_per_step * args.steps / elapsed if case.fixed_groups is None else \
@@ -275,6 +292,8 @@ def main():
                      "avg_call_us": round(avg_call * 1e6, 2),
                      "alg_bytes_per_call": int(call_bytes.mean())},
         "wall_s": round(wall, 3),
+        "host_enqueue_us_per_call": round(host_s / (n_calls * args.steps) * 1e6, 1),
+        "gpu_us_per_call": round(elapsed / (n_calls * args.steps) * 1e6, 2),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, layout, args.cpu_seconds)

@@ -100,16 +100,26 @@ def _i32(a, n: Optional[int] = None):
     return arr
 
 
-def _groups(groups: Iterable) -> ctypes.Array:
-    gl = list(groups)
-    arr = (ripe_group_t * max(len(gl), 1))()
-    for i, g in enumerate(gl):
+def pack_groups(groups: Iterable) -> np.ndarray:
+    """Groups as a contiguous int32 array [n, 4] of (seq, depth, row_start,
+    n_rows), the memory layout of ripe_group_t.  Pack once and reuse it to
+    keep per-call host work minimal."""
+    if isinstance(groups, np.ndarray):
+        arr = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 4)
+        return arr
+    rows = []
+    for g in groups:
         if isinstance(g, tuple):
-            seq, depth, row_start, n_rows = g
+            rows.append(g)
         else:
-            seq, depth, row_start, n_rows = g.seq, g.depth, g.row_start, g.n_rows
-        arr[i] = ripe_group_t(int(seq), int(depth), int(row_start), int(n_rows))
-    return arr, len(gl)
+            rows.append((g.seq, g.depth, g.row_start, g.n_rows))
+    return np.ascontiguousarray(np.array(rows, dtype=np.int32).reshape(-1, 4))
+
+
+def _groups(groups):
+    arr = groups if (isinstance(groups, np.ndarray) and groups.dtype == np.int32
+                     and groups.ndim == 2 and groups.flags["C_CONTIGUOUS"]) else pack_groups(groups)
+    return arr.ctypes.data_as(ctypes.POINTER(ripe_group_t)), arr.shape[0], arr
 
 
 def ripe_layout_bytes(desc: ripe_desc_t, kind: int = RIPE_BYTES_CACHE) -> int:
@@ -123,12 +133,15 @@ def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: I
                      n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
                      workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
     """Launch verification attention (asynchronous on ``stream``)."""
-    sl = _i32(seq_len, desc.batch)
-    garr, ng = _groups(groups)
+    sl = seq_len if (isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32
+                     and seq_len.flags["C_CONTIGUOUS"]) else _i32(seq_len, desc.batch)
+    if sl.size != desc.batch:
+        raise ValueError("seq_len must have one entry per sequence")
+    gptr, ng, _keep = _groups(groups)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.ripe_verify_attn(ctypes.byref(desc), _ptr(cache),
-                              sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr, ng,
+                              sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr, ng,
                               int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
                               _ptr(lse), _ptr(plane_sel), _ptr(workspace), int(workspace_bytes),
                               _stream(stream))

@@ -20,7 +20,7 @@
 #include "ripe.h"
 
 namespace ripe {
-hipError_t launch_verify(const VerifyParams& p, int dtype, int D, int NB, hipStream_t stream);
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, int dtype, int D, int NB, hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream);
 }  // namespace ripe
 
@@ -29,7 +29,7 @@ namespace {
 using namespace ripe;
 
 constexpr int64_t kMaxBytes = int64_t(1) << 50;   // sanity bound on any buffer size
-constexpr int64_t kMaxItems = int64_t(1) << 30;   // commit work items per launch
+constexpr int64_t kMaxCommitItems = int64_t(1) << 30;  // commit work items per launch
 constexpr int kMaxCQ = 32;                        // query columns per verify work-group
 
 int elem_bytes(int dtype) { return dtype == RIPE_F32 ? 4 : 2; }
@@ -102,16 +102,32 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   per_seq += groups + (rows + S - 1) / S;
   const int64_t col_chunks = (rows * G + 15) / 16 + nseq;
   const long double slots = (long double)d.n_kv_heads * col_chunks * per_seq;
-  const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4;
+  const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4 + 256;
   if (bytes > (long double)kMaxBytes) return -1;
-  return int64_t(bytes) + 256;
+  return int64_t(bytes);
 }
 
 struct LaunchPlan {
   VerifyParams p;
-  int NB;
-  int64_t ws_bytes;
+  ItemTable t;
+  int64_t part_bytes;  // split partials
 };
+
+// Per-thread planning buffers, reused across calls (no per-call allocation
+// once they have grown to the call sizes in use).
+struct VerifyScratch {
+  std::vector<std::pair<int, int>> spans;
+  std::vector<int> count, fill, order;
+  std::vector<Seg> segs;
+  std::vector<Item> tail;
+  std::vector<LaunchPlan> plans;
+  int n_plans = 0;
+};
+
+VerifyScratch& verify_scratch() {
+  thread_local VerifyScratch sc;
+  return sc;
+}
 
 }  // namespace
 
@@ -146,8 +162,8 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   for (int b = 0; b < d.batch; ++b)
     if (seq_len[b] < 0 || seq_len[b] > d.t_max) return RIPE_ERANGE;
   const int G = d.n_q_heads / d.n_kv_heads;
-  std::vector<std::pair<int, int>> spans;  // (row_start, n_rows) for the overlap check
-  spans.reserve(n_groups);
+  VerifyScratch& sc = verify_scratch();
+  sc.spans.clear();
   for (int i = 0; i < n_groups; ++i) {
     const ripe_group_t& g = groups[i];
     if (g.n_rows < 1) return RIPE_EINVAL;
@@ -155,21 +171,29 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
         int64_t(g.row_start) + g.n_rows > n_rows)
       return RIPE_ERANGE;
     if (g.n_rows > 65535) return RIPE_EUNSUPPORTED;
-    spans.emplace_back(g.row_start, g.n_rows);
+    sc.spans.emplace_back(g.row_start, g.n_rows);
   }
-  std::sort(spans.begin(), spans.end());
-  for (size_t i = 1; i < spans.size(); ++i)
-    if (spans[i - 1].first + spans[i - 1].second > spans[i].first) return RIPE_EINVAL;
+  std::sort(sc.spans.begin(), sc.spans.end());
+  for (size_t i = 1; i < sc.spans.size(); ++i)
+    if (sc.spans[i - 1].first + sc.spans[i - 1].second > sc.spans[i].first) return RIPE_EINVAL;
 
-  // groups of each sequence, in the caller's order
-  std::vector<std::vector<int>> by_seq(d.batch);
-  for (int i = 0; i < n_groups; ++i) by_seq[groups[i].seq].push_back(i);
+  // groups of each sequence in the caller's order (counting sort by sequence)
+  sc.count.assign(d.batch + 1, 0);
+  for (int i = 0; i < n_groups; ++i) ++sc.count[groups[i].seq + 1];
+  for (int b = 0; b < d.batch; ++b) sc.count[b + 1] += sc.count[b];  // count[b] = first index of b
+  sc.order.resize(n_groups);
+  sc.fill.assign(sc.count.begin(), sc.count.end() - 1);
+  for (int i = 0; i < n_groups; ++i) sc.order[sc.fill[groups[i].seq]++] = i;
+  int NB = 1;
   for (int b = 0; b < d.batch; ++b) {
-    if (by_seq[b].size() > size_t(kMaxGroups)) return RIPE_EUNSUPPORTED;
+    const int cnt = sc.count[b + 1] - sc.count[b];
+    if (cnt > kMaxGroups) return RIPE_EUNSUPPORTED;
     int64_t nq = 0;
-    for (int i : by_seq[b]) nq += int64_t(groups[i].n_rows) * G;
+    for (int k = sc.count[b]; k < sc.count[b + 1]; ++k) nq += int64_t(groups[sc.order[k]].n_rows) * G;
     if (nq > 65535) return RIPE_EUNSUPPORTED;
+    if (nq > 16) NB = 2;  // query-column chunks of 32 if any sequence needs more than 16
   }
+  const int CQ = 16 * NB;
 
   const int D = d.head_dim;
   const int We = ring_width(d);
@@ -179,11 +203,12 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   const char* cache_k = static_cast<const char*>(cache);
   const char* cache_v = cache_k + size_t(reg) * E;
 
-  std::vector<LaunchPlan> plans;
-  int b = 0;
-  while (b < d.batch) {
-    LaunchPlan lp;
-    std::memset(&lp.p, 0, sizeof(lp.p));
+  // Pack (sequence, KV-head range) pieces into launches of <= kMaxItems
+  // items, <= kMaxSeq sequence records and <= kMaxGroups group records.
+  sc.n_plans = 0;
+  auto new_plan = [&]() -> LaunchPlan& {
+    if (sc.plans.size() <= size_t(sc.n_plans)) sc.plans.emplace_back();
+    LaunchPlan& lp = sc.plans[sc.n_plans++];
     VerifyParams& p = lp.p;
     p.cache_k = cache_k;
     p.cache_v = cache_v;
@@ -204,72 +229,113 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
     p.G = G;
     p.n_rows = n_rows;
     p.S = S;
+    p.n_seq = 0;
+    p.n_wg = 0;
+    p.n_units = 0;
+    p.n_grp = 0;
     p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
-    int n_seq = 0, n_grp = 0;
-    bool wide = false;
-    for (; b < d.batch; ++b) {
-      const int cnt = int(by_seq[b].size());
-      if (cnt == 0) continue;
-      if (n_seq == kMaxSeq || n_grp + cnt > kMaxGroups) break;
-      SeqRec& sr = p.seq[n_seq];
-      sr.T = seq_len[b];
+    return lp;
+  };
+  LaunchPlan* cur = nullptr;
+  GroupRec grp[kMaxGroups];
+  for (int b = 0; b < d.batch; ++b) {
+    const int g0 = sc.count[b], gc = sc.count[b + 1] - sc.count[b];
+    if (gc == 0) continue;
+    int nq = 0;
+    for (int k = 0; k < gc; ++k) {
+      const ripe_group_t& g = groups[sc.order[g0 + k]];
+      grp[k].row_start = g.row_start;
+      grp[k].n_rows = uint16_t(g.n_rows);
+      grp[k].depth = uint8_t(g.depth);
+      grp[k].seq = 0;
+      nq += g.n_rows * G;
+    }
+    const int T = seq_len[b];
+    sc.segs.clear();
+    int64_t n_split = 0;
+    enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, [&](const Seg& sg) {
+      sc.segs.push_back(sg);
+      n_split += (int64_t(sg.len) + S - 1) / S;
+      return false;
+    });
+    const int n_cc = (nq + CQ - 1) / CQ;
+    const int64_t per_head = n_split * n_cc;
+    if (per_head > kMaxItems) return RIPE_EUNSUPPORTED;  // one KV head must fit a launch
+    int h = 0;
+    while (h < d.n_kv_heads) {
+      if (cur == nullptr || cur->p.n_seq == kMaxSeq || cur->p.n_grp + gc > kMaxGroups ||
+          cur->p.n_wg + per_head > kMaxItems)
+        cur = &new_plan();
+      VerifyParams& p = cur->p;
+      const int hc = int(std::min<int64_t>((kMaxItems - p.n_wg) / per_head, d.n_kv_heads - h));
+      SeqRec& sr = p.seq[p.n_seq];
+      sr.T = T;
       sr.b = uint16_t(b);
-      sr.g_begin = uint8_t(n_grp);
-      sr.g_count = uint8_t(cnt);
-      int nq = 0;
-      for (int i : by_seq[b]) {
-        GroupRec& gr = p.grp[n_grp];
-        gr.row_start = groups[i].row_start;
-        gr.n_rows = uint16_t(groups[i].n_rows);
-        gr.depth = uint8_t(groups[i].depth);
-        gr.seq = uint8_t(n_seq);
-        p.gorig[n_grp] = uint16_t(i);
-        nq += groups[i].n_rows * G;
-        ++n_grp;
-      }
       sr.nq = uint16_t(nq);
-      wide |= nq > 16;
-      ++n_seq;
-    }
-    if (n_seq == 0) break;
-    p.n_seq = n_seq;
-    p.n_grp = n_grp;
-    lp.NB = wide ? 2 : 1;
-    const int CQ = 16 * lp.NB;
-    int64_t wg = 0, parts = 0, mwg = 0;
-    for (int s = 0; s < n_seq; ++s) {
-      SeqRec& sr = p.seq[s];
-      int64_t n_pre = 0, n_split = 0;
-      enumerate_segments(d.layout, d.R, We, sr.T, p.grp, sr.g_begin, sr.g_count, [&](const Seg& sg) {
-        const int64_t nch = (int64_t(sg.len) + S - 1) / S;
-        if (sg.kind == kSegPlane) n_pre += nch;
-        n_split += nch;
-        return false;
-      });
-      const int n_cc = (sr.nq + CQ - 1) / CQ;
       sr.n_cc = uint16_t(n_cc);
-      sr.n_pre = int32_t(n_pre);
       sr.n_split = int32_t(n_split);
-      sr.wg0 = int32_t(wg);
-      sr.part0 = int32_t(parts);
-      sr.mwg0 = int32_t(mwg);
-      wg += n_split * d.n_kv_heads * n_cc;
-      parts += n_split * d.n_kv_heads * n_cc;
-      mwg += int64_t(d.n_kv_heads) * n_cc;
-      if (wg > INT32_MAX || parts > INT32_MAX) return RIPE_EUNSUPPORTED;
+      sr.h0 = uint16_t(h);
+      sr.h_cnt = uint16_t(hc);
+      sr.g_begin = uint8_t(p.n_grp);
+      sr.g_count = uint8_t(gc);
+      sr.part0 = p.n_wg;  // one partial per item
+      sr.unit0 = p.n_units;
+      for (int k = 0; k < gc; ++k) {
+        p.grp[p.n_grp] = grp[k];
+        p.grp[p.n_grp].seq = uint8_t(p.n_seq);
+        p.gorig[p.n_grp] = uint16_t(sc.order[g0 + k]);
+        ++p.n_grp;
+      }
+      // items: unit (h, cc) and chunk `split` of the sequence's segment list;
+      // partial slot = part0 + ((h - h0) * n_cc + cc) * n_split + split
+      for (int hh = 0; hh < hc; ++hh)
+        for (int cc = 0; cc < n_cc; ++cc) {
+          int split = 0;
+          for (const Seg& sg : sc.segs) {
+            for (int c0 = 0; c0 < sg.len; c0 += S, ++split) {
+              Item& it = cur->t.item[p.n_wg++];
+              it.c0 = c0;
+              it.seg_len = sg.len;
+              it.part = sr.part0 + (hh * n_cc + cc) * int(n_split) + split;
+              it.h = uint16_t(h + hh);
+              it.cc = uint16_t(cc);
+              it.s = uint8_t(p.n_seq);
+              it.kind = uint8_t(sg.kind);
+              it.depth = uint8_t(sg.depth);
+              it.gidx = uint8_t(sg.kind == kSegDraft ? sr.g_begin + sg.gidx : 0);
+            }
+          }
+        }
+      p.n_units += hc * n_cc;
+      ++p.n_seq;
+      h += hc;
     }
-    p.n_wg = int32_t(wg);
-    p.n_mwg = int32_t(mwg);
-    lp.ws_bytes = parts * CQ * (D + 2) * 4;
-    plans.push_back(lp);
   }
-  for (const LaunchPlan& lp : plans) {
-    if (lp.ws_bytes > 0 && (workspace == nullptr || size_t(lp.ws_bytes) > workspace_bytes))
-      return RIPE_EWORKSPACE;
+  for (int pi = 0; pi < sc.n_plans; ++pi) {
+    LaunchPlan& lp = sc.plans[pi];
+    // dispatch order: full-length chunks first (creation order), then the
+    // shorter items longest first, so that no long item starts late
+    Item* items = lp.t.item;
+    const int n = lp.p.n_wg;
+    sc.tail.clear();
+    int w = 0;
+    for (int i = 0; i < n; ++i) {
+      if (std::min(S, items[i].seg_len - items[i].c0) == S)
+        items[w++] = items[i];
+      else
+        sc.tail.push_back(items[i]);
+    }
+    std::stable_sort(sc.tail.begin(), sc.tail.end(), [&](const Item& x, const Item& y) {
+      return x.seg_len - x.c0 > y.seg_len - y.c0;
+    });
+    std::copy(sc.tail.begin(), sc.tail.end(), items + w);
+    lp.part_bytes = int64_t(n) * CQ * (D + 2) * 4;
+    if (workspace == nullptr || size_t(lp.part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  for (const LaunchPlan& lp : plans) {
-    const ripe_status_t st2 = hip_status(launch_verify(lp.p, d.dtype, D, lp.NB, hs), "ripe_verify_attn");
+  for (int pi = 0; pi < sc.n_plans; ++pi) {
+    const LaunchPlan& lp = sc.plans[pi];
+    const ripe_status_t st2 = hip_status(launch_verify(lp.p, lp.t, d.dtype, D, NB, hs), "ripe_verify_attn");
     if (st2 != RIPE_OK) return st2;
   }
   return RIPE_OK;
@@ -308,7 +374,7 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
   auto add = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes) {
     // cut rows so that no job exceeds the per-launch item budget
     const int64_t per_row = per_row_plane * n_planes;
-    const int max_rows = int(std::max<int64_t>(1, kMaxItems / per_row));
+    const int max_rows = int(std::max<int64_t>(1, kMaxCommitItems / per_row));
     for (int r0 = 0; r0 < n; r0 += max_rows) {
       const int cnt = std::min(max_rows, n - r0);
       jobs.push_back(Job{b, j0 + r0, src0 + r0, cnt, plane_lo, n_planes});
@@ -350,7 +416,7 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
     for (; i < jobs.size() && nj < kMaxJobs; ++i) {
       const Job& jb = jobs[i];
       const int64_t cnt = int64_t(jb.n) * jb.n_planes * per_row_plane;
-      if (nj > 0 && items + cnt > kMaxItems) break;
+      if (nj > 0 && items + cnt > kMaxCommitItems) break;
       CommitJob& cj = p.job[nj++];
       cj.item0 = int32_t(items);
       cj.j0 = jb.j0;

@@ -33,18 +33,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSeq = 64;      // sequences per launch
 constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
+constexpr int kMaxItems = 1024;  // verify work items per launch
 
 enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
 
-struct SeqRec {        // one sequence of a launch (32 bytes)
+struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   int32_t T;           // committed prefix length
-  int32_t wg0;         // first verify work-group
-  int32_t part0;       // first split partial slot
-  int32_t mwg0;        // first merge work-group
-  int32_t n_pre;       // chunks of kind-0 segments
+  int32_t part0;       // first split partial slot of its units
+  int32_t unit0;       // first (KV head, column chunk) unit
   int32_t n_split;     // chunks of all segments
   uint16_t b;          // sequence index within the cache
   uint16_t n_cc;       // query-column chunks
+  uint16_t h0;         // first KV head of this launch's range
+  uint16_t h_cnt;      // KV heads in the range
   uint8_t g_begin;     // first group record of this sequence
   uint8_t g_count;     // its number of groups
   uint16_t nq;         // query columns = sum(rows) * (Hq / Hkv)
@@ -55,6 +56,25 @@ struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
   uint16_t n_rows;
   uint8_t depth;
   uint8_t seq;         // launch-local sequence index
+};
+
+// One verify work item: a chunk of <= S positions of one segment of one
+// sequence, for one KV head and one query-column chunk (20 bytes).
+struct Item {
+  int32_t c0;          // chunk start, segment-local
+  int32_t seg_len;     // segment length
+  int32_t part;        // split partial slot
+  uint16_t h;          // KV head
+  uint16_t cc;         // query-column chunk
+  uint8_t s;           // launch-local sequence
+  uint8_t kind;        // SegKind
+  uint8_t depth;       // plane read (kind 0) or depth r (kinds 1, 2)
+  uint8_t gidx;        // group record (kind 2)
+};
+
+// Work items of one launch, largest first (one work-group each).
+struct ItemTable {
+  Item item[kMaxItems];
 };
 
 struct Seg {
@@ -72,9 +92,9 @@ struct VerifyParams {
   void* out;
   float* lse;
   int8_t* plane_sel;
-  float* ws;
+  float* ws;             // split partials
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
-  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, S, n_seq, n_wg, n_mwg, n_grp;
+  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, S, n_seq, n_wg, n_units, n_grp;
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];

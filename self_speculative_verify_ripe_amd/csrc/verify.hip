@@ -10,23 +10,22 @@
 // with KV head h / (Hq / Hkv).
 //
 // How (split-K / flash-decoding):
-//   verify_partial  one work-group (4 wavefronts) per (sequence, KV head,
-//                   query-column chunk, chunk of <= S key positions of one
-//                   segment).  Each wavefront streams 32-position steps
-//                   straight from HBM into VGPRs in MFMA operand order:
-//                   K rows (row-major [pos][D]) feed the A operand of
-//                   S^T = K Q^T, and the V blocks (stored transposed,
-//                   [D][32] per 32 positions) feed the A operand of
-//                   O^T += V^T P^T, so no LDS staging or shuffles are needed
-//                   on the hot loop.  The next step's K/V loads are issued
-//                   before the current step's MFMAs.  Online softmax in the
-//                   log2 domain with one max reduction per step.  The four
-//                   wavefronts' (m, l, O) are merged through LDS and written
-//                   as one fp32 partial per work-item.
-//   verify_merge    one work-group per (sequence, KV head, column chunk)
-//                   merges the partials in split order, normalises, writes
-//                   out (storage dtype, round-to-nearest-even) and the
-//                   natural-log LSE; extra work-groups write plane_sel.
+//   one work-group (4 wavefronts) per (sequence, KV head, query-column
+//   chunk, chunk of <= S key positions of one segment).  Each wavefront
+//   streams 32-position steps straight from HBM into VGPRs in MFMA operand
+//   order: K rows (row-major [pos][D]) feed the A operand of S^T = K Q^T, and
+//   the V blocks (stored transposed, [D][32] per 32 positions) feed the A
+//   operand of O^T += V^T P^T, so no LDS staging or shuffles are needed on
+//   the hot loop.  The next step's K (V) loads are issued as soon as the
+//   current step's K (V) registers are consumed.  Online softmax in the log2
+//   domain with one max reduction per step.  The four wavefronts' (m, l, O)
+//   are merged through LDS into one fp32 partial per work item.  A second
+//   kernel, one work-group per (sequence, KV head, column chunk), merges the
+//   partials in split order, normalises, and writes out (storage dtype,
+//   round-to-nearest-even), the natural-log LSE and plane_sel.  (The merge
+//   is not folded into the first kernel: cross-work-group hand-off on this
+//   multi-die part needs a device-scope fence per work-group, i.e. an L2
+//   writeback and invalidate each, which costs far more than the launch.)
 //
 // MFMA shapes: bf16 v_mfma_f32_16x16x32_bf16 (8 bf16 per lane per operand);
 // fp32 v_mfma_f32_16x16x4_f32 (no reduced-precision path).  For the
@@ -145,19 +144,6 @@ __device__ inline float wave_sum_lanegroups(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
   return x;
-}
-
-__device__ inline int find_seq_by(const VerifyParams& p, int idx, bool merge) {
-  int lo = 0, hi = p.n_seq - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const int start = merge ? p.seq[mid].mwg0 : p.seq[mid].wg0;
-    if (start <= idx)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
 }
 
 // Locate the group, row and head-in-group of query column `col` of sequence
@@ -301,10 +287,22 @@ constexpr int waves_per_simd() {
   return (sizeof(T) == 4 && D == 128 && NB == 2) ? RIPE_FP32_WAVES : 2;
 }
 
+// LDS bytes of the verify kernel: the four wavefronts' (m, l, O) for the
+// merge, which the draft-row path also uses, one slice per wavefront, to
+// transpose V rows.
+template <typename T, int D, int NB>
+constexpr int verify_lds_bytes() {
+  constexpr int merge = kWaves * 16 * NB * (D + 4) * 4 + 2 * kWaves * 16 * NB * 4;
+  constexpr int draft = kWaves * kStep * D * int(sizeof(T));
+  return merge > draft ? merge : draft;
+}
+
+// One work-group per work item (sequence, KV head, query-column chunk, chunk
+// of <= S key positions of one segment); see the file comment.
 template <typename T, int D, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
-void verify_partial(const VerifyParams p) {
+void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   using O = Op<T>;
   constexpr int VEC = O::VEC;
   constexpr int VCH = O::VCH;
@@ -312,48 +310,27 @@ void verify_partial(const VerifyParams p) {
   constexpr int DB = D / 16;         // 16-wide head-dim blocks of the output
   constexpr int CQ = 16 * NB;        // query columns per work-group
   constexpr int E = sizeof(T);
+  constexpr int TPC = kThreads / CQ;  // epilogue threads per column
+  constexpr int DPT = D / TPC;        // head-dim values per epilogue thread
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 15;
   const int lg = lane >> 4;
 
-  // ---- which work item -------------------------------------------------
-  const int s = find_seq_by(p, blockIdx.x, false);
-  const SeqRec& sr = p.seq[s];
-  int local = blockIdx.x - sr.wg0;
-  const int n_cc = sr.n_cc;
-  const int cc = local % n_cc;
-  local /= n_cc;
-  const int h = local % p.H;
-  const int chunk = local / p.H;
-
-  Seg seg{0, 0, -1, 0};
-  int chunk_in = 0;
-  {
-    int acc = 0;
-    const int S = p.S;
-    enumerate_segments(p.layout, p.R, p.We, sr.T, p.grp, sr.g_begin, sr.g_count, [&](const Seg& sg) {
-      const int nch = ceil_div(sg.len, S);
-      if (chunk < acc + nch) {
-        seg = sg;
-        chunk_in = chunk - acc;
-        return true;
-      }
-      acc += nch;
-      return false;
-    });
-  }
-  // every quantity below is wave-uniform; say so, so that buffer
-  // descriptors and loop bounds live in scalar registers
-  seg.kind = __builtin_amdgcn_readfirstlane(seg.kind);
-  seg.depth = __builtin_amdgcn_readfirstlane(seg.depth);
-  seg.gidx = __builtin_amdgcn_readfirstlane(seg.gidx);
-  seg.len = __builtin_amdgcn_readfirstlane(seg.len);
-  chunk_in = __builtin_amdgcn_readfirstlane(chunk_in);
-  const int c0 = chunk_in * p.S;
-  const int clen = min(p.S, seg.len - c0);
+  // ---- this work item (host-planned; wave-uniform) ----------------------
+  const Item it = tab.item[blockIdx.x];
+  const int s = it.s;
+  const SeqRec sr = p.seq[s];
+  const int h = it.h;
+  const int cc = it.cc;
+  const int kind = it.kind;
+  const int sdepth = it.depth;
+  const int sgidx = it.gidx;
+  const int c0 = it.c0;
+  const int seg_len = it.seg_len;
+  const int clen = min(p.S, seg_len - c0);
   const int nsteps = ceil_div(clen, kStep);
-  const int seg_len = seg.len;
+  const int Wb = min(p.We, sr.T);
 
   // ---- query columns of this lane ---------------------------------------
   // Straight-line on purpose: every lane loads from a valid address and
@@ -361,54 +338,53 @@ void verify_partial(const VerifyParams p) {
   // control flow.
   int hi[NB];  // visible segment-local positions are < hi
   u32x4 qf[NB][KC];
-  const int Wb = min(p.We, sr.T);
+  auto setup_columns = [&]() {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = cc * CQ + ln + 16 * nb;
-    int row = 0, hh = 0;
-    const int gi = column_group(p, sr, col, row, hh);
-    const bool valid = gi >= 0;
-    const GroupRec& g = p.grp[valid ? gi : sr.g_begin];
-    const T* qp = static_cast<const T*>(p.q) + (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = cc * CQ + ln + 16 * nb;
+      int row = 0, hh = 0;
+      const int gi = column_group(p, sr, col, row, hh);
+      const bool valid = gi >= 0;
+      const GroupRec& g = p.grp[valid ? gi : sr.g_begin];
+      const T* qp = static_cast<const T*>(p.q) + (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 v = ld16(qp + c * 4 * VEC + lg * VEC);
-      qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 v = ld16(qp + c * 4 * VEC + lg * VEC);
+        qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      const int gd = g.depth;
+      const int h_plane = (p.layout == 0) ? (gd == sdepth ? sr.T : 0)
+                          : (p.layout == 1) ? sr.T
+                                            : (gd == p.R ? sr.T : sr.T - Wb);
+      const int h_ring = (gd == sdepth) ? Wb : 0;
+      const int h_draft = (gi == sgidx) ? row + 1 : 0;
+      const int hv = (kind == kSegPlane) ? h_plane : (kind == kSegRing) ? h_ring : h_draft;
+      hi[nb] = valid ? hv : 0;
     }
-    const int gd = g.depth;
-    const int h_plane = (p.layout == 0) ? (gd == seg.depth ? sr.T : 0)
-                        : (p.layout == 1) ? sr.T
-                                          : (gd == p.R ? sr.T : sr.T - Wb);
-    const int h_ring = (gd == seg.depth) ? Wb : 0;
-    const int h_draft = (gi == seg.gidx) ? row + 1 : 0;
-    const int hv = (seg.kind == kSegPlane) ? h_plane : (seg.kind == kSegRing) ? h_ring : h_draft;
-    hi[nb] = valid ? hv : 0;
-  }
+  };
 
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
   Softmax<T, D, NB> sm;
   sm.init();
   const float sl2 = p.scale_log2;
 
-  if (seg.kind != kSegDraft) {
+  if (kind != kSegDraft) {
     // ---- prefix plane or window ring: streamed with buffer loads ----------
     size_t off;
     int bw = kStep;
-    if (seg.kind == kSegPlane) {
+    if (kind == kSegPlane) {
       if (p.layout == 0)
-        off = ((size_t(sr.b) * p.R + (seg.depth - 1)) * p.H + h) * size_t(p.t_max) * D;
+        off = ((size_t(sr.b) * p.R + (sdepth - 1)) * p.H + h) * size_t(p.t_max) * D;
       else
         off = (size_t(sr.b) * p.H + h) * size_t(p.t_max) * D;
     } else {
-      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (seg.depth - 1)) * p.H + h) * size_t(p.We) * D;
+      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (sdepth - 1)) * p.H + h) * size_t(p.We) * D;
       bw = p.BW;
     }
-    off = uniform_u64(off);
-    bw = __builtin_amdgcn_readfirstlane(bw);
     const T* kb = static_cast<const T*>(p.cache_k) + off;
     const T* vb = static_cast<const T*>(p.cache_v) + off;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, uint32_t(seg_len) * D * E);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, uint32_t(ceil_div(seg_len, bw)) * bw * D * E);
-    // lane-constant parts of the byte offsets
     const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
     const uint32_t koff = (krow * D + lg * VEC) * E;
     // A step index past the chunk maps to an offset beyond the buffer's
@@ -431,57 +407,77 @@ void verify_partial(const VerifyParams p) {
 #pragma unroll
         for (int v = 0; v < VCH; ++v) vf[db][v] = bload16(vrs, base + (16 * db * bw + v * VEC) * E);
     };
-    if (wave < nsteps) {
-      u32x4 kf[2][KC], vf[DB][VCH];
-      load_k(wave, true, kf);
-      load_v(wave, true, vf);
-      for (int st = wave; st < nsteps; st += kWaves) {
-        const bool more = st + kWaves < nsteps;
-        floatx4 sacc[2][NB];
-        qk<T, D, NB>(kf, qf, sacc);
-        load_k(st + kWaves, more, kf);
-        int lim[NB];
+    // first step's loads go out before the query setup
+    u32x4 kf[2][KC], vf[DB][VCH];
+    const bool any = wave < nsteps;
+    load_k(wave, any, kf);
+    load_v(wave, any, vf);
+    setup_columns();
+    for (int st = wave; st < nsteps; st += kWaves) {
+      const bool more = st + kWaves < nsteps;
+      floatx4 sacc[2][NB];
+      qk<T, D, NB>(kf, qf, sacc);
+      load_k(st + kWaves, more, kf);
+      int lim[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - (c0 + st * kStep);
-        typename O::P pf[NB];
-        sm.update(sacc, lim, sl2, pf);
-        // a step reaching past the segment's end: zero the V values of the
-        // missing positions (they may hold anything, even NaN)
-        if (c0 + (st + 1) * kStep > seg_len) {
-          const int nval = seg_len - (c0 + st * kStep + 8 * lg);
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - (c0 + st * kStep);
+      typename O::P pf[NB];
+      sm.update(sacc, lim, sl2, pf);
+      // a step reaching past the segment's end: zero the V values of the
+      // missing positions (they may hold anything, even NaN)
+      if (c0 + (st + 1) * kStep > seg_len) {
+        const int nval = seg_len - (c0 + st * kStep + 8 * lg);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
-        }
-        sm.pv(vf, pf);
-        load_v(st + kWaves, more, vf);
+        for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
       }
+      sm.pv(vf, pf);
+      load_v(st + kWaves, more, vf);
     }
   } else {
-    // ---- a group's own draft rows: gathered from kv_new -------------------
-    const GroupRec& g = p.grp[seg.gidx];
+    // ---- a group's own draft rows (kv_new, row-major): K rows are loaded
+    // in MFMA order directly; V rows are staged in this wavefront's LDS slice
+    // with 16-byte loads and read back transposed.
+    setup_columns();
+    const GroupRec& g = p.grp[sgidx];
     const int Hd = p.H * D;
-    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(seg.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(sdepth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
     const T* vb = static_cast<const T*>(p.kv_new) +
-                  (size_t(p.R + seg.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+                  (size_t(p.R + sdepth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
+    constexpr int CPR = D / VEC;  // 16-byte pieces per row
     for (int st = wave; st < nsteps; st += kWaves) {
       u32x4 kf[2][KC], vf[DB][VCH];
       const int base = c0 + st * kStep;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int pos = base + 8 * (ln >> 2) + 4 * mb + (ln & 3);
-        const T* rp = kb + size_t(pos) * Hd + lg * VEC;
+        const bool ok = pos < seg_len;
+        const T* rp = kb + size_t(ok ? pos : 0) * Hd + lg * VEC;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) kf[mb][c] = pos < seg_len ? ld16(rp + c * 4 * VEC) : u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < KC; ++c) {
+          const u32x4 v = ld16(rp + c * 4 * VEC);
+          kf[mb][c] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
       }
-      const int slot0 = base + 8 * lg;
+      // stage V rows [base, base + 32) of this head: piece i = (row, 16 B)
+#pragma unroll
+      for (int i = lane; i < kStep * CPR; i += 64) {
+        const int r = i / CPR;
+        const int c = i - r * CPR;
+        const bool ok = base + r < seg_len;
+        const u32x4 v = ld16(vb + size_t(ok ? base + r : 0) * Hd + c * VEC);
+        *reinterpret_cast<u32x4*>(stage + r * D + c * VEC) = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged rows are in LDS
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int v = 0; v < VCH; ++v) vf[db][v] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (slot0 + e < seg_len) O::put_elem(vf[db], e, vb, size_t(slot0 + e) * Hd + 16 * db + ln);
+        for (int e = 0; e < 8; ++e) O::put_elem(vf[db], e, stage, size_t(8 * lg + e) * D + 16 * db + ln);
       }
+      __builtin_amdgcn_wave_barrier();
       floatx4 sacc[2][NB];
       qk<T, D, NB>(kf, qf, sacc);
       int lim[NB];
@@ -494,9 +490,11 @@ void verify_partial(const VerifyParams p) {
   }
 
   // ---- merge the four wavefronts through LDS, write one partial ----------
-  __shared__ float lds_o[kWaves][CQ][D + 4];
-  __shared__ float lds_m[kWaves][CQ];
-  __shared__ float lds_l[kWaves][CQ];
+  __syncthreads();  // the draft path's staging slices are reused below
+  typedef float OSlice[CQ][D + 4];
+  OSlice* lds_o = reinterpret_cast<OSlice*>(lds_raw);
+  float (*lds_m)[CQ] = reinterpret_cast<float (*)[CQ]>(lds_raw + kWaves * sizeof(OSlice));
+  float (*lds_l)[CQ] = lds_m + kWaves;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float lt = wave_sum_lanegroups(sm.l[nb]);
@@ -510,8 +508,6 @@ void verify_partial(const VerifyParams p) {
     }
   }
   __syncthreads();
-  constexpr int TPC = kThreads / CQ;  // threads per column
-  constexpr int DPT = D / TPC;        // head-dim values per thread
   const int col = threadIdx.x / TPC;
   const int d0 = (threadIdx.x % TPC) * DPT;
   if (cc * CQ + col >= sr.nq) return;
@@ -527,7 +523,7 @@ void verify_partial(const VerifyParams p) {
     L += f[w] * lds_l[w][col];
   }
   const size_t stride = size_t(CQ) * (D + 2);
-  float* part = p.ws + (size_t(sr.part0) + (size_t(h) * n_cc + cc) * sr.n_split + chunk) * stride;
+  float* part = p.ws + size_t(it.part) * stride;
 #pragma unroll
   for (int d = 0; d < DPT; d += 4) {
     floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -541,127 +537,124 @@ void verify_partial(const VerifyParams p) {
   }
 }
 
+// One work-group per (sequence, KV head, query-column chunk): merges the
+// unit's split partials in split order, normalises and writes out, lse and
+// (unit h 0, chunk 0) the sequence's plane_sel rows.
 template <typename T, int D, int NB>
-__global__ __launch_bounds__(kThreads) void verify_merge(const VerifyParams p) {
+__global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyParams p) {
   using O = Op<T>;
   constexpr int CQ = 16 * NB;
   constexpr int TPC = kThreads / CQ;
   constexpr int DPT = D / TPC;
-  if (int(blockIdx.x) >= p.n_mwg) {
-    // plane_sel of one group: plane read at each committed position
-    const int gi = blockIdx.x - p.n_mwg;
-    if (p.plane_sel == nullptr || gi >= p.n_grp) return;
-    const GroupRec& g = p.grp[gi];
-    const int Tl = p.seq[g.seq].T;
-    const int Wb = min(p.We, Tl);
-    int8_t* row = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
-    const int r = g.depth;
-    for (int j0 = threadIdx.x * 16; j0 < Tl; j0 += kThreads * 16) {
-      int8_t v[16];
+  const int bid = blockIdx.x;
+  int s = 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + e;
-        int pl;
-        if (p.layout == 0)
-          pl = r;
-        else if (p.layout == 1)
-          pl = p.R;
-        else
-          pl = (j >= Tl - Wb) ? r : p.R;
-        v[e] = int8_t(pl);
-      }
-      if (j0 + 16 <= Tl) {
-        *reinterpret_cast<u32x4*>(row + j0) = *reinterpret_cast<const u32x4*>(v);
-      } else {
-        for (int e = 0; j0 + e < Tl; ++e) row[j0 + e] = v[e];
-      }
-    }
-    return;
-  }
-  const int s = find_seq_by(p, blockIdx.x, true);
-  const SeqRec& sr = p.seq[s];
-  const int local = blockIdx.x - sr.mwg0;
+  for (int i = 1; i < kMaxSeq; ++i) s += (i < p.n_seq && p.seq[i].unit0 <= bid) ? 1 : 0;
+  const SeqRec sr = p.seq[s];
+  const int local = bid - sr.unit0;
   const int n_cc = sr.n_cc;
   const int cc = local % n_cc;
-  const int h = local / n_cc;
+  const int hl = local / n_cc;  // KV head within this launch's range
+  const int h = sr.h0 + hl;
+  const size_t stride = size_t(CQ) * (D + 2);
+  const float* const part_base = p.ws + (size_t(sr.part0) + size_t(hl * n_cc + cc) * sr.n_split) * stride;
+  const int Wb = min(p.We, sr.T);
   const int col = threadIdx.x / TPC;
   const int d0 = (threadIdx.x % TPC) * DPT;
-  int row = 0, hh = 0;
-  const int gi = column_group(p, sr, cc * CQ + col, row, hh);
-  if (gi < 0) return;
-  const size_t stride = size_t(CQ) * (D + 2);
-  const float* base = p.ws + (size_t(sr.part0) + (size_t(h) * n_cc + cc) * sr.n_split) * stride;
-  const int ns = sr.n_split;
-  constexpr int U = 4;  // splits whose loads are issued together
-  float M = -INFINITY;
-  for (int sp = 0; sp < ns; sp += U) {
-    float mm[U];
+  const bool col_valid = cc * CQ + col < sr.nq;
+  if (col_valid) {
+    int row = 0, hh = 0;
+    const int gi = column_group(p, sr, cc * CQ + col, row, hh);
+    const int ns = sr.n_split;
+    constexpr int U = 4;  // splits whose loads are issued together
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; sp += U) {
+      float mm[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      mm[u] = (sp + u < ns) ? base[size_t(sp + u) * stride + size_t(CQ) * D + col] : -INFINITY;
+      for (int u = 0; u < U; ++u)
+        mm[u] = (sp + u < ns) ? part_base[size_t(sp + u) * stride + size_t(CQ) * D + col] : -INFINITY;
 #pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
-  }
-  float L = 0.f;
-  float o[DPT];
-#pragma unroll
-  for (int d = 0; d < DPT; ++d) o[d] = 0.f;
-  for (int sp = 0; sp < ns; sp += U) {
-    float ms[U], ls[U];
-    floatx4 ov[U][DPT / 4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = sp + u < ns;
-      const float* part = base + size_t(ok ? sp + u : 0) * stride;
-      ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
-      ls[u] = part[size_t(CQ) * D + CQ + col];
-#pragma unroll
-      for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+      for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
     }
+    float L = 0.f;
+    float o[DPT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float f = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
-      L += f * ls[u];
+    for (int d = 0; d < DPT; ++d) o[d] = 0.f;
+    for (int sp = 0; sp < ns; sp += U) {
+      float ms[U], ls[U];
+      floatx4 ov[U][DPT / 4];
 #pragma unroll
-      for (int d = 0; d < DPT; d += 4)
+      for (int u = 0; u < U; ++u) {
+        const bool ok = sp + u < ns;
+        const float* part = part_base + size_t(ok ? sp + u : 0) * stride;
+        ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
+        ls[u] = part[size_t(CQ) * D + CQ + col];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[d + e] += f * ov[u][d / 4][e];
+        for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+        L += fs * ls[u];
+#pragma unroll
+        for (int d = 0; d < DPT; d += 4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[d + e] += fs * ov[u][d / 4][e];
+      }
+    }
+    const GroupRec& g = p.grp[gi];
+    const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
+    float res[DPT];
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
+    O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
+    if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
+  }
+  // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0)
+  if (p.plane_sel != nullptr && h == 0 && cc == 0) {
+    for (int gi = sr.g_begin; gi < sr.g_begin + sr.g_count; ++gi) {
+      const int r = p.grp[gi].depth;
+      int8_t* rowp = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
+      for (int j0 = threadIdx.x * 16; j0 < sr.T; j0 += kThreads * 16) {
+        int8_t v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + e;
+          const int pl = (p.layout == 0) ? r : (p.layout == 1) ? p.R : ((j >= sr.T - Wb) ? r : p.R);
+          v[e] = int8_t(pl);
+        }
+        if (j0 + 16 <= sr.T) {
+          *reinterpret_cast<u32x4*>(rowp + j0) = *reinterpret_cast<const u32x4*>(v);
+        } else {
+          for (int e = 0; j0 + e < sr.T; ++e) rowp[j0 + e] = v[e];
+        }
+      }
     }
   }
-  const GroupRec& g = p.grp[gi];
-  const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
-  float res[DPT];
-#pragma unroll
-  for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
-  O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
-  if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
-// launchers
+// launcher
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NB>
-static hipError_t launch_verify_t(const VerifyParams& p, hipStream_t stream) {
-  void* args[] = {const_cast<VerifyParams*>(&p)};
-  if (p.n_wg > 0) {
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_partial<T, D, NB>),
-                                         dim3(p.n_wg), dim3(kThreads), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  const int n2 = p.n_mwg + (p.plane_sel ? p.n_grp : 0);
-  if (n2 > 0)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge<T, D, NB>), dim3(n2),
-                           dim3(kThreads), args, 0, stream);
-  return hipSuccess;
+static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, hipStream_t stream) {
+  if (p.n_wg <= 0) return hipSuccess;
+  void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(p.n_wg),
+                                 dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess) return e;
+  void* margs[] = {const_cast<VerifyParams*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB>), dim3(p.n_units),
+                         dim3(kThreads), margs, 0, stream);
 }
 
-hipError_t launch_verify(const VerifyParams& p, int dtype, int D, int NB, hipStream_t stream) {
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, int dtype, int D, int NB, hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, stream) : launch_verify_t<__bf16, 128, 2>(p, stream);
-    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, stream) : launch_verify_t<__bf16, 64, 2>(p, stream);
+    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, t, stream) : launch_verify_t<__bf16, 128, 2>(p, t, stream);
+    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, t, stream) : launch_verify_t<__bf16, 64, 2>(p, t, stream);
   }
-  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, stream) : launch_verify_t<float, 128, 2>(p, stream);
-  return NB == 1 ? launch_verify_t<float, 64, 1>(p, stream) : launch_verify_t<float, 64, 2>(p, stream);
+  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, stream) : launch_verify_t<float, 128, 2>(p, t, stream);
+  return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, stream) : launch_verify_t<float, 64, 2>(p, t, stream);
 }
 
 }  // namespace ripe

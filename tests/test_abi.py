@@ -87,7 +87,7 @@ def test_bad_kind():
 def call_verify(desc, seq_len, groups, n_rows=16, scale=1.0, cache=FAKE, q=FAKE, kv=FAKE,
                 out=FAKE, lse=None, ps=None, ws=FAKE, ws_bytes=1 << 40):
     sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
-    garr, ng = binding._groups(groups)
+    garr, ng, _keep = binding._groups(groups if len(groups) else np.zeros((0, 4), np.int32))
     return binding.lib.ripe_verify_attn(
         ctypes.byref(desc), cache, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr, ng,
         n_rows, scale, q, kv, out, lse, ps, ws, ws_bytes, None)
