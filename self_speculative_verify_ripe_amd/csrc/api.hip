@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <queue>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -20,7 +21,9 @@
 #include "ripe.h"
 
 namespace ripe {
-hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, int dtype, int D, int NB, hipStream_t stream);
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid, int dtype, int D,
+                         int NB, hipStream_t stream);
+int verify_slots(int dtype, int D, int NB);
 hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream);
 }  // namespace ripe
 
@@ -110,6 +113,8 @@ int64_t workspace_bound(const ripe_desc_t& d) {
 struct LaunchPlan {
   VerifyParams p;
   ItemTable t;
+  UnitTable u;
+  int grid;            // persistent work-groups
   int64_t part_bytes;  // split partials
 };
 
@@ -120,6 +125,7 @@ struct VerifyScratch {
   std::vector<int> count, fill, order;
   std::vector<Seg> segs;
   std::vector<Item> tail;
+  std::vector<int> by_size, bin_of, bin_cnt;
   std::vector<LaunchPlan> plans;
   int n_plans = 0;
 };
@@ -306,36 +312,71 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
             }
           }
         }
+      for (int hh = 0; hh < hc; ++hh)
+        for (int cc = 0; cc < n_cc; ++cc) {
+          Unit& un = cur->u.unit[p.n_units + hh * n_cc + cc];
+          un.s = uint16_t(p.n_seq);
+          un.h = uint16_t(h + hh);
+          un.cc = uint16_t(cc);
+          un.hl = uint16_t(hh);
+        }
       p.n_units += hc * n_cc;
       ++p.n_seq;
       h += hc;
     }
   }
+  // Persistent work-groups: as many as fit on the device at once (at most
+  // kMaxSlots).  Items are assigned longest first to the least-loaded
+  // work-group (cost = 32-position steps + a fixed per-item latency).
   for (int pi = 0; pi < sc.n_plans; ++pi) {
     LaunchPlan& lp = sc.plans[pi];
-    // dispatch order: full-length chunks first (creation order), then the
-    // shorter items longest first, so that no long item starts late
+    lp.part_bytes = int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
+    if (workspace == nullptr || size_t(lp.part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
+  }
+  int slots = sc.n_plans > 0 ? verify_slots(d.dtype, D, NB) : 0;
+  if (slots <= 0) slots = 512;
+  slots = std::min(slots, kMaxSlots);
+  for (int pi = 0; pi < sc.n_plans; ++pi) {
+    LaunchPlan& lp = sc.plans[pi];
     Item* items = lp.t.item;
     const int n = lp.p.n_wg;
-    sc.tail.clear();
-    int w = 0;
-    for (int i = 0; i < n; ++i) {
-      if (std::min(S, items[i].seg_len - items[i].c0) == S)
-        items[w++] = items[i];
-      else
-        sc.tail.push_back(items[i]);
+    auto cost = [&](const Item& it) { return (std::min(S, it.seg_len - it.c0) + kStep - 1) / kStep + 2; };
+    sc.by_size.resize(n);
+    for (int i = 0; i < n; ++i) sc.by_size[i] = i;
+    std::stable_sort(sc.by_size.begin(), sc.by_size.end(),
+                     [&](int x, int y) { return cost(items[x]) > cost(items[y]); });
+    const int W = std::min(n, slots);
+    using Load = std::pair<int64_t, int>;  // (accumulated cost, work-group)
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int w = 0; w < W; ++w) heap.push(Load(0, w));
+    sc.bin_of.resize(n);
+    sc.bin_cnt.assign(W + 1, 0);
+    for (int k = 0; k < n; ++k) {
+      Load top = heap.top();
+      heap.pop();
+      const int i = sc.by_size[k];
+      sc.bin_of[i] = top.second;
+      ++sc.bin_cnt[top.second + 1];
+      top.first += cost(items[i]);
+      heap.push(top);
     }
-    std::stable_sort(sc.tail.begin(), sc.tail.end(), [&](const Item& x, const Item& y) {
-      return x.seg_len - x.c0 > y.seg_len - y.c0;
-    });
-    std::copy(sc.tail.begin(), sc.tail.end(), items + w);
-    lp.part_bytes = int64_t(n) * CQ * (D + 2) * 4;
-    if (workspace == nullptr || size_t(lp.part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
+    for (int w = 0; w < W; ++w) sc.bin_cnt[w + 1] += sc.bin_cnt[w];
+    for (int w = 0; w <= W; ++w) lp.t.first[w] = uint16_t(sc.bin_cnt[w]);
+    // place items by work-group, each work-group's items longest first
+    sc.tail.resize(n);
+    std::vector<int>& fill = sc.fill;
+    fill.assign(sc.bin_cnt.begin(), sc.bin_cnt.end() - 1);
+    for (int k = 0; k < n; ++k) {
+      const int i = sc.by_size[k];
+      sc.tail[fill[sc.bin_of[i]]++] = items[i];
+    }
+    std::copy(sc.tail.begin(), sc.tail.end(), items);
+    lp.grid = W;
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (int pi = 0; pi < sc.n_plans; ++pi) {
     const LaunchPlan& lp = sc.plans[pi];
-    const ripe_status_t st2 = hip_status(launch_verify(lp.p, lp.t, d.dtype, D, NB, hs), "ripe_verify_attn");
+    const ripe_status_t st2 = hip_status(launch_verify(lp.p, lp.t, lp.u, lp.grid, d.dtype, D, NB, hs), "ripe_verify_attn");
     if (st2 != RIPE_OK) return st2;
   }
   return RIPE_OK;

@@ -34,6 +34,7 @@ constexpr int kMaxSeq = 64;      // sequences per launch
 constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
 constexpr int kMaxItems = 1024;  // verify work items per launch
+constexpr int kMaxSlots = 1024;  // persistent verify work-groups per launch
 
 enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
 
@@ -72,9 +73,23 @@ struct Item {
   uint8_t gidx;        // group record (kind 2)
 };
 
-// Work items of one launch, largest first (one work-group each).
+// Work items of one launch, grouped by the work-group that runs them:
+// work-group w runs items first[w] .. first[w + 1] - 1 in order.
 struct ItemTable {
   Item item[kMaxItems];
+  uint16_t first[kMaxSlots + 1];
+};
+
+// (sequence, KV head, column chunk) of each merge work-group (8 bytes).
+struct Unit {
+  uint16_t s;          // launch-local sequence
+  uint16_t h;          // KV head
+  uint16_t cc;         // query-column chunk
+  uint16_t hl;         // KV head within the sequence record's range
+};
+
+struct UnitTable {
+  Unit unit[kMaxItems];
 };
 
 struct Seg {

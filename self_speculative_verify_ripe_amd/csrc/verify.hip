@@ -317,8 +317,15 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   const int ln = lane & 15;
   const int lg = lane >> 4;
 
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
+  // Persistent: as many work-groups as fit on the device at once, each
+  // running the items the host assigned to it (longest-processing-time
+  // first).  Results do not depend on which work-group runs an item.
+  const int item_end = tab.first[blockIdx.x + 1];
+  for (int item = tab.first[blockIdx.x]; item < item_end; ++item) {
+  __syncthreads();  // LDS of the previous item is free
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  const Item it = tab.item[blockIdx.x];
+  const Item it = tab.item[item];
   const int s = it.s;
   const SeqRec sr = p.seq[s];
   const int h = it.h;
@@ -363,7 +370,6 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     }
   };
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
   Softmax<T, D, NB> sm;
   sm.init();
   const float sl2 = p.scale_log2;
@@ -510,52 +516,50 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __syncthreads();
   const int col = threadIdx.x / TPC;
   const int d0 = (threadIdx.x % TPC) * DPT;
-  if (cc * CQ + col >= sr.nq) return;
-  float M = -INFINITY;
+  if (cc * CQ + col < sr.nq) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][col]);
-  float f[kWaves];
-  float L = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][col]);
+    float f[kWaves];
+    float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = lds_m[w][col];
-    f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    L += f[w] * lds_l[w][col];
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = lds_m[w][col];
+      f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += f[w] * lds_l[w][col];
+    }
+    const size_t stride = size_t(CQ) * (D + 2);
+    float* part = p.ws + size_t(it.part) * stride;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4) {
+      floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) o += f[w] * *reinterpret_cast<const floatx4*>(&lds_o[w][col][d0 + d]);
+      *reinterpret_cast<floatx4*>(part + size_t(col) * D + d0 + d) = o;
+    }
+    if (d0 == 0) {
+      part[size_t(CQ) * D + col] = M;
+      part[size_t(CQ) * D + CQ + col] = L;
+    }
   }
-  const size_t stride = size_t(CQ) * (D + 2);
-  float* part = p.ws + size_t(it.part) * stride;
-#pragma unroll
-  for (int d = 0; d < DPT; d += 4) {
-    floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += f[w] * *reinterpret_cast<const floatx4*>(&lds_o[w][col][d0 + d]);
-    *reinterpret_cast<floatx4*>(part + size_t(col) * D + d0 + d) = o;
-  }
-  if (d0 == 0) {
-    part[size_t(CQ) * D + col] = M;
-    part[size_t(CQ) * D + CQ + col] = L;
-  }
+  }  // work items
 }
 
 // One work-group per (sequence, KV head, query-column chunk): merges the
 // unit's split partials in split order, normalises and writes out, lse and
 // (unit h 0, chunk 0) the sequence's plane_sel rows.
 template <typename T, int D, int NB>
-__global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyParams p) {
+__global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyParams p, const UnitTable ut) {
   using O = Op<T>;
   constexpr int CQ = 16 * NB;
   constexpr int TPC = kThreads / CQ;
   constexpr int DPT = D / TPC;
-  const int bid = blockIdx.x;
-  int s = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxSeq; ++i) s += (i < p.n_seq && p.seq[i].unit0 <= bid) ? 1 : 0;
-  const SeqRec sr = p.seq[s];
-  const int local = bid - sr.unit0;
+  const Unit un = ut.unit[blockIdx.x];
+  const SeqRec sr = p.seq[un.s];
   const int n_cc = sr.n_cc;
-  const int cc = local % n_cc;
-  const int hl = local / n_cc;  // KV head within this launch's range
-  const int h = sr.h0 + hl;
+  const int cc = un.cc;
+  const int hl = un.hl;  // KV head within this launch's range
+  const int h = un.h;
   const size_t stride = size_t(CQ) * (D + 2);
   const float* const part_base = p.ws + (size_t(sr.part0) + size_t(hl * n_cc + cc) * sr.n_split) * stride;
   const int Wb = min(p.We, sr.T);
@@ -566,40 +570,68 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
     int row = 0, hh = 0;
     const int gi = column_group(p, sr, cc * CQ + col, row, hh);
     const int ns = sr.n_split;
-    constexpr int U = 4;  // splits whose loads are issued together
+    // Global maximum first, then the splits' weighted sums in split order.
+    // Up to kFast splits are loaded in one round and kept in registers.
+    constexpr int kFast = 8;
     float M = -INFINITY;
-    for (int sp = 0; sp < ns; sp += U) {
-      float mm[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        mm[u] = (sp + u < ns) ? part_base[size_t(sp + u) * stride + size_t(CQ) * D + col] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
-    }
     float L = 0.f;
     float o[DPT];
 #pragma unroll
     for (int d = 0; d < DPT; ++d) o[d] = 0.f;
-    for (int sp = 0; sp < ns; sp += U) {
-      float ms[U], ls[U];
-      floatx4 ov[U][DPT / 4];
+    if (ns <= kFast) {
+      float ms[kFast], ls[kFast];
+      floatx4 ov[kFast][DPT / 4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = sp + u < ns;
-        const float* part = part_base + size_t(ok ? sp + u : 0) * stride;
+      for (int u = 0; u < kFast; ++u) {
+        const bool ok = u < ns;
+        const float* part = part_base + size_t(ok ? u : 0) * stride;
         ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
         ls[u] = part[size_t(CQ) * D + CQ + col];
 #pragma unroll
         for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < kFast; ++u) M = fmaxf(M, ms[u]);
+#pragma unroll
+      for (int u = 0; u < kFast; ++u) {
         const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
         L += fs * ls[u];
 #pragma unroll
         for (int d = 0; d < DPT; d += 4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[d + e] += fs * ov[u][d / 4][e];
+      }
+    } else {
+      constexpr int U = 4;  // splits whose loads are issued together
+      for (int sp = 0; sp < ns; sp += U) {
+        float mm[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          mm[u] = (sp + u < ns) ? part_base[size_t(sp + u) * stride + size_t(CQ) * D + col] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
+      }
+      for (int sp = 0; sp < ns; sp += U) {
+        float ms[U], ls[U];
+        floatx4 ov[U][DPT / 4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = sp + u < ns;
+          const float* part = part_base + size_t(ok ? sp + u : 0) * stride;
+          ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
+          ls[u] = part[size_t(CQ) * D + CQ + col];
+#pragma unroll
+          for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
+          L += fs * ls[u];
+#pragma unroll
+          for (int d = 0; d < DPT; d += 4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[d + e] += fs * ov[u][d / 4][e];
+        }
       }
     }
     const GroupRec& g = p.grp[gi];
@@ -636,25 +668,53 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// Work-groups of verify_attn_kernel<T, D, NB> that fit on the current
+// device at once (queried once per device and instance).
 template <typename T, int D, int NB>
-static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, hipStream_t stream) {
+static int resident_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>),
+                                                  kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cached[dev] = per_cu * cus;
+  return cached[dev];
+}
+
+template <typename T, int D, int NB>
+static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid,
+                                  hipStream_t stream) {
   if (p.n_wg <= 0) return hipSuccess;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(p.n_wg),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(grid),
                                  dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
-  void* margs[] = {const_cast<VerifyParams*>(&p)};
+  void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB>), dim3(p.n_units),
                          dim3(kThreads), margs, 0, stream);
 }
 
-hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, int dtype, int D, int NB, hipStream_t stream) {
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid, int dtype, int D,
+                         int NB, hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, t, stream) : launch_verify_t<__bf16, 128, 2>(p, t, stream);
-    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, t, stream) : launch_verify_t<__bf16, 64, 2>(p, t, stream);
+    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, t, u, grid, stream) : launch_verify_t<__bf16, 128, 2>(p, t, u, grid, stream);
+    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, t, u, grid, stream) : launch_verify_t<__bf16, 64, 2>(p, t, u, grid, stream);
   }
-  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, stream) : launch_verify_t<float, 128, 2>(p, t, stream);
-  return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, stream) : launch_verify_t<float, 64, 2>(p, t, stream);
+  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, u, grid, stream) : launch_verify_t<float, 128, 2>(p, t, u, grid, stream);
+  return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, u, grid, stream) : launch_verify_t<float, 64, 2>(p, t, u, grid, stream);
+}
+
+int verify_slots(int dtype, int D, int NB) {
+  if (dtype == 1) {
+    if (D == 128) return NB == 1 ? resident_groups<__bf16, 128, 1>() : resident_groups<__bf16, 128, 2>();
+    return NB == 1 ? resident_groups<__bf16, 64, 1>() : resident_groups<__bf16, 64, 2>();
+  }
+  if (D == 128) return NB == 1 ? resident_groups<float, 128, 1>() : resident_groups<float, 128, 2>();
+  return NB == 1 ? resident_groups<float, 64, 1>() : resident_groups<float, 64, 2>();
 }
 
 }  // namespace ripe
