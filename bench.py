@@ -40,7 +40,12 @@ def parse():
     ap.add_argument("--layout", default=None, help="override the workload's layout")
     ap.add_argument("--split-len", type=int, default=0)
     ap.add_argument("--layers", type=int, default=None, help="recurrent layers (default: workload's)")
-    ap.add_argument("--depths", default="all", help="'all' or comma list of depths per step")
+    ap.add_argument("--depths", default="workload",
+                    help="'workload' (the workload's depths), 'all' or a comma list")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --workload (skip the other workloads' figures)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB before the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--json-out", default=None)
@@ -134,37 +139,66 @@ def cpu_baseline(case, layout, budget_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verify path shards by sequence or KV head with no exchange; see DESIGN.md)",
-              file=sys.stderr)
-        sys.exit(2)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_c3_ripe_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "self_speculative_verify_ripe_amd", "csrc", f)
+                  for f in ("verify.hip", "plan.h", "api.hip")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per verify call from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none for this workload or the kernel sources have
+    changed since it was taken."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line
+                  and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("workload") != workload or kv.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return int(float(kv["hbm_bytes_per_call"]))
+
+
+def run_workload(name, layout_override, steps, warmup, split_len, layers, depths_arg,
+                 copy_calibration_mib=0):
     import torch
     import self_speculative_verify_ripe_amd as rp
     from workloads import device_kv_rows
 
-    case, layout = geometry(args.workload, args.layout)
+    case, layout = geometry(name, layout_override)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
     elem = 2 if case.dtype == "bf16" else 4
-    L = args.layers or case.L_r
-    R, W, B, Hkv, Hq, D, k = case.R, case.W, case.B, case.Hkv, case.Hq, case.D, case.blocks[0][1]
-    growth = (args.steps + args.warmup) * k
-    t_max = int(-(-(int(case.seq_len.max()) + growth + k) // 32) * 32)
-    depths = list(range(1, R + 1)) if args.depths == "all" else [int(x) for x in args.depths.split(",")]
+    L = layers or case.L_r
+    R, W, B, Hkv, Hq, D = case.R, case.W, case.B, case.Hkv, case.Hq, case.D
+    k = case.blocks[0][1]
+    growth = (steps + warmup) * int(case.n_accept.max())
+    t_max = int(-(-(int(case.seq_len.max()) + growth + case.n_rows) // 32) * 32)
+    if depths_arg == "all":
+        depths = list(range(1, R + 1))
+    elif depths_arg in (None, "workload"):
+        depths = list(case.depths)
+    else:
+        depths = [int(x) for x in depths_arg.split(",")]
     if case.fixed_groups is not None:
-        base_groups = [(g.seq, g.depth, g.row_start, g.n_rows) for g in case.fixed_groups]
-        group_sets = [base_groups]
+        group_sets = [[(g.seq, g.depth, g.row_start, g.n_rows) for g in case.fixed_groups]]
     else:
         group_sets = [[(b, r, case.blocks[b][0], case.blocks[b][1]) for b in range(B)]
                       for r in depths]
     packed_sets = [rp.pack_groups(gs) for gs in group_sets]
     n_rows = case.n_rows
     desc = rp.make_desc(layout, case.dtype, R, W, B, t_max, Hkv, D, Hq, max_rows=n_rows,
-                        max_groups=2 * B, split_len=args.split_len)
+                        max_groups=2 * B, split_len=split_len)
     cache_bytes = rp.ripe_layout_bytes(desc)
     ws_bytes = rp.ripe_layout_bytes(desc, rp.RIPE_BYTES_WORKSPACE)
     stream = torch.cuda.current_stream()
@@ -179,12 +213,9 @@ def main():
             T = int(case.seq_len[b])
             if T == 0:
                 continue
-            need = None
-            if layout == "deepest":
-                need = [R]
-            elif layout == "ripe":
-                need = None  # plane R for all rows, planes < R for the last W rows
-            rows = device_kv_rows(1000003 * (layer + 1) + b, R, T, Hkv, D, 0.81, dev, dt, planes=need)
+            need = [R] if layout == "deepest" else None
+            rows = device_kv_rows(1000003 * (layer + 1) + b, R, T, Hkv, D, case.planes.decay, dev, dt,
+                                  planes=need)
             na = np.zeros(B, dtype=np.int32)
             na[b] = T
             rp.ripe_commit(desc, cache, sl, na, np.zeros(B, dtype=np.int32), rows, T)
@@ -193,7 +224,8 @@ def main():
     seq_len0 = case.seq_len.astype(np.int32).copy()
     torch.cuda.synchronize()
     t_fill = time.perf_counter() - t_fill
-    print(f"[bench] filled {L} x {cache_bytes/2**30:.2f} GiB caches in {t_fill:.1f}s", flush=True)
+    print(f"[bench] {name} {layout}: filled {L} x {cache_bytes/2**30:.2f} GiB caches in "
+          f"{t_fill:.1f}s", flush=True)
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261203)
@@ -209,8 +241,6 @@ def main():
     n_calls = len(group_sets) * L
 
     def step_bytes(sl):
-        """Per-call algorithmic bytes (KV read; all incl. q/out/lse) for the
-        current committed lengths."""
         kv = [kv_read_bytes(layout, R, W, sl, gs, Hkv, D, elem) for gs in group_sets]
         io = [io_bytes(gs, Hq, D, elem) for gs in group_sets]
         return kv, io
@@ -234,13 +264,21 @@ def main():
             rp.ripe_commit(desc, caches[layer], sl, n_accept, src_row, kv_new, n_rows, stream)
         seq_len = sl
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         one_step(None, 0)
+    if copy_calibration_mib:
+        # A plain device copy of known size, outside the timed region: the
+        # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
+        n = (copy_calibration_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # reads and writes exactly MIB MiB
+        del src, dst
     torch.cuda.synchronize()
-    # byte counts of every timed call, computed before timing starts
     per_step = []
     sl = seq_len.copy()
-    for _ in range(args.steps):
+    for _ in range(steps):
         kv, io = step_bytes(sl)
         per_step.append((kv, io))
         sl = sl + n_accept
@@ -248,55 +286,118 @@ def main():
     call_bytes = np.array([kv[gi] + io[gi] for kv, io in per_step for gi in range(len(group_sets))
                            for _ in range(L)], dtype=np.float64)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n_calls * args.steps)]
+              for _ in range(n_calls * steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record(stream)
     wall0 = time.perf_counter()
-    for k in range(args.steps):
-        one_step(events, k * n_calls)
+    for st in range(steps):
+        one_step(events, st * n_calls)
     host_s = time.perf_counter() - wall0
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed = t0.elapsed_time(t1) / 1e3
     call_s = np.array([a.elapsed_time(b) / 1e3 for a, b in events])
-    calls_per_step = len(group_sets) * L
     rows_per_step = sum(g[3] for g in group_sets[0])
-    verified_tok_s = rows_per_step * args.steps / elapsed if case.fixed_groups is None else \
-        rows_per_step * args.steps / (elapsed * R / len(depths))
     avg_call = float(call_s.mean())
+    # A draft block is verified once it has passed all R loops of every
+    # recurrent layer.  A step covering fewer depths (c2: r in {4, 32}; c4:
+    # one mixed-depth call per layer) is extrapolated to all R loops with its
+    # mean call time; the commit time is measured.
+    covers_all = case.fixed_groups is None and len(depths) == R
+    commit_s = max(0.0, elapsed / steps - float(call_s.sum()) / steps)
+    pass_s = elapsed / steps if covers_all else avg_call * L * R + commit_s
     achieved = float(call_bytes.mean()) / avg_call / 1e9
+    res = {
+        "value": total_kv / elapsed / 1e9,
+        "elapsed": elapsed,
+        "ms_per_step": elapsed / steps * 1e3,
+        "verified_tokens_per_s": rows_per_step / pass_s,
+        "tokens_extrapolated": not covers_all,
+        "achieved": achieved,
+        "avg_call_us": avg_call * 1e6,
+        "alg_bytes_per_call": int(call_bytes.mean()),
+        "calls_per_step": n_calls,
+        "wall": wall,
+        "host_us_per_call": host_s / (n_calls * steps) * 1e6,
+        "gpu_us_per_call": elapsed / (n_calls * steps) * 1e6,
+        "describe": f"{case.name} {layout}: B={B}, T~U[{int(case.seq_len.min())},"
+                    f"{int(case.seq_len.max())}], R={R}, layers={L}, Hq/Hkv={Hq}/{Hkv}, D={D}, "
+                    f"k={k}, W={W}, depths/step={len(depths) if case.fixed_groups is None else 'mixed'}",
+        "case": case,
+        "layout": layout,
+        "dtype": case.dtype,
+    }
+    del caches, q, kv_new, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+EXTRA_WORKLOADS = [("c2", "ripe"), ("c2", "full"), ("c2", "deepest"), ("c4", None),
+                   ("c5-ripe", None), ("c5-full", None), ("c5-deepest", None)]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify path shards by sequence or KV head with no exchange between GPUs)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    r = run_workload(args.workload, args.layout, args.steps, args.warmup, args.split_len,
+                     args.layers, args.depths, args.copy_calibration)
+    workload_key = f"{args.workload}-{r['layout']}" if not args.workload.startswith("c5") \
+        else args.workload
+    traffic = counted_traffic(workload_key) if args.split_len == 0 and args.layers is None \
+        and args.depths in (None, "workload") else None
     result = {
         "metric": "verify-attn KV read GB/s (% of HBM peak) and verified draft tokens/s, 1 GPU",
-        "value": round(total_kv / elapsed / 1e9, 2),
+        "value": round(r["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "ms_per_step": round(r["ms_per_step"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
+        "dtype": r["dtype"],
         "data": "synthetic (seeded; caches filled through ripe_commit)",
-        "config": {"workload": f"{case.name} {layout}: B={B}, T~U[{int(case.seq_len.min())},"
-                               f"{int(case.seq_len.max())}], R={R}, layers={L}, Hq/Hkv={Hq}/{Hkv}, "
-                               f"D={D}, k={k}, W={W}, depths/step={len(depths)}",
-                   "calls_per_step": calls_per_step, "split_len": args.split_len or "default"},
-        "hbm_frac": round(total_kv / elapsed / 1e9 / HBM_PEAK_GBS, 4),
-        "verified_tokens_per_s": round(verified_tok_s, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "ripe_verify_attn call (verify_partial + verify_merge)",
-                     "avg_call_us": round(avg_call * 1e6, 2),
-                     "alg_bytes_per_call": int(call_bytes.mean())},
-        "wall_s": round(wall, 3),
-        "host_enqueue_us_per_call": round(host_s / (n_calls * args.steps) * 1e6, 1),
-        "gpu_us_per_call": round(elapsed / (n_calls * args.steps) * 1e6, 2),
+        "config": {"workload": r["describe"], "calls_per_step": r["calls_per_step"],
+                   "split_len": args.split_len or "default"},
+        "hbm_frac": round(r["value"] / HBM_PEAK_GBS, 4),
+        "verified_tokens_per_s": round(r["verified_tokens_per_s"], 1),
+        "verified_tokens_extrapolated_to_R_loops": r["tokens_extrapolated"],
+        "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "ripe_verify_attn call = verify_attn_kernel + verify_merge_kernel",
+                     "avg_call_us": round(r["avg_call_us"], 2),
+                     "alg_bytes_per_call": r["alg_bytes_per_call"]},
+        "wall_s": round(r["wall"], 3),
+        "host_enqueue_us_per_call": round(r["host_us_per_call"], 1),
+        "gpu_us_per_call": round(r["gpu_us_per_call"], 2),
     }
+    if not args.no_extra:
+        extra = {}
+        for name, lay in EXTRA_WORKLOADS:
+            if name == args.workload and (lay is None or lay == r["layout"]):
+                continue
+            e = run_workload(name, lay, max(2, min(args.steps, 3)), 1, 0, None, None)
+            extra[f"{name}-{e['layout']}" if not name.startswith("c5") else name] = {
+                "GB/s": round(e["value"], 1), "hbm_frac": round(e["value"] / HBM_PEAK_GBS, 4),
+                "call_GB/s": round(e["achieved"], 1), "avg_call_us": round(e["avg_call_us"], 2),
+                "verified_tokens_per_s": round(e["verified_tokens_per_s"], 1),
+                "tokens_extrapolated": e["tokens_extrapolated"],
+                "ms_per_step": round(e["ms_per_step"], 3), "calls_per_step": e["calls_per_step"],
+                "workload": e["describe"]}
+        result["by_workload"] = extra
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, layout, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(r["case"], r["layout"], args.cpu_seconds)
     line = json.dumps(result)
     print(line, flush=True)
     if args.json_out:
