@@ -233,7 +233,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     kv_new = torch.randn((2, R, n_rows, Hkv, D), generator=gen, device=dev).to(dt)
     out = torch.empty((n_rows, Hq, D), dtype=dt, device=dev)
     lse = torch.empty((n_rows, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     n_accept = case.n_accept.astype(np.int32)
     src_row = case.src_row.astype(np.int32)
 

@@ -129,6 +129,14 @@ def ripe_layout_bytes(desc: ripe_desc_t, kind: int = RIPE_BYTES_CACHE) -> int:
     return n
 
 
+def new_workspace(desc: ripe_desc_t, device="cuda"):
+    """A workspace big enough for any verify call within the descriptor's
+    bounds (zero-filled; the kernels need no particular contents)."""
+    import torch
+    return torch.zeros(ripe_layout_bytes(desc, RIPE_BYTES_WORKSPACE), dtype=torch.uint8,
+                       device=device)
+
+
 def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
                      n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
                      workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:

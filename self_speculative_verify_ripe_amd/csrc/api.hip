@@ -9,7 +9,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <queue>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -21,9 +20,8 @@
 #include "ripe.h"
 
 namespace ripe {
-hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid, int dtype, int D,
-                         int NB, hipStream_t stream);
-int verify_slots(int dtype, int D, int NB);
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
+                         hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream);
 }  // namespace ripe
 
@@ -48,17 +46,30 @@ ripe_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Partials start 256 bytes into the workspace.
+constexpr int64_t kWsHeader = 256;
+
+
 int ring_width(const ripe_desc_t& d) {
   if (d.layout != RIPE_LAYOUT_RIPE) return 0;
   return d.W < d.t_max ? d.W : d.t_max;
 }
 
+// Longest piece.  Fixed by the descriptor alone, so that a sequence's plan
+// never depends on the rest of the batch: about two pieces per resident
+// work-group (512) when every sequence is full, and at least 1024 positions
+// (shorter pieces cost more in per-piece start-up than they gain in balance).
 int split_len(const ripe_desc_t& d) {
   if (d.split_len > 0) return d.split_len;
-  const int G = d.n_q_heads / d.n_kv_heads;
-  // Few query columns per KV head -> small partials -> shorter splits for
-  // more parallelism; many columns -> longer splits to amortise the partial.
-  return G >= 4 ? 1024 : (G >= 2 ? 512 : 256);
+  const int64_t work = int64_t(d.batch) * d.n_kv_heads * d.t_max;
+  const int64_t s = ((work + 1023) / 1024 + 31) / 32 * 32;
+  return int(std::min<int64_t>(std::max<int64_t>(s, 1024), 8192));
+}
+
+// Near-equal pieces of at most S positions (multiples of 32 but the last).
+inline int piece_len(int len, int S) {
+  const int n = (len + S - 1) / S;
+  return ((len + n - 1) / n + kStep - 1) / kStep * kStep;
 }
 
 // Elements of one region (K or V) of the cache, or -1 on overflow.
@@ -91,7 +102,8 @@ ripe_status_t check_desc(const ripe_desc_t* d) {
 }
 
 // Upper bound on split partial slots of any verify call within the
-// descriptor's max_rows / max_groups bounds.
+// descriptor's max_rows / max_groups bounds: one partial per piece per
+// (sequence, KV head, column chunk).
 int64_t workspace_bound(const ripe_desc_t& d) {
   const int64_t S = split_len(d);
   const int64_t G = d.n_q_heads / d.n_kv_heads;
@@ -99,10 +111,10 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   const int64_t groups = std::max<int64_t>(d.max_groups, 1);
   const int64_t rows = std::max<int64_t>(d.max_rows, groups);
   const int64_t nseq = std::min<int64_t>(d.batch, groups);
-  const int64_t tchunks = (int64_t(d.t_max) + S - 1) / S;
-  int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tchunks;
+  const int64_t tpieces = (int64_t(d.t_max) + S - 1) / S;
+  int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tpieces;
   if (d.layout == RIPE_LAYOUT_RIPE) per_seq += std::min<int64_t>(groups, d.R - 1) * ((We + S - 1) / S);
-  per_seq += groups + (rows + S - 1) / S;
+  per_seq += groups + (rows + S - 1) / S;  // draft rows
   const int64_t col_chunks = (rows * G + 15) / 16 + nseq;
   const long double slots = (long double)d.n_kv_heads * col_chunks * per_seq;
   const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4 + 256;
@@ -114,7 +126,6 @@ struct LaunchPlan {
   VerifyParams p;
   ItemTable t;
   UnitTable u;
-  int grid;            // persistent work-groups
   int64_t part_bytes;  // split partials
 };
 
@@ -124,10 +135,21 @@ struct VerifyScratch {
   std::vector<std::pair<int, int>> spans;
   std::vector<int> count, fill, order;
   std::vector<Seg> segs;
-  std::vector<Item> tail;
-  std::vector<int> by_size, bin_of, bin_cnt;
+  std::vector<Piece> pieces;
+  std::vector<Item> items;
+  std::vector<int> cost, by_size;
   std::vector<LaunchPlan> plans;
   int n_plans = 0;
+  // The inputs the plans above were built from (pointers aside).  A call
+  // with the same inputs, e.g. the same verify step on the next recurrent
+  // layer's cache, reuses them.
+  bool have_key = false;
+  ripe_desc_t key_desc;
+  int32_t key_rows = 0;
+  float key_scale = 0.f;
+  int key_NB = 1;
+  std::vector<int32_t> key_seq;
+  std::vector<ripe_group_t> key_groups;
 };
 
 VerifyScratch& verify_scratch() {
@@ -168,7 +190,38 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   for (int b = 0; b < d.batch; ++b)
     if (seq_len[b] < 0 || seq_len[b] > d.t_max) return RIPE_ERANGE;
   const int G = d.n_q_heads / d.n_kv_heads;
+  const int D = d.head_dim;
+  const size_t E = elem_bytes(d.dtype);
   VerifyScratch& sc = verify_scratch();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto set_pointers = [&](VerifyParams& p) {
+    p.cache_k = cache;
+    p.cache_v = static_cast<const char*>(cache) + size_t(region_elems(d)) * E;
+    p.q = q;
+    p.kv_new = kv_new;
+    p.out = out;
+    p.lse = lse;
+    p.plane_sel = plane_sel;
+    p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
+  };
+  auto launch_all = [&](int NB) -> ripe_status_t {
+    for (int pi = 0; pi < sc.n_plans; ++pi)
+      if (workspace == nullptr || size_t(sc.plans[pi].part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
+    for (int pi = 0; pi < sc.n_plans; ++pi) {
+      LaunchPlan& lp = sc.plans[pi];
+      set_pointers(lp.p);
+      const ripe_status_t st2 = hip_status(launch_verify(lp.p, lp.t, lp.u, d.dtype, D, NB, hs), "ripe_verify_attn");
+      if (st2 != RIPE_OK) return st2;
+    }
+    return RIPE_OK;
+  };
+  // same inputs as the plans in hand (already validated): launch them
+  if (sc.have_key && std::memcmp(&sc.key_desc, &d, sizeof(d)) == 0 && sc.key_rows == n_rows &&
+      std::memcmp(&sc.key_scale, &softmax_scale, sizeof(float)) == 0 && sc.key_groups.size() == size_t(n_groups) &&
+      std::memcmp(sc.key_seq.data(), seq_len, sizeof(int32_t) * size_t(d.batch)) == 0 &&
+      std::memcmp(sc.key_groups.data(), groups, sizeof(ripe_group_t) * size_t(n_groups)) == 0)
+    return launch_all(sc.key_NB);
+  sc.have_key = false;
   sc.spans.clear();
   for (int i = 0; i < n_groups; ++i) {
     const ripe_group_t& g = groups[i];
@@ -201,29 +254,17 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   }
   const int CQ = 16 * NB;
 
-  const int D = d.head_dim;
   const int We = ring_width(d);
   const int S = split_len(d);
-  const size_t E = elem_bytes(d.dtype);
-  const int64_t reg = region_elems(d);
-  const char* cache_k = static_cast<const char*>(cache);
-  const char* cache_v = cache_k + size_t(reg) * E;
 
   // Pack (sequence, KV-head range) pieces into launches of <= kMaxItems
-  // items, <= kMaxSeq sequence records and <= kMaxGroups group records.
+  // items, <= kMaxPieces pieces, <= kMaxSeq sequence records and
+  // <= kMaxGroups group records.
   sc.n_plans = 0;
   auto new_plan = [&]() -> LaunchPlan& {
     if (sc.plans.size() <= size_t(sc.n_plans)) sc.plans.emplace_back();
     LaunchPlan& lp = sc.plans[sc.n_plans++];
     VerifyParams& p = lp.p;
-    p.cache_k = cache_k;
-    p.cache_v = cache_v;
-    p.q = q;
-    p.kv_new = kv_new;
-    p.out = out;
-    p.lse = lse;
-    p.plane_sel = plane_sel;
-    p.ws = static_cast<float*>(workspace);
     p.ring_off = uint64_t(d.batch) * d.n_kv_heads * uint64_t(d.t_max) * D;
     p.layout = d.layout;
     p.R = d.R;
@@ -234,11 +275,11 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
     p.Hq = d.n_q_heads;
     p.G = G;
     p.n_rows = n_rows;
-    p.S = S;
     p.n_seq = 0;
     p.n_wg = 0;
     p.n_units = 0;
     p.n_grp = 0;
+    p.n_pieces = 0;
     p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
     return lp;
   };
@@ -257,20 +298,25 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
       nq += g.n_rows * G;
     }
     const int T = seq_len[b];
-    sc.segs.clear();
-    int64_t n_split = 0;
+    // pieces of this sequence: every segment cut into near-equal runs of at
+    // most S positions
+    sc.pieces.clear();
     enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, [&](const Seg& sg) {
-      sc.segs.push_back(sg);
-      n_split += (int64_t(sg.len) + S - 1) / S;
+      const int pl = piece_len(sg.len, S);
+      for (int c0 = 0; c0 < sg.len; c0 += pl)
+        sc.pieces.push_back(Piece{c0, std::min(pl, sg.len - c0), uint8_t(sg.kind), uint8_t(sg.depth),
+                                  uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
       return false;
     });
+    const int n_piece = int(sc.pieces.size());
+    const int n_split = n_piece;
     const int n_cc = (nq + CQ - 1) / CQ;
-    const int64_t per_head = n_split * n_cc;
-    if (per_head > kMaxItems) return RIPE_EUNSUPPORTED;  // one KV head must fit a launch
+    const int64_t per_head = int64_t(n_split) * n_cc;
+    if (per_head > kMaxItems || n_piece > kMaxPieces) return RIPE_EUNSUPPORTED;  // one KV head must fit a launch
     int h = 0;
     while (h < d.n_kv_heads) {
       if (cur == nullptr || cur->p.n_seq == kMaxSeq || cur->p.n_grp + gc > kMaxGroups ||
-          cur->p.n_wg + per_head > kMaxItems)
+          cur->p.n_wg + per_head > kMaxItems || cur->p.n_pieces + n_piece > kMaxPieces)
         cur = &new_plan();
       VerifyParams& p = cur->p;
       const int hc = int(std::min<int64_t>((kMaxItems - p.n_wg) / per_head, d.n_kv_heads - h));
@@ -292,29 +338,26 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
         p.gorig[p.n_grp] = uint16_t(sc.order[g0 + k]);
         ++p.n_grp;
       }
-      // items: unit (h, cc) and chunk `split` of the sequence's segment list;
-      // partial slot = part0 + ((h - h0) * n_cc + cc) * n_split + split
+      const int pbase = p.n_pieces;
+      for (int k = 0; k < n_piece; ++k) {
+        Piece pc = sc.pieces[k];
+        pc.s = uint8_t(p.n_seq);
+        if (pc.kind == kSegDraft) pc.gidx = uint8_t(sr.g_begin + pc.gidx);
+        cur->t.piece[p.n_pieces++] = pc;
+      }
+      // items of unit (h, cc): one per piece; partial slot = part0 + unit *
+      // n_split + piece
       for (int hh = 0; hh < hc; ++hh)
         for (int cc = 0; cc < n_cc; ++cc) {
-          int split = 0;
-          for (const Seg& sg : sc.segs) {
-            for (int c0 = 0; c0 < sg.len; c0 += S, ++split) {
-              Item& it = cur->t.item[p.n_wg++];
-              it.c0 = c0;
-              it.seg_len = sg.len;
-              it.part = sr.part0 + (hh * n_cc + cc) * int(n_split) + split;
-              it.h = uint16_t(h + hh);
-              it.cc = uint16_t(cc);
-              it.s = uint8_t(p.n_seq);
-              it.kind = uint8_t(sg.kind);
-              it.depth = uint8_t(sg.depth);
-              it.gidx = uint8_t(sg.kind == kSegDraft ? sr.g_begin + sg.gidx : 0);
-            }
+          const int unit = hh * n_cc + cc;
+          for (int k = 0; k < n_piece; ++k) {
+            Item& it = cur->t.item[p.n_wg++];
+            it.piece = uint16_t(pbase + k);
+            it.part = uint16_t(sr.part0 + unit * n_split + k);
+            it.h = uint16_t(h + hh);
+            it.cc = uint16_t(cc);
           }
-        }
-      for (int hh = 0; hh < hc; ++hh)
-        for (int cc = 0; cc < n_cc; ++cc) {
-          Unit& un = cur->u.unit[p.n_units + hh * n_cc + cc];
+          Unit& un = cur->u.unit[p.n_units + unit];
           un.s = uint16_t(p.n_seq);
           un.h = uint16_t(h + hh);
           un.cc = uint16_t(cc);
@@ -325,61 +368,35 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
       h += hc;
     }
   }
-  // Persistent work-groups: as many as fit on the device at once (at most
-  // kMaxSlots).  Items are assigned longest first to the least-loaded
-  // work-group (cost = 32-position steps + a fixed per-item latency).
+  // Items run longest first (by 32-position steps; a stable counting sort);
+  // work-group i runs item i and the hardware dispatches work-groups in
+  // order, so the shortest items fill in at the end.
   for (int pi = 0; pi < sc.n_plans; ++pi) {
     LaunchPlan& lp = sc.plans[pi];
-    lp.part_bytes = int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
-    if (workspace == nullptr || size_t(lp.part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
-  }
-  int slots = sc.n_plans > 0 ? verify_slots(d.dtype, D, NB) : 0;
-  if (slots <= 0) slots = 512;
-  slots = std::min(slots, kMaxSlots);
-  for (int pi = 0; pi < sc.n_plans; ++pi) {
-    LaunchPlan& lp = sc.plans[pi];
+    lp.part_bytes = kWsHeader + int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
     Item* items = lp.t.item;
     const int n = lp.p.n_wg;
-    auto cost = [&](const Item& it) { return (std::min(S, it.seg_len - it.c0) + kStep - 1) / kStep + 2; };
-    sc.by_size.resize(n);
-    for (int i = 0; i < n; ++i) sc.by_size[i] = i;
-    std::stable_sort(sc.by_size.begin(), sc.by_size.end(),
-                     [&](int x, int y) { return cost(items[x]) > cost(items[y]); });
-    const int W = std::min(n, slots);
-    using Load = std::pair<int64_t, int>;  // (accumulated cost, work-group)
-    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-    for (int w = 0; w < W; ++w) heap.push(Load(0, w));
-    sc.bin_of.resize(n);
-    sc.bin_cnt.assign(W + 1, 0);
-    for (int k = 0; k < n; ++k) {
-      Load top = heap.top();
-      heap.pop();
-      const int i = sc.by_size[k];
-      sc.bin_of[i] = top.second;
-      ++sc.bin_cnt[top.second + 1];
-      top.first += cost(items[i]);
-      heap.push(top);
+    int max_steps = 0;
+    sc.cost.resize(n);
+    for (int i = 0; i < n; ++i) {
+      sc.cost[i] = (lp.t.piece[items[i].piece].len + kStep - 1) / kStep;
+      max_steps = std::max(max_steps, sc.cost[i]);
     }
-    for (int w = 0; w < W; ++w) sc.bin_cnt[w + 1] += sc.bin_cnt[w];
-    for (int w = 0; w <= W; ++w) lp.t.first[w] = uint16_t(sc.bin_cnt[w]);
-    // place items by work-group, each work-group's items longest first
-    sc.tail.resize(n);
-    std::vector<int>& fill = sc.fill;
-    fill.assign(sc.bin_cnt.begin(), sc.bin_cnt.end() - 1);
-    for (int k = 0; k < n; ++k) {
-      const int i = sc.by_size[k];
-      sc.tail[fill[sc.bin_of[i]]++] = items[i];
-    }
-    std::copy(sc.tail.begin(), sc.tail.end(), items);
-    lp.grid = W;
+    sc.by_size.assign(max_steps + 2, 0);  // by_size[max_steps - c + 1]: items with more steps than c
+    for (int i = 0; i < n; ++i) ++sc.by_size[max_steps - sc.cost[i] + 1];
+    for (int c = 1; c <= max_steps + 1; ++c) sc.by_size[c] += sc.by_size[c - 1];
+    sc.items.resize(n);
+    for (int i = 0; i < n; ++i) sc.items[sc.by_size[max_steps - sc.cost[i]]++] = items[i];
+    std::copy(sc.items.begin(), sc.items.end(), items);
   }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  for (int pi = 0; pi < sc.n_plans; ++pi) {
-    const LaunchPlan& lp = sc.plans[pi];
-    const ripe_status_t st2 = hip_status(launch_verify(lp.p, lp.t, lp.u, lp.grid, d.dtype, D, NB, hs), "ripe_verify_attn");
-    if (st2 != RIPE_OK) return st2;
-  }
-  return RIPE_OK;
+  sc.key_desc = d;
+  sc.key_rows = n_rows;
+  sc.key_scale = softmax_scale;
+  sc.key_NB = NB;
+  sc.key_seq.assign(seq_len, seq_len + d.batch);
+  sc.key_groups.assign(groups, groups + n_groups);
+  sc.have_key = true;
+  return launch_all(NB);
 }
 
 extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,

@@ -8,13 +8,18 @@
 //   kind 1  a RIPE window ring for each distinct depth r < R, read in ring
 //           slot order (slot s holds the one window position j = s mod We);
 //   kind 2  one group's own draft rows at its depth (causal within the group).
-// Segments are cut into chunks of at most S positions; a chunk is one split-K
-// work item of one work-group.  The plan of a sequence depends only on the
-// descriptor, its committed length and its own groups, so a group's result is
-// bit-identical whether it is verified alone or batched with other sequences.
-// Groups of one sequence share its prefix chunks; a chunk that does not apply
-// to a group is masked for that group's query columns, which leaves its
-// running softmax state bit-identical (factor 1, zero added).
+// Every segment is cut into near-equal pieces of at most S positions (S a
+// multiple of 32, fixed by the descriptor; every piece but a segment's last
+// is a multiple of 32 long).  A work item is one piece for one KV head and one
+// query-column chunk: one work-group streams it and writes one split partial.
+// Partials start 256 bytes into the workspace.
+// The plan of a sequence depends only on the descriptor, its committed length
+// and its own groups, so a group's result is bit-identical whether it is
+// verified alone or batched with other sequences, and RIPE with W >= T (or
+// W = 0) runs exactly the pieces of FULL (of DEEPEST).  Groups of one
+// sequence share its pieces; a piece that does not apply to a group is masked
+// for that group's query columns, which leaves its running softmax state
+// bit-identical (factor 1, zero added).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -33,8 +38,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSeq = 64;      // sequences per launch
 constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
-constexpr int kMaxItems = 1024;  // verify work items per launch
-constexpr int kMaxSlots = 1024;  // persistent verify work-groups per launch
+constexpr int kMaxItems = 2048;  // verify work items (and merge units) per launch
+constexpr int kMaxPieces = 512;  // pieces per launch
 
 enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
 
@@ -42,7 +47,7 @@ struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   int32_t T;           // committed prefix length
   int32_t part0;       // first split partial slot of its units
   int32_t unit0;       // first (KV head, column chunk) unit
-  int32_t n_split;     // chunks of all segments
+  int32_t n_split;     // work items (= partials) per (KV head, column chunk)
   uint16_t b;          // sequence index within the cache
   uint16_t n_cc;       // query-column chunks
   uint16_t h0;         // first KV head of this launch's range
@@ -59,25 +64,31 @@ struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
   uint8_t seq;         // launch-local sequence index
 };
 
-// One verify work item: a chunk of <= S positions of one segment of one
-// sequence, for one KV head and one query-column chunk (20 bytes).
-struct Item {
-  int32_t c0;          // chunk start, segment-local
-  int32_t seg_len;     // segment length
-  int32_t part;        // split partial slot
-  uint16_t h;          // KV head
-  uint16_t cc;         // query-column chunk
-  uint8_t s;           // launch-local sequence
+// A run of positions of one segment of one sequence (12 bytes).
+struct Piece {
+  int32_t c0;          // first position, segment-local (a multiple of 32)
+  int32_t len;         // positions (kind 0), ring slots (kind 1) or rows (kind 2)
   uint8_t kind;        // SegKind
   uint8_t depth;       // plane read (kind 0) or depth r (kinds 1, 2)
   uint8_t gidx;        // group record (kind 2)
+  uint8_t s;           // launch-local sequence
 };
 
-// Work items of one launch, grouped by the work-group that runs them:
-// work-group w runs items first[w] .. first[w + 1] - 1 in order.
+// One verify work item (8 bytes): piece `piece` for KV head h and
+// query-column chunk cc, written to split partial slot `part`.
+struct Item {
+  uint16_t piece;
+  uint16_t part;
+  uint16_t h;
+  uint16_t cc;
+};
+
+// Pieces and work items of one launch; work-group i runs item i.  Items are
+// ordered longest first, so the hardware's in-order dispatch hands the
+// shortest ones to the work-groups that free up last.
 struct ItemTable {
+  Piece piece[kMaxPieces];
   Item item[kMaxItems];
-  uint16_t first[kMaxSlots + 1];
 };
 
 // (sequence, KV head, column chunk) of each merge work-group (8 bytes).
@@ -107,9 +118,9 @@ struct VerifyParams {
   void* out;
   float* lse;
   int8_t* plane_sel;
-  float* ws;             // split partials
+  float* ws;             // split partials, [item][16 NB columns][D + 2]
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
-  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, S, n_seq, n_wg, n_units, n_grp;
+  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];

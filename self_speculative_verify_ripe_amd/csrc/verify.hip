@@ -276,15 +276,11 @@ __device__ inline void qk(const u32x4 (&kf)[2][D / (4 * Op<T>::VEC)],
     }
 }
 
-#ifndef RIPE_FP32_WAVES
-#define RIPE_FP32_WAVES 2
-#endif
-// Wavefronts per SIMD the register allocation targets: two for bf16 (the
-// streaming configuration); fp32 with D = 128 and 32 columns needs more
-// registers than two wavefronts allow.
+// Wavefronts per SIMD the register allocation targets: two work-groups per
+// CU, each wavefront with one K/V step in flight ahead of the one it computes.
 template <typename T, int D, int NB>
 constexpr int waves_per_simd() {
-  return (sizeof(T) == 4 && D == 128 && NB == 2) ? RIPE_FP32_WAVES : 2;
+  return 2;
 }
 
 // LDS bytes of the verify kernel: the four wavefronts' (m, l, O) for the
@@ -297,8 +293,9 @@ constexpr int verify_lds_bytes() {
   return merge > draft ? merge : draft;
 }
 
-// One work-group per work item (sequence, KV head, query-column chunk, chunk
-// of <= S key positions of one segment); see the file comment.
+// One work-group per work item: one piece of one sequence for one KV head and
+// one query-column chunk (see plan.h).  Work-group i runs item i; items are
+// ordered longest first and the hardware dispatches work-groups in order.
 template <typename T, int D, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
@@ -313,37 +310,26 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   constexpr int TPC = kThreads / CQ;  // epilogue threads per column
   constexpr int DPT = D / TPC;        // head-dim values per epilogue thread
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15;
   const int lg = lane >> 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
-  // Persistent: as many work-groups as fit on the device at once, each
-  // running the items the host assigned to it (longest-processing-time
-  // first).  Results do not depend on which work-group runs an item.
-  const int item_end = tab.first[blockIdx.x + 1];
-  for (int item = tab.first[blockIdx.x]; item < item_end; ++item) {
-  __syncthreads();  // LDS of the previous item is free
+
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  const Item it = tab.item[item];
-  const int s = it.s;
-  const SeqRec sr = p.seq[s];
+  const Item it = tab.item[blockIdx.x];
+  const Piece pc = tab.piece[it.piece];
   const int h = it.h;
   const int cc = it.cc;
-  const int kind = it.kind;
-  const int sdepth = it.depth;
-  const int sgidx = it.gidx;
-  const int c0 = it.c0;
-  const int seg_len = it.seg_len;
-  const int clen = min(p.S, seg_len - c0);
-  const int nsteps = ceil_div(clen, kStep);
+  const SeqRec sr = p.seq[pc.s];
   const int Wb = min(p.We, sr.T);
+  const int nsteps = ceil_div(pc.len, kStep);
 
   // ---- query columns of this lane ---------------------------------------
   // Straight-line on purpose: every lane loads from a valid address and
   // padding columns are zeroed by selects, with no loads under divergent
-  // control flow.
-  int hi[NB];  // visible segment-local positions are < hi
+  // control flow.  hi[nb]: piece-local end of what the column sees.
+  int hi[NB];
   u32x4 qf[NB][KC];
   auto setup_columns = [&]() {
 #pragma unroll
@@ -360,64 +346,69 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
         qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
       }
       const int gd = g.depth;
-      const int h_plane = (p.layout == 0) ? (gd == sdepth ? sr.T : 0)
-                          : (p.layout == 1) ? sr.T
-                                            : (gd == p.R ? sr.T : sr.T - Wb);
-      const int h_ring = (gd == sdepth) ? Wb : 0;
-      const int h_draft = (gi == sgidx) ? row + 1 : 0;
-      const int hv = (kind == kSegPlane) ? h_plane : (kind == kSegRing) ? h_ring : h_draft;
-      hi[nb] = valid ? hv : 0;
+      int hv;
+      if (pc.kind == kSegPlane)
+        hv = (p.layout == 0) ? (gd == pc.depth ? sr.T : 0)
+             : (p.layout == 1) ? sr.T
+                               : (gd == p.R ? sr.T : sr.T - Wb);
+      else if (pc.kind == kSegRing)
+        hv = (gd == pc.depth) ? Wb : 0;
+      else
+        hv = (gi == pc.gidx) ? row + 1 : 0;
+      hi[nb] = valid ? hv - pc.c0 : 0;
     }
   };
 
   Softmax<T, D, NB> sm;
   sm.init();
   const float sl2 = p.scale_log2;
+  u32x4 kf[2][KC], vf[DB][VCH];
 
-  if (kind != kSegDraft) {
-    // ---- prefix plane or window ring: streamed with buffer loads ----------
+  // Wavefront w runs steps w, w + 4, ... of the piece.
+  if (pc.kind != kSegDraft) {
+    // ---- prefix plane or window ring: raw buffer loads ------------------
+    // The buffer resources span the piece only: loads past its end return
+    // zeros.
     size_t off;
     int bw = kStep;
-    if (kind == kSegPlane) {
+    if (pc.kind == kSegPlane) {
       if (p.layout == 0)
-        off = ((size_t(sr.b) * p.R + (sdepth - 1)) * p.H + h) * size_t(p.t_max) * D;
+        off = ((size_t(sr.b) * p.R + (pc.depth - 1)) * p.H + h) * size_t(p.t_max) * D;
       else
         off = (size_t(sr.b) * p.H + h) * size_t(p.t_max) * D;
     } else {
-      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (sdepth - 1)) * p.H + h) * size_t(p.We) * D;
+      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D;
       bw = p.BW;
     }
-    const T* kb = static_cast<const T*>(p.cache_k) + off;
-    const T* vb = static_cast<const T*>(p.cache_v) + off;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, uint32_t(seg_len) * D * E);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, uint32_t(ceil_div(seg_len, bw)) * bw * D * E);
+    off += size_t(pc.c0) * D;  // c0 is a multiple of 32, and of the ring's block width
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.cache_k) + off, uint32_t(pc.len) * D * E);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(static_cast<const T*>(p.cache_v) + off, uint32_t(ceil_div(pc.len, bw)) * bw * D * E);
     const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
     const uint32_t koff = (krow * D + lg * VEC) * E;
-    // A step index past the chunk maps to an offset beyond the buffer's
-    // range: those loads return zeros without touching memory, so the
-    // prefetch below is unconditional and the wait counts stay exact.
+    // A step past the piece maps to an offset beyond the resource's range:
+    // those loads return zeros without touching memory, so the prefetch
+    // below is unconditional and the wait counts stay exact.
     constexpr uint32_t kOutOfRange = 0x80000000u;
-    auto load_k = [&](int st, bool live, u32x4 (&kf)[2][KC]) {
-      const uint32_t base = live ? uint32_t(c0 + st * kStep) * D * E + koff : kOutOfRange;
+    auto load_k = [&](int st, bool live, u32x4 (&k)[2][KC]) {
+      const uint32_t base = live ? uint32_t(st * kStep) * D * E + koff : kOutOfRange;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int c = 0; c < KC; ++c) kf[mb][c] = bload16(krs, base + (4 * mb * D + c * 4 * VEC) * E);
+        for (int c = 0; c < KC; ++c) k[mb][c] = bload16(krs, base + (4 * mb * D + c * 4 * VEC) * E);
     };
-    auto load_v = [&](int st, bool live, u32x4 (&vf)[DB][VCH]) {
-      const int slot0 = c0 + st * kStep + 8 * lg;
+    auto load_v = [&](int st, bool live, u32x4 (&v)[DB][VCH]) {
+      const int slot0 = st * kStep + 8 * lg;
       const int blk = slot0 / bw;
       const uint32_t base = live ? uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E : kOutOfRange;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < VCH; ++v) vf[db][v] = bload16(vrs, base + (16 * db * bw + v * VEC) * E);
+        for (int c = 0; c < VCH; ++c) v[db][c] = bload16(vrs, base + (16 * db * bw + c * VEC) * E);
     };
     // first step's loads go out before the query setup
-    u32x4 kf[2][KC], vf[DB][VCH];
-    const bool any = wave < nsteps;
-    load_k(wave, any, kf);
-    load_v(wave, any, vf);
+    load_k(wave, wave < nsteps, kf);
+    load_v(wave, wave < nsteps, vf);
     setup_columns();
     for (int st = wave; st < nsteps; st += kWaves) {
       const bool more = st + kWaves < nsteps;
@@ -426,13 +417,13 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       load_k(st + kWaves, more, kf);
       int lim[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - (c0 + st * kStep);
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - st * kStep;
       typename O::P pf[NB];
       sm.update(sacc, lim, sl2, pf);
-      // a step reaching past the segment's end: zero the V values of the
+      // a step reaching past the piece's end: zero the V values of the
       // missing positions (they may hold anything, even NaN)
-      if (c0 + (st + 1) * kStep > seg_len) {
-        const int nval = seg_len - (c0 + st * kStep + 8 * lg);
+      if ((st + 1) * kStep > pc.len) {
+        const int nval = pc.len - (st * kStep + 8 * lg);
 #pragma unroll
         for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
       }
@@ -444,20 +435,20 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     // in MFMA order directly; V rows are staged in this wavefront's LDS slice
     // with 16-byte loads and read back transposed.
     setup_columns();
-    const GroupRec& g = p.grp[sgidx];
+    const GroupRec& g = p.grp[pc.gidx];
     const int Hd = p.H * D;
-    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(sdepth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
     const T* vb = static_cast<const T*>(p.kv_new) +
-                  (size_t(p.R + sdepth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+                  (size_t(p.R + pc.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
     T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
     constexpr int CPR = D / VEC;  // 16-byte pieces per row
+    const int len = pc.len;
     for (int st = wave; st < nsteps; st += kWaves) {
-      u32x4 kf[2][KC], vf[DB][VCH];
-      const int base = c0 + st * kStep;
+      const int base = st * kStep;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int pos = base + 8 * (ln >> 2) + 4 * mb + (ln & 3);
-        const bool ok = pos < seg_len;
+        const bool ok = pos < len;
         const T* rp = kb + size_t(ok ? pos : 0) * Hd + lg * VEC;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
@@ -470,7 +461,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       for (int i = lane; i < kStep * CPR; i += 64) {
         const int r = i / CPR;
         const int c = i - r * CPR;
-        const bool ok = base + r < seg_len;
+        const bool ok = base + r < len;
         const u32x4 v = ld16(vb + size_t(ok ? base + r : 0) * Hd + c * VEC);
         *reinterpret_cast<u32x4*>(stage + r * D + c * VEC) = ok ? v : u32x4{0u, 0u, 0u, 0u};
       }
@@ -542,7 +533,6 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       part[size_t(CQ) * D + CQ + col] = L;
     }
   }
-  }  // work items
 }
 
 // One work-group per (sequence, KV head, query-column chunk): merges the
@@ -668,29 +658,12 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-// Work-groups of verify_attn_kernel<T, D, NB> that fit on the current
-// device at once (queried once per device and instance).
 template <typename T, int D, int NB>
-static int resident_groups() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] > 0) return cached[dev];
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>),
-                                                  kThreads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  cached[dev] = per_cu * cus;
-  return cached[dev];
-}
-
-template <typename T, int D, int NB>
-static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid,
+static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u,
                                   hipStream_t stream) {
   if (p.n_wg <= 0) return hipSuccess;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(grid),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(p.n_wg),
                                  dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
@@ -698,23 +671,14 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
                          dim3(kThreads), margs, 0, stream);
 }
 
-hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int grid, int dtype, int D,
-                         int NB, hipStream_t stream) {
+hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
+                         hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, t, u, grid, stream) : launch_verify_t<__bf16, 128, 2>(p, t, u, grid, stream);
-    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, t, u, grid, stream) : launch_verify_t<__bf16, 64, 2>(p, t, u, grid, stream);
+    if (D == 128) return NB == 1 ? launch_verify_t<__bf16, 128, 1>(p, t, u, stream) : launch_verify_t<__bf16, 128, 2>(p, t, u, stream);
+    return NB == 1 ? launch_verify_t<__bf16, 64, 1>(p, t, u, stream) : launch_verify_t<__bf16, 64, 2>(p, t, u, stream);
   }
-  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, u, grid, stream) : launch_verify_t<float, 128, 2>(p, t, u, grid, stream);
-  return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, u, grid, stream) : launch_verify_t<float, 64, 2>(p, t, u, grid, stream);
-}
-
-int verify_slots(int dtype, int D, int NB) {
-  if (dtype == 1) {
-    if (D == 128) return NB == 1 ? resident_groups<__bf16, 128, 1>() : resident_groups<__bf16, 128, 2>();
-    return NB == 1 ? resident_groups<__bf16, 64, 1>() : resident_groups<__bf16, 64, 2>();
-  }
-  if (D == 128) return NB == 1 ? resident_groups<float, 128, 1>() : resident_groups<float, 128, 2>();
-  return NB == 1 ? resident_groups<float, 64, 1>() : resident_groups<float, 64, 2>();
+  if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, u, stream) : launch_verify_t<float, 128, 2>(p, t, u, stream);
+  return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, u, stream) : launch_verify_t<float, 64, 2>(p, t, u, stream);
 }
 
 }  // namespace ripe

@@ -64,7 +64,7 @@ class Device:
 
 
 def gpu_verify(desc, cache_dev, case, dev: Device, groups, seq_len=None, with_ps=True,
-               with_lse=True):
+               with_lse=True, ws=None):
     n_rows = case.n_rows
     out = torch.full((n_rows, case.Hq, case.D), float("nan"), dtype=TORCH_DT[case.dtype],
                      device=DEV)
@@ -72,8 +72,8 @@ def gpu_verify(desc, cache_dev, case, dev: Device, groups, seq_len=None, with_ps
         if with_lse else None
     ps = torch.full((max(len(groups), 1), case.t_max), -1, dtype=torch.int8, device=DEV) \
         if with_ps else None
-    wsb = rp.ripe_layout_bytes(desc, rp.RIPE_BYTES_WORKSPACE)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    if ws is None:
+        ws = rp.new_workspace(desc, DEV)
     sl = case.seq_len if seq_len is None else seq_len
     rp.ripe_verify_attn(desc, cache_dev, sl, groups, n_rows, case.scale, dev.q, dev.kv_new, out,
                         lse, ps, ws)

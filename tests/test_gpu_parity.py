@@ -14,7 +14,7 @@ from oracle import layout as olay
 from oracle import ripe_oracle as ro
 from workloads import Group, make_case
 
-from gpu_util import (DEV, Device, check, gpu_verify, make_desc, oracle_cache, to_dev,
+from gpu_util import (DEV, Device, check, gpu_verify, make_desc, oracle_cache, rows_of, to_dev,
                       upload)
 
 pytestmark = pytest.mark.gpu
@@ -213,3 +213,23 @@ def test_optional_outputs_and_determinism():
     b = gpu_verify(desc, cache, case, dev, groups, with_ps=False, with_lse=False)
     c = gpu_verify(desc, cache, case, dev, groups)
     assert torch.equal(a[0], b[0]) and torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_shared_workspace_across_calls():
+    """One workspace reused by calls of different shapes and launch counts
+    gives the results of fresh workspaces (bit-exact)."""
+    case = make_case("c3", B=70, T_range=(40, 200), R=4, Hkv=2, Hq=8, D=64, seed_offset=3)
+    oc = oracle_cache(case, "ripe")
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, "ripe", split_len=32)
+    ws = rp.new_workspace(desc, DEV)
+    for r in (3, 4, 1, 2):
+        for seqs in (None, [0, 5, 69]):
+            groups = case.groups_at(r, seqs)
+            print(f"[case] shared workspace r={r} groups={len(groups)}", flush=True)
+            a = gpu_verify(desc, cache, case, dev, groups, ws=ws)
+            b = gpu_verify(desc, cache, case, dev, groups)
+            rows = torch.from_numpy(rows_of(groups)).to(DEV)
+            assert torch.equal(a[0][rows], b[0][rows]) and torch.equal(a[1][rows], b[1][rows])
+            assert torch.equal(a[2], b[2])
