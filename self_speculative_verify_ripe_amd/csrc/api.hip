@@ -388,6 +388,9 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
     sc.items.resize(n);
     for (int i = 0; i < n; ++i) sc.items[sc.by_size[max_steps - sc.cost[i]]++] = items[i];
     std::copy(sc.items.begin(), sc.items.end(), items);
+    int n_big = 0;
+    while (n_big < n && (lp.t.piece[items[n_big].piece].len + kStep - 1) / kStep > kSoloSteps) ++n_big;
+    lp.p.n_big = n_big;
   }
   sc.key_desc = d;
   sc.key_rows = n_rows;

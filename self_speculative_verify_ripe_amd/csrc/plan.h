@@ -40,6 +40,7 @@ constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
 constexpr int kMaxItems = 2048;  // verify work items (and merge units) per launch
 constexpr int kMaxPieces = 512;  // pieces per launch
+constexpr int kSoloSteps = 4;    // a piece of at most this many steps runs on one wavefront
 
 enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
 
@@ -83,9 +84,10 @@ struct Item {
   uint16_t cc;
 };
 
-// Pieces and work items of one launch; work-group i runs item i.  Items are
-// ordered longest first, so the hardware's in-order dispatch hands the
-// shortest ones to the work-groups that free up last.
+// Pieces and work items of one launch, ordered longest first so that the
+// hardware's in-order dispatch hands the shortest ones to the work-groups
+// that free up last.  Items of at most kSoloSteps steps are short: four of
+// them share a work-group, one per wavefront.
 struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];
@@ -121,6 +123,7 @@ struct VerifyParams {
   float* ws;             // split partials, [item][16 NB columns][D + 2]
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
+  int32_t n_big;         // items 0 .. n_big - 1 are long (one work-group each)
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];

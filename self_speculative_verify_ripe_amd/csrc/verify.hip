@@ -293,9 +293,12 @@ constexpr int verify_lds_bytes() {
   return merge > draft ? merge : draft;
 }
 
-// One work-group per work item: one piece of one sequence for one KV head and
-// one query-column chunk (see plan.h).  Work-group i runs item i; items are
-// ordered longest first and the hardware dispatches work-groups in order.
+// Work items: one piece of one sequence for one KV head and one query-column
+// chunk (see plan.h).  The first n_big work-groups run one long item each,
+// its steps spread over the four wavefronts and merged through LDS; every
+// later work-group runs four short items, one per wavefront, each wavefront
+// writing its own partial.  Items are ordered longest first and the hardware
+// dispatches work-groups in order.
 template <typename T, int D, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
@@ -317,7 +320,14 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
 
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  const Item it = tab.item[blockIdx.x];
+  // A long item: wavefront w runs steps w, w + 4, ...  A short one: the
+  // wavefront runs every step of its own item.
+  const bool solo = int(blockIdx.x) >= p.n_big;
+  const int idx = solo ? p.n_big + (int(blockIdx.x) - p.n_big) * kWaves + wave : int(blockIdx.x);
+  if (idx >= p.n_wg) return;  // (short items only: no barrier follows)
+  const int st0 = solo ? 0 : wave;
+  const int sstride = solo ? 1 : kWaves;
+  const Item it = tab.item[idx];
   const Piece pc = tab.piece[it.piece];
   const int h = it.h;
   const int cc = it.cc;
@@ -407,14 +417,14 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
         for (int c = 0; c < VCH; ++c) v[db][c] = bload16(vrs, base + (16 * db * bw + c * VEC) * E);
     };
     // first step's loads go out before the query setup
-    load_k(wave, wave < nsteps, kf);
-    load_v(wave, wave < nsteps, vf);
+    load_k(st0, st0 < nsteps, kf);
+    load_v(st0, st0 < nsteps, vf);
     setup_columns();
-    for (int st = wave; st < nsteps; st += kWaves) {
-      const bool more = st + kWaves < nsteps;
+    for (int st = st0; st < nsteps; st += sstride) {
+      const bool more = st + sstride < nsteps;
       floatx4 sacc[2][NB];
       qk<T, D, NB>(kf, qf, sacc);
-      load_k(st + kWaves, more, kf);
+      load_k(st + sstride, more, kf);
       int lim[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - st * kStep;
@@ -428,7 +438,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
         for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
       }
       sm.pv(vf, pf);
-      load_v(st + kWaves, more, vf);
+      load_v(st + sstride, more, vf);
     }
   } else {
     // ---- a group's own draft rows (kv_new, row-major): K rows are loaded
@@ -443,7 +453,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
     constexpr int CPR = D / VEC;  // 16-byte pieces per row
     const int len = pc.len;
-    for (int st = wave; st < nsteps; st += kWaves) {
+    for (int st = st0; st < nsteps; st += sstride) {
       const int base = st * kStep;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -486,6 +496,27 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     }
   }
 
+  const size_t stride = size_t(CQ) * (D + 2);
+  float* const part = p.ws + size_t(it.part) * stride;
+  if (solo) {
+    // ---- a short item's partial, straight from this wavefront's registers
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float lt = wave_sum_lanegroups(sm.l[nb]);
+      const int col = ln + 16 * nb;
+      if (cc * CQ + col < sr.nq) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<floatx4*>(part + size_t(col) * D + 16 * db + 4 * lg) = sm.acc[db][nb];
+        if (lg == 0) {
+          part[size_t(CQ) * D + col] = sm.m[nb];
+          part[size_t(CQ) * D + CQ + col] = lt;
+        }
+      }
+    }
+    return;
+  }
+
   // ---- merge the four wavefronts through LDS, write one partial ----------
   __syncthreads();  // the draft path's staging slices are reused below
   typedef float OSlice[CQ][D + 4];
@@ -519,8 +550,6 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L += f[w] * lds_l[w][col];
     }
-    const size_t stride = size_t(CQ) * (D + 2);
-    float* part = p.ws + size_t(it.part) * stride;
 #pragma unroll
     for (int d = 0; d < DPT; d += 4) {
       floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -662,8 +691,9 @@ template <typename T, int D, int NB>
 static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u,
                                   hipStream_t stream) {
   if (p.n_wg <= 0) return hipSuccess;
+  const int grid = p.n_big + (p.n_wg - p.n_big + kWaves - 1) / kWaves;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(p.n_wg),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(grid),
                                  dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
