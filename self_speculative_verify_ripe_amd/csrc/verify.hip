@@ -564,16 +564,29 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   }
 }
 
-// One work-group per (sequence, KV head, query-column chunk): merges the
-// unit's split partials in split order, normalises and writes out, lse and
-// (unit h 0, chunk 0) the sequence's plane_sel rows.
-template <typename T, int D, int NB>
-__global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyParams p, const UnitTable ut) {
+// Merge: one work-group per (sequence, KV head, query-column chunk) and
+// head-dim slice of SLICE values.  It combines the unit's split partials in
+// split order, normalises and writes its slice of out; slice 0 also writes
+// lse, and (KV head 0, chunk 0, slice 0) the sequence's plane_sel rows.
+// Narrow slices give small batches more work-groups (and room to load up to
+// 16 splits in one round); large batches use whole rows.
+constexpr int kMergeThreads = 256;  // threads per merge work-group
+
+template <int N>
+struct FloatN {
+  typedef float type __attribute__((ext_vector_type(N)));
+};
+
+template <typename T, int D, int NB, int SLICE>
+__global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const VerifyParams p, const UnitTable ut) {
   using O = Op<T>;
   constexpr int CQ = 16 * NB;
-  constexpr int TPC = kThreads / CQ;
-  constexpr int DPT = D / TPC;
-  const Unit un = ut.unit[blockIdx.x];
+  constexpr int TPC = kMergeThreads / CQ;  // threads per column
+  constexpr int DPT = SLICE / TPC;         // head-dim values per thread
+  constexpr int NS = D / SLICE;            // slices per unit
+  typedef typename FloatN<DPT>::type VecT;
+  const int slice = blockIdx.x % NS;
+  const Unit un = ut.unit[blockIdx.x / NS];
   const SeqRec sr = p.seq[un.s];
   const int n_cc = sr.n_cc;
   const int cc = un.cc;
@@ -583,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
   const float* const part_base = p.ws + (size_t(sr.part0) + size_t(hl * n_cc + cc) * sr.n_split) * stride;
   const int Wb = min(p.We, sr.T);
   const int col = threadIdx.x / TPC;
-  const int d0 = (threadIdx.x % TPC) * DPT;
+  const int d0 = slice * SLICE + (threadIdx.x % TPC) * DPT;
   const bool col_valid = cc * CQ + col < sr.nq;
   if (col_valid) {
     int row = 0, hh = 0;
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
     const int ns = sr.n_split;
     // Global maximum first, then the splits' weighted sums in split order.
     // Up to kFast splits are loaded in one round and kept in registers.
-    constexpr int kFast = 8;
+    constexpr int kFast = DPT <= 4 ? 16 : 8;
     float M = -INFINITY;
     float L = 0.f;
     float o[DPT];
@@ -599,15 +612,14 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
     for (int d = 0; d < DPT; ++d) o[d] = 0.f;
     if (ns <= kFast) {
       float ms[kFast], ls[kFast];
-      floatx4 ov[kFast][DPT / 4];
+      VecT ov[kFast];
 #pragma unroll
       for (int u = 0; u < kFast; ++u) {
         const bool ok = u < ns;
         const float* part = part_base + size_t(ok ? u : 0) * stride;
         ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
         ls[u] = part[size_t(CQ) * D + CQ + col];
-#pragma unroll
-        for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+        ov[u] = *reinterpret_cast<const VecT*>(part + size_t(col) * D + d0);
       }
 #pragma unroll
       for (int u = 0; u < kFast; ++u) M = fmaxf(M, ms[u]);
@@ -616,12 +628,10 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
         const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
         L += fs * ls[u];
 #pragma unroll
-        for (int d = 0; d < DPT; d += 4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[d + e] += fs * ov[u][d / 4][e];
+        for (int e = 0; e < DPT; ++e) o[e] += fs * ov[u][e];
       }
     } else {
-      constexpr int U = 4;  // splits whose loads are issued together
+      constexpr int U = DPT <= 4 ? 8 : 4;  // splits whose loads are issued together
       for (int sp = 0; sp < ns; sp += U) {
         float mm[U];
 #pragma unroll
@@ -632,24 +642,21 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
       }
       for (int sp = 0; sp < ns; sp += U) {
         float ms[U], ls[U];
-        floatx4 ov[U][DPT / 4];
+        VecT ov[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const bool ok = sp + u < ns;
           const float* part = part_base + size_t(ok ? sp + u : 0) * stride;
           ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
           ls[u] = part[size_t(CQ) * D + CQ + col];
-#pragma unroll
-          for (int d = 0; d < DPT; d += 4) ov[u][d / 4] = *reinterpret_cast<const floatx4*>(part + size_t(col) * D + d0 + d);
+          ov[u] = *reinterpret_cast<const VecT*>(part + size_t(col) * D + d0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - M);
           L += fs * ls[u];
 #pragma unroll
-          for (int d = 0; d < DPT; d += 4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[d + e] += fs * ov[u][d / 4][e];
+          for (int e = 0; e < DPT; ++e) o[e] += fs * ov[u][e];
         }
       }
     }
@@ -661,12 +668,12 @@ __global__ __launch_bounds__(kThreads) void verify_merge_kernel(const VerifyPara
     O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
     if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
   }
-  // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0)
-  if (p.plane_sel != nullptr && h == 0 && cc == 0) {
+  // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0), slice 0
+  if (p.plane_sel != nullptr && h == 0 && cc == 0 && slice == 0) {
     for (int gi = sr.g_begin; gi < sr.g_begin + sr.g_count; ++gi) {
       const int r = p.grp[gi].depth;
       int8_t* rowp = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
-      for (int j0 = threadIdx.x * 16; j0 < sr.T; j0 += kThreads * 16) {
+      for (int j0 = threadIdx.x * 16; j0 < sr.T; j0 += kMergeThreads * 16) {
         int8_t v[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -697,8 +704,11 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
                                  dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB>), dim3(p.n_units),
-                         dim3(kThreads), margs, 0, stream);
+  if (p.n_units * (D / 32) <= 1024)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, 32>),
+                           dim3(p.n_units * (D / 32)), dim3(kMergeThreads), margs, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, D>), dim3(p.n_units),
+                         dim3(kMergeThreads), margs, 0, stream);
 }
 
 hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
