@@ -11,9 +11,10 @@ timed region starts.
 
 Printed: one JSON line with the whole-step KV-read bandwidth (value), the
 verified draft tokens per second, the roofline of the verify kernel
-(algorithmic bytes per call / average call duration measured with HIP
-events on the launch stream), and the float64 oracle timed on host cores on
-a bounded sample.
+(algorithmic bytes per call / average call duration: the time between HIP
+events on the launch stream that bracket each step's verify calls, divided by
+the number of calls), and the float64 oracle timed on host cores on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -245,19 +246,19 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
         io = [io_bytes(gs, Hq, D, elem) for gs in group_sets]
         return kv, io
 
-    def one_step(events, ev0):
+    def one_step(events):
+        # One event pair brackets the step's verify calls: an event around
+        # every call would add its own few microseconds to each call.
         nonlocal seq_len
-        i = ev0
+        if events is not None:
+            events[0].record(stream)
         for gi in range(len(group_sets)):
             gs = packed_sets[gi]
             for layer in range(L):
-                if events is not None:
-                    events[i][0].record(stream)
                 rp.ripe_verify_attn(desc, caches[layer], seq_len, gs, n_rows, 1.0, q, kv_new, out,
                                     lse, None, ws, ws_bytes, stream)
-                if events is not None:
-                    events[i][1].record(stream)
-                i += 1
+        if events is not None:
+            events[1].record(stream)
         sl = seq_len
         for layer in range(L):
             sl = seq_len.copy()
@@ -265,7 +266,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
         seq_len = sl
 
     for _ in range(warmup):
-        one_step(None, 0)
+        one_step(None)
     if copy_calibration_mib:
         # A plain device copy of known size, outside the timed region: the
         # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
@@ -286,28 +287,28 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     call_bytes = np.array([kv[gi] + io[gi] for kv, io in per_step for gi in range(len(group_sets))
                            for _ in range(L)], dtype=np.float64)
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n_calls * steps)]
+              for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     wall0 = time.perf_counter()
     for st in range(steps):
-        one_step(events, st * n_calls)
+        one_step(events[st])
     host_s = time.perf_counter() - wall0
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed = t0.elapsed_time(t1) / 1e3
-    call_s = np.array([a.elapsed_time(b) / 1e3 for a, b in events])
+    verify_s = np.array([a.elapsed_time(b) / 1e3 for a, b in events])
     rows_per_step = sum(g[3] for g in group_sets[0])
-    avg_call = float(call_s.mean())
+    avg_call = float(verify_s.sum()) / (n_calls * steps)
     # A draft block is verified once it has passed all R loops of every
     # recurrent layer.  A step covering fewer depths (c2: r in {4, 32}; c4:
     # one mixed-depth call per layer) is extrapolated to all R loops with its
     # mean call time; the commit time is measured.
     covers_all = case.fixed_groups is None and len(depths) == R
-    commit_s = max(0.0, elapsed / steps - float(call_s.sum()) / steps)
+    commit_s = max(0.0, elapsed / steps - float(verify_s.sum()) / steps)
     pass_s = elapsed / steps if covers_all else avg_call * L * R + commit_s
     achieved = float(call_bytes.mean()) / avg_call / 1e9
     res = {
