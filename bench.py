@@ -19,6 +19,7 @@ sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -265,6 +266,11 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
             rp.ripe_commit(desc, caches[layer], sl, n_accept, src_row, kv_new, n_rows, stream)
         seq_len = sl
 
+    # Python's cyclic garbage collector can pause the host for tens of
+    # milliseconds at an arbitrary call, leaving the GPU idle: collect once
+    # here and keep it off while the steps run.
+    gc.collect()
+    gc.disable()
     for _ in range(warmup):
         one_step(None)
     if copy_calibration_mib:
@@ -299,6 +305,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     elapsed = t0.elapsed_time(t1) / 1e3
     verify_s = np.array([a.elapsed_time(b) / 1e3 for a, b in events])
     rows_per_step = sum(g[3] for g in group_sets[0])

@@ -23,6 +23,7 @@ namespace ripe {
 hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
                          hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, int dtype, int D, hipStream_t stream);
+int verify_blocks_per_cu(int dtype, int D, int NB);
 }  // namespace ripe
 
 namespace {
@@ -135,6 +136,20 @@ struct LaunchPlan {
 
 // Per-thread planning buffers, reused across calls (no per-call allocation
 // once they have grown to the call sizes in use).
+struct WgCost {
+  int work;        // 32-position steps streamed by the work-group
+  uint16_t entry;  // its ItemTable::wg entry
+};
+
+// Compute units of the current device (0 if the runtime cannot say).
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
 struct VerifyScratch {
   std::vector<std::pair<int, int>> spans;
   std::vector<int> count, fill, order;
@@ -142,6 +157,7 @@ struct VerifyScratch {
   std::vector<Piece> pieces;
   std::vector<Item> items;
   std::vector<int> cost, by_size;
+  std::vector<WgCost> long_wg, solo_wg, wgs;
   std::vector<LaunchPlan> plans;
   int n_plans = 0;
   // The inputs the plans above were built from (pointers aside).  A call
@@ -372,9 +388,19 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
       h += hc;
     }
   }
-  // Items run longest first (by 32-position steps; a stable counting sort);
-  // work-group i runs item i and the hardware dispatches work-groups in
-  // order, so the shortest items fill in at the end.
+  // Items run longest first (by 32-position steps; a stable counting sort).
+  // Work-groups: one per long item, one per four consecutive short items.
+  // The hardware dispatches work-groups in grid order: the first round puts
+  // work-group j on compute unit j mod n_cu, and with two resident per unit,
+  // j and j + n_cu share one.  A unit's finishing time follows the total
+  // work of its pair, so when every work-group fits in that first round the
+  // grid pairs the largest with the smallest (the largest ones alone when
+  // fewer than 2 n_cu); beyond that, longest-first order lets the
+  // work-groups that free up last take the shortest items.  Placement only
+  // moves work-groups between compute units: every item writes its own
+  // partial and the merge order is fixed, so results do not depend on it.
+  const int n_cu = compute_units();
+  const int per_cu = verify_blocks_per_cu(d.dtype, D, NB);
   for (int pi = 0; pi < sc.n_plans; ++pi) {
     LaunchPlan& lp = sc.plans[pi];
     lp.part_bytes = kWsHeader + int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
@@ -392,9 +418,37 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
     sc.items.resize(n);
     for (int i = 0; i < n; ++i) sc.items[sc.by_size[max_steps - sc.cost[i]]++] = items[i];
     std::copy(sc.items.begin(), sc.items.end(), items);
+    for (int i = 0; i < n; ++i) sc.cost[i] = (lp.t.piece[items[i].piece].len + kStep - 1) / kStep;
     int n_big = 0;
-    while (n_big < n && (lp.t.piece[items[n_big].piece].len + kStep - 1) / kStep > kSoloSteps) ++n_big;
-    lp.p.n_big = n_big;
+    while (n_big < n && sc.cost[n_big] > kSoloSteps) ++n_big;
+    // work-groups by decreasing work (steps): both runs below are already
+    // decreasing, so one merge orders them
+    sc.long_wg.clear();
+    sc.solo_wg.clear();
+    for (int i = 0; i < n_big; ++i) sc.long_wg.push_back({sc.cost[i], uint16_t(i)});
+    for (int i = n_big; i < n; i += kWaves) {
+      const int cnt = std::min(kWaves, n - i);
+      int w = 0;
+      for (int k = 0; k < cnt; ++k) w += sc.cost[i + k];
+      sc.solo_wg.push_back({w, uint16_t(i | ((cnt - 1) << 11) | kWgSolo)});
+    }
+    sc.wgs.resize(sc.long_wg.size() + sc.solo_wg.size());
+    std::merge(sc.long_wg.begin(), sc.long_wg.end(), sc.solo_wg.begin(), sc.solo_wg.end(), sc.wgs.begin(),
+               [](const WgCost& x, const WgCost& y) { return x.work > y.work; });
+    const int N = int(sc.wgs.size());
+    uint16_t* wg = lp.t.wg;
+    if (per_cu == 2 && n_cu > 0 && N > n_cu && N <= 2 * n_cu) {
+      const int P = N - n_cu;  // compute units running two work-groups
+      const int S = n_cu - P;  // ... and one
+      for (int j = 0; j < P; ++j) {
+        wg[j] = sc.wgs[S + j].entry;
+        wg[n_cu + j] = sc.wgs[N - 1 - j].entry;
+      }
+      for (int j = 0; j < S; ++j) wg[P + j] = sc.wgs[j].entry;
+    } else {
+      for (int j = 0; j < N; ++j) wg[j] = sc.wgs[j].entry;
+    }
+    lp.p.n_blocks = N;
   }
   sc.key_desc = d;
   sc.key_rows = n_rows;

@@ -84,13 +84,20 @@ struct Item {
   uint16_t cc;
 };
 
-// Pieces and work items of one launch, ordered longest first so that the
-// hardware's in-order dispatch hands the shortest ones to the work-groups
-// that free up last.  Items of at most kSoloSteps steps are short: four of
-// them share a work-group, one per wavefront.
+// Work-group entries (16 bits): bits 0-10 the first item, bits 11-12 the
+// number of items less one, bit 15 set for a work-group of short items.
+constexpr uint16_t kWgSolo = 0x8000;
+static_assert(kMaxItems <= 2048, "work-group entries hold an 11-bit item index");
+
+// Pieces, work items and work-groups of one launch.  Items are ordered
+// longest first.  Items of at most kSoloSteps steps are short: up to four of
+// them share a work-group, one per wavefront; every other item has a
+// work-group of its own.  wg[] maps each work-group of the grid to its items
+// (see the planner for the placement order).
 struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];
+  uint16_t wg[kMaxItems];
 };
 
 // (sequence, KV head, column chunk) of each merge work-group (8 bytes).
@@ -123,7 +130,7 @@ struct VerifyParams {
   float* ws;             // split partials, [item][16 NB columns][D + 2]
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
-  int32_t n_big;         // items 0 .. n_big - 1 are long (one work-group each)
+  int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];

@@ -294,11 +294,11 @@ constexpr int verify_lds_bytes() {
 }
 
 // Work items: one piece of one sequence for one KV head and one query-column
-// chunk (see plan.h).  The first n_big work-groups run one long item each,
-// its steps spread over the four wavefronts and merged through LDS; every
-// later work-group runs four short items, one per wavefront, each wavefront
-// writing its own partial.  Items are ordered longest first and the hardware
-// dispatches work-groups in order.
+// chunk (see plan.h).  A work-group runs either one long item, its steps
+// spread over the four wavefronts and merged through LDS, or up to four short
+// items, one per wavefront, each wavefront writing its own partial.  The
+// host's work-group table says which; the hardware dispatches work-groups in
+// grid order.
 template <typename T, int D, int NB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
@@ -322,9 +322,10 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   // ---- this work item (host-planned; wave-uniform) ----------------------
   // A long item: wavefront w runs steps w, w + 4, ...  A short one: the
   // wavefront runs every step of its own item.
-  const bool solo = int(blockIdx.x) >= p.n_big;
-  const int idx = solo ? p.n_big + (int(blockIdx.x) - p.n_big) * kWaves + wave : int(blockIdx.x);
-  if (idx >= p.n_wg) return;  // (short items only: no barrier follows)
+  const uint32_t wge = tab.wg[blockIdx.x];
+  const bool solo = (wge & kWgSolo) != 0;
+  if (solo && wave > int((wge >> 11) & 3)) return;  // (short items only: no barrier follows)
+  const int idx = int(wge & 0x7ffu) + (solo ? wave : 0);
   const int st0 = solo ? 0 : wave;
   const int sstride = solo ? 1 : kWaves;
   const Item it = tab.item[idx];
@@ -698,7 +699,7 @@ template <typename T, int D, int NB>
 static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u,
                                   hipStream_t stream) {
   if (p.n_wg <= 0) return hipSuccess;
-  const int grid = p.n_big + (p.n_wg - p.n_big + kWaves - 1) / kWaves;
+  const int grid = p.n_blocks;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(grid),
                                  dim3(kThreads), args, 0, stream);
@@ -719,6 +720,28 @@ hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTa
   }
   if (D == 128) return NB == 1 ? launch_verify_t<float, 128, 1>(p, t, u, stream) : launch_verify_t<float, 128, 2>(p, t, u, stream);
   return NB == 1 ? launch_verify_t<float, 64, 1>(p, t, u, stream) : launch_verify_t<float, 64, 2>(p, t, u, stream);
+}
+
+// Resident verify work-groups per compute unit (0 if the runtime cannot say).
+template <typename T, int D, int NB>
+static int blocks_per_cu_t() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>),
+                                                     kThreads, 0) != hipSuccess)
+      b = 0;
+    return b;
+  }();
+  return n;
+}
+
+int verify_blocks_per_cu(int dtype, int D, int NB) {
+  if (dtype == 1) {
+    if (D == 128) return NB == 1 ? blocks_per_cu_t<__bf16, 128, 1>() : blocks_per_cu_t<__bf16, 128, 2>();
+    return NB == 1 ? blocks_per_cu_t<__bf16, 64, 1>() : blocks_per_cu_t<__bf16, 64, 2>();
+  }
+  if (D == 128) return NB == 1 ? blocks_per_cu_t<float, 128, 1>() : blocks_per_cu_t<float, 128, 2>();
+  return NB == 1 ? blocks_per_cu_t<float, 64, 1>() : blocks_per_cu_t<float, 64, 2>();
 }
 
 }  // namespace ripe
