@@ -60,13 +60,14 @@ int ring_width(const ripe_desc_t& d) {
 // never depends on the rest of the batch.  1024 positions, the best measured
 // trade-off between per-piece start-up and balance, unless full sequences
 // would then give more than about 1024 pieces per launch (longer pieces) or
-// fewer than about 256, too few for the 512 work-group slots of the device
-// (shorter pieces, down to 256 positions).
+// fewer than about 448 (shorter pieces, down to 256 positions): a launch
+// runs best when its long pieces nearly fill the 512 resident work-group
+// slots of the device in one round, leaving some for the short items.
 int split_len(const ripe_desc_t& d) {
   if (d.split_len > 0) return d.split_len;
   const int64_t work = int64_t(d.batch) * d.n_kv_heads * d.t_max;  // positions of full sequences
   int64_t s = std::max<int64_t>(1024, (work + 1023) / 1024);
-  s = std::min<int64_t>(s, std::max<int64_t>(256, (work + 255) / 256));
+  s = std::min<int64_t>(s, std::max<int64_t>(256, (work + 447) / 448));
   s = (s + 31) / 32 * 32;
   return int(std::min<int64_t>(std::max<int64_t>(s, 256), 8192));
 }
