@@ -343,6 +343,45 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     return res
 
 
+def run_accept(calls: int = 50, warmup: int = 5, B: int = 16, k: int = 4, V: int = 65536,
+               temperature: float = 0.8):
+    """ripe_accept at the c4 shape (16 sequences, k = 4 draft rows per chain,
+    a fallback for about 40% of them) over a 64K vocabulary: mean call time
+    with HIP events on the launch stream, and the logit bytes the row
+    statistics kernel reads (every target and draft row that a decision may
+    need: both chains' rows for sequences with a fallback, the primary's
+    otherwise)."""
+    import torch
+    import self_speculative_verify_ripe_amd as rp
+    from workloads import accept_inputs
+    dev = torch.device("cuda:0")
+    inp = accept_inputs(20261203, B, k, V, temperature)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    args = [t(inp.target), t(inp.draft), t(inp.tokens), t(inp.has_fallback), t(inp.rand.view(np.int32))]
+    outs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(3)]
+    d = rp.make_accept_desc(B, k, V, temperature)
+    ws = torch.empty(max(256, rp.ripe_accept_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        rp.ripe_accept(d, *args, *outs, ws, None, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        rp.ripe_accept(d, *args, *outs, ws, None, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    n_fb = int(inp.has_fallback.astype(bool).sum())
+    rows = B * (2 * k + 1) + n_fb * (2 * k)  # primary k+1 target + k draft; fallback k target + k draft
+    nbytes = rows * V * 4
+    return {"workload": f"c4 shape: B={B}, k={k}, V={V}, temperature {temperature}, {n_fb} fallbacks",
+            "avg_call_us": round(us, 2), "logit_bytes_per_call": nbytes,
+            "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "n_accept_histogram": np.bincount(outs[0].cpu().numpy(), minlength=k + 1).tolist()}
+
+
 EXTRA_WORKLOADS = [("c2", "ripe"), ("c2", "full"), ("c2", "deepest"), ("c4", None),
                    ("c5-ripe", None), ("c5-full", None), ("c5-deepest", None)]
 
@@ -404,6 +443,8 @@ def main():
                 "ms_per_step": round(e["ms_per_step"], 3), "calls_per_step": e["calls_per_step"],
                 "workload": e["describe"]}
         result["by_workload"] = extra
+    if not args.no_extra:
+        result["accept"] = run_accept()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(r["case"], r["layout"], args.cpu_seconds)
     line = json.dumps(result)

@@ -210,6 +210,88 @@ ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len
                           const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
                           int32_t n_rows, void* stream);
 
+/*
+ * Accept / rollback after verification (LoopSpec summary, rit.work blog,
+ * section on the second branch; RIPE abstract, zhuanzhiai.com paper page: the
+ * target distributions come from the verify pass at depth R).
+ *
+ * Per sequence b there is a primary chain of k draft tokens and, when
+ * has_fallback[b] != 0, a fallback chain of k tokens that replaces the
+ * primary from position 0 (an alternative first token drawn from the deeper
+ * state's distribution after the first proposal is taken out, followed by
+ * its own continuation).  The rows:
+ *
+ *  target_logits device float [batch][2][k+1][vocab]: row [b][c][i] gives
+ *                the target distribution softmax(z / temperature) of position
+ *                i of chain c (c = 0 primary, 1 fallback); row k scores the
+ *                bonus position after a fully accepted chain.  Position 0 of
+ *                both chains follows the same committed prefix, so the
+ *                fallback's row 0 is not read.
+ *  draft_logits  device float [batch][2][k][vocab]: row [b][0][i] is the
+ *                distribution q_i the primary's token i was drawn from; row
+ *                [b][1][0] is the deeper state's distribution m (the fallback's
+ *                first token was drawn from q' = norm(max(0, m - q_0))), rows
+ *                [b][1][i >= 1] are the fallback's draft distributions.  Not
+ *                read when temperature == 0.
+ *  tokens        device int32 [batch][2][k]: the drafted tokens; a token
+ *                outside [0, vocab) is never accepted
+ *  has_fallback  device uint8 [batch]
+ *  rand          device uint32 [batch][2k+1]: random words, u = word / 2^32;
+ *                word i for the primary's test i, word k for the fallback's
+ *                first test, word k+i for the fallback's test i >= 1, word 2k
+ *                for the final draw.  Not read when temperature == 0.
+ *  n_accept, branch, next_token   device int32 [batch], written: tokens kept,
+ *                the chain they come from (0 when none are kept), and the
+ *                token that follows them (a correction, or a bonus token
+ *                after a fully accepted chain).  With the verify call's
+ *                groups, n_accept and the kept chain's first row are the
+ *                n_accept / src_row of ripe_commit.
+ *  workspace     device, ripe_accept_workspace_bytes(desc) bytes, 256-byte
+ *                aligned; contents need no initialisation and are clobbered
+ *
+ * Rules (the scheme in full; all arithmetic in double):
+ *  - temperature == 0 (greedy): a token is accepted iff it is the arg max of
+ *    its target row (lowest index on ties).  The primary chain is checked in
+ *    order; if its first token is rejected and a fallback exists, the
+ *    fallback's first token is checked against the primary's row 0 and, if
+ *    accepted, the fallback chain continues.  The next token is the arg max
+ *    of the target row at the position where the kept chain stopped (row 0
+ *    of the primary when nothing is kept).
+ *  - temperature > 0 (speculative sampling): token t of a row is accepted iff
+ *    u * q(t) < p(t), i.e. with probability min(1, p(t)/q(t)).  At the
+ *    primary's first rejection j, with no fallback or j > 0, n = j and the
+ *    next token is drawn from max(0, p_j - q_j).  At j = 0 with a fallback,
+ *    the fallback's first token y is tested against the residual target
+ *    r = norm(max(0, p_0 - q_0)) with q': u * q'(y) < r(y); if accepted the
+ *    fallback chain continues with the ordinary test (rejection at j':
+ *    draw from max(0, p'_j' - q'_j')); if rejected, n = 0 and the next token
+ *    is drawn from max(0, r - q') (restart after two rejections).  A fully
+ *    accepted chain draws its bonus token from its row k.  A draw from
+ *    weights w takes the first index whose running sum exceeds u * sum(w),
+ *    or the last index with w > 0 if rounding leaves none; a residual with
+ *    no mass is replaced by the row's target distribution (r after a
+ *    restart).  Sampling this way keeps each output token's probability
+ *    under ordinary decoding.
+ *
+ * desc->batch >= 0 (0 is a no-op), 1 <= k <= 64, 1 <= vocab <= 2^24,
+ * temperature finite and >= 0.  Every row needs at least one finite logit.
+ */
+typedef struct ripe_accept_desc {
+  int32_t batch;
+  int32_t k;
+  int32_t vocab;
+  float temperature;
+} ripe_accept_desc_t;
+
+/* Workspace bytes of ripe_accept, or a negative ripe_status_t for an invalid
+ * descriptor. */
+int64_t ripe_accept_workspace_bytes(const ripe_accept_desc_t* desc);
+
+ripe_status_t ripe_accept(const ripe_accept_desc_t* desc, const float* target_logits,
+                          const float* draft_logits, const int32_t* tokens, const uint8_t* has_fallback,
+                          const uint32_t* rand, int32_t* n_accept, int32_t* branch, int32_t* next_token,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -106,6 +106,8 @@ def check_token(p: np.ndarray, q: np.ndarray, t: int, u: float):
     if t < 0 or t >= p.size:
         return False, np.inf
     a, b = u * q[t], p[t]
+    if a == 0.0 and b == 0.0:
+        return False, np.inf  # exact zeros: no rounding can flip this
     return bool(a < b), abs(b - a) / max(b, a, 1e-300)
 
 
@@ -150,7 +152,7 @@ def accept(target_logits, draft_logits, tokens, has_fallback, rand, temperature:
     br_out = np.zeros(B, np.int32)
     nx_out = np.zeros(B, np.int32)
     mg_out = np.full(B, np.inf)
-    tau = float(temperature)
+    tau = float(np.float32(temperature))  # the temperature is a float32 parameter
     for b in range(B):
         if tau == 0.0:
             n, br, nx = _greedy(tl[b], tok[b], bool(fb[b]), k, V)
@@ -203,8 +205,13 @@ def _sample(tl, dl, tok, fb, rw, k, tau):
     r = w_r / w_r.sum() if w_r.sum() > 0 else p[0]
     w_m = residual(softmax(dl[1][0], tau), q_j)
     q1 = w_m / w_m.sum() if w_m.sum() > 0 else np.zeros_like(w_m)
-    acc, m = check_token(r, q1, int(tok[1][0]), uniform(rw[k]))
+    y = int(tok[1][0])
+    acc, m = check_token(r, q1, y, uniform(rw[k]))
     margin = min(margin, m)
+    if 0 <= y < r.size:  # r(y), q'(y) come through max(0, .): how close each clamp was
+        pm = softmax(dl[1][0], tau)
+        for a, c in ((p[0][y], q_j[y]), (pm[y], q_j[y])):
+            margin = min(margin, abs(a - c) / max(a, c, 1e-300))
     if not acc:
         t, m = draw(residual(r, q1), u_last, r)
         return 0, 0, t, min(margin, m)

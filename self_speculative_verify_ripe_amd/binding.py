@@ -42,6 +42,11 @@ class ripe_group_t(ctypes.Structure):
                 ("n_rows", ctypes.c_int32)]
 
 
+class ripe_accept_desc_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("k", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("temperature", ctypes.c_float)]
+
+
 def _load():
     # torch ships its own HIP runtime under the same soname as /opt/rocm's.
     # Load torch first so that libripe.so binds to the runtime torch already
@@ -62,6 +67,10 @@ def _load():
                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), P,
                                 ctypes.c_int32, P]
     lib.ripe_commit.restype = ctypes.c_int
+    lib.ripe_accept_workspace_bytes.argtypes = [ctypes.POINTER(ripe_accept_desc_t)]
+    lib.ripe_accept_workspace_bytes.restype = ctypes.c_int64
+    lib.ripe_accept.argtypes = [ctypes.POINTER(ripe_accept_desc_t)] + [P] * 9 + [ctypes.c_size_t, P]
+    lib.ripe_accept.restype = ctypes.c_int
     return lib
 
 
@@ -174,3 +183,43 @@ def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],
     if st != 0:
         raise RipeError(st, "ripe_commit")
     return sl
+
+
+def make_accept_desc(batch: int, k: int, vocab: int, temperature: float) -> ripe_accept_desc_t:
+    return ripe_accept_desc_t(int(batch), int(k), int(vocab), float(temperature))
+
+
+def ripe_accept_workspace_bytes(desc: ripe_accept_desc_t) -> int:
+    n = int(lib.ripe_accept_workspace_bytes(ctypes.byref(desc)))
+    if n < 0:
+        raise RipeError(n, "ripe_accept_workspace_bytes")
+    return n
+
+
+def ripe_accept(desc: ripe_accept_desc_t, target_logits, draft_logits, tokens, has_fallback, rand,
+                n_accept, branch, next_token, workspace=None, workspace_bytes: Optional[int] = None,
+                stream=None) -> None:
+    """Accept / rollback (asynchronous on ``stream``); every array is a device tensor."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(ripe_accept_workspace_bytes(desc), dtype=torch.uint8,
+                                device=n_accept.device)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.ripe_accept(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits), _ptr(tokens),
+                         _ptr(has_fallback), _ptr(rand), _ptr(n_accept), _ptr(branch), _ptr(next_token),
+                         _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_accept")
+
+
+def commit_args(n_accept, branch, primary_rows, fallback_rows):
+    """ripe_commit's n_accept / src_row (host int32 arrays) from an accept
+    result: the kept tokens start at the first draft row of the chosen
+    chain's group.  primary_rows / fallback_rows: first row of each
+    sequence's primary / fallback group (fallback ignored where unused)."""
+    n = _i32(n_accept)
+    br = _i32(branch, n.size)
+    src = np.where(br == 1, _i32(fallback_rows, n.size), _i32(primary_rows, n.size)).astype(np.int32)
+    src[n == 0] = 0
+    return n, src

@@ -16,6 +16,7 @@
 #include <cstring>
 #include <vector>
 
+#include "accept.h"
 #include "plan.h"
 #include "ripe.h"
 
@@ -556,4 +557,60 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
     if (hip_status(launch_commit(p, d.dtype, D, hs), "ripe_commit") != RIPE_OK) return RIPE_EHIP;
   for (int b = 0; b < d.batch; ++b) seq_len[b] += n_accept[b];
   return RIPE_OK;
+}
+
+extern "C" int64_t ripe_accept_workspace_bytes(const ripe_accept_desc_t* desc) {
+  if (desc == nullptr) return RIPE_EINVAL;
+  const ripe_accept_desc_t& d = *desc;
+  if (d.batch < 0 || d.k < 1 || d.vocab < 1 || !std::isfinite(d.temperature) || d.temperature < 0.f)
+    return RIPE_EINVAL;
+  if (d.k > 64 || d.vocab > (1 << 24)) return RIPE_EUNSUPPORTED;
+  if (d.batch == 0) return 0;
+  return accept_layout(d.batch, d.k, d.vocab).bytes;
+}
+
+extern "C" ripe_status_t ripe_accept(const ripe_accept_desc_t* desc, const float* target_logits,
+                                     const float* draft_logits, const int32_t* tokens,
+                                     const uint8_t* has_fallback, const uint32_t* rand, int32_t* n_accept,
+                                     int32_t* branch, int32_t* next_token, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const int64_t need = ripe_accept_workspace_bytes(desc);
+  if (need < 0) return static_cast<ripe_status_t>(need);
+  const ripe_accept_desc_t& d = *desc;
+  if (d.batch == 0) return RIPE_OK;
+  const bool greedy = d.temperature == 0.f;
+  if (target_logits == nullptr || tokens == nullptr || has_fallback == nullptr || n_accept == nullptr ||
+      branch == nullptr || next_token == nullptr || (!greedy && (draft_logits == nullptr || rand == nullptr)))
+    return RIPE_EINVAL;
+  const void* ptrs[] = {target_logits, draft_logits, tokens, has_fallback, rand, n_accept, branch, next_token};
+  for (const void* q : ptrs)
+    if (q != nullptr && !aligned(q, 16)) return RIPE_EINVAL;
+  if (workspace == nullptr || int64_t(workspace_bytes) < need) return RIPE_EWORKSPACE;
+  if (!aligned(workspace, 256)) return RIPE_EINVAL;
+  AcceptParams p;
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = tokens;
+  p.has_fb = has_fallback;
+  p.rand = rand;
+  p.n_accept = n_accept;
+  p.branch = branch;
+  p.next_token = next_token;
+  const AcceptLayout L = accept_layout(d.batch, d.k, d.vocab);
+  char* ws = static_cast<char*>(workspace);
+  p.part = reinterpret_cast<RowStat*>(ws + L.off_part);
+  p.stats = reinterpret_cast<RowStat*>(ws + L.off_stats);
+  p.state = reinterpret_cast<SeqState*>(ws + L.off_state);
+  p.sums = reinterpret_cast<double*>(ws + L.off_sums);
+  p.tiles = reinterpret_cast<double*>(ws + L.off_tiles);
+  p.last = reinterpret_cast<int32_t*>(ws + L.off_last);
+  p.split = L.split;
+  p.slice = L.slice;
+  p.n_tiles = L.n_tiles;
+  p.B = d.batch;
+  p.k = d.k;
+  p.V = d.vocab;
+  p.greedy = greedy ? 1 : 0;
+  p.inv_tau = greedy ? 0.0 : 1.0 / double(d.temperature);
+  return hip_status(launch_accept(p, static_cast<hipStream_t>(stream)), "ripe_accept");
 }

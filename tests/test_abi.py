@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert names == ["ripe_commit", "ripe_layout_bytes", "ripe_verify_attn"]
+    assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_layout_bytes",
+                     "ripe_verify_attn"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -36,6 +37,7 @@ def test_header_symbols_exported():
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(rp.ripe_desc_t) == 12 * 4
     assert ctypes.sizeof(rp.ripe_group_t) == 16
+    assert ctypes.sizeof(rp.ripe_accept_desc_t) == 16
 
 
 @pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
@@ -162,3 +164,61 @@ def test_commit_nothing_accepted_is_noop():
 def test_commit_null_buffers():
     st, sl = call_commit(desc2(), [7, 9], [1, 0], [0, 0], cache=0)
     assert st == -1 and sl.tolist() == [7, 9]
+
+
+# ---------------------------------------------------------------------------
+# ripe_accept: descriptor and argument checks (no HIP call on these paths)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("batch,k,vocab,temp,status", [
+    (-1, 4, 100, 1.0, rp.binding.RipeError), (2, 0, 100, 1.0, None), (2, 65, 100, 1.0, None),
+    (2, 4, 0, 1.0, None), (2, 4, (1 << 24) + 1, 1.0, None), (2, 4, 100, -0.5, None),
+    (2, 4, 100, float("nan"), None), (2, 4, 100, float("inf"), None)])
+def test_accept_bad_descriptor(batch, k, vocab, temp, status):
+    d = rp.make_accept_desc(batch, k, vocab, temp)
+    with pytest.raises(rp.RipeError) as e:
+        rp.ripe_accept_workspace_bytes(d)
+    expect = -4 if (k > 64 or vocab > (1 << 24)) else -1
+    assert e.value.status == expect
+
+
+def test_accept_workspace_bytes():
+    wb = lambda B, k, V: rp.ripe_accept_workspace_bytes(rp.make_accept_desc(B, k, V, 0.8))
+    assert wb(0, 1, 7) == 0
+    base = wb(16, 4, 65536)
+    assert base > 0 and base % 256 == 0
+    # at least the row statistics (4k + 2 rows of 16 bytes per sequence) and one
+    # double per 64-index tile per sequence
+    assert base >= 16 * 18 * 16 + 16 * (65536 // 64) * 8
+    assert wb(32, 4, 65536) > base and wb(16, 8, 65536) > base and wb(16, 4, 1 << 20) > base
+
+
+def call_accept(d, **over):
+    args = dict(target=FAKE, draft=FAKE, tokens=FAKE, fb=FAKE, rand=FAKE, n=FAKE, br=FAKE, nx=FAKE,
+                ws=FAKE, ws_bytes=1 << 20)
+    args.update(over)
+    return binding.lib.ripe_accept(ctypes.byref(d), args["target"], args["draft"], args["tokens"], args["fb"],
+                                   args["rand"], args["n"], args["br"], args["nx"], args["ws"],
+                                   args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"target": None}, -1), ({"tokens": None}, -1), ({"fb": None}, -1), ({"n": None}, -1),
+    ({"br": None}, -1), ({"nx": None}, -1), ({"draft": None}, -1), ({"rand": None}, -1),
+    ({"target": FAKE + 4}, -1), ({"nx": FAKE + 8}, -1), ({"ws": None}, -5), ({"ws_bytes": 100}, -5),
+    ({"ws": FAKE + 16}, -1)])
+def test_accept_rejects(over, status):
+    assert call_accept(rp.make_accept_desc(2, 4, 100, 0.7), **over) == status
+
+
+def test_accept_greedy_needs_no_draft_or_rand_but_checks_the_rest():
+    d = rp.make_accept_desc(2, 4, 100, 0.0)
+    assert call_accept(d, target=None, draft=None, rand=None) == -1
+
+
+def test_accept_empty_batch_is_noop():
+    assert call_accept(rp.make_accept_desc(0, 4, 100, 0.7), target=None, ws=None, ws_bytes=0) == 0
+
+
+def test_commit_args_from_accept_result():
+    n, src = rp.commit_args([0, 3, 2], [0, 0, 1], [10, 20, 30], [14, 24, 34])
+    assert list(n) == [0, 3, 2] and list(src) == [0, 20, 34]

@@ -5,3 +5,4 @@ none of the method's arithmetic: no plane selection, no attention, no commit
 rule and no byte layout.
 """
 from .synth import *  # noqa: F401,F403
+from .accept_inputs import *  # noqa: F401,F403
