@@ -14,7 +14,9 @@ verified draft tokens per second, the roofline of the verify kernel
 (algorithmic bytes per call / average call duration: the time between HIP
 events on the launch stream that bracket each step's verify calls, divided by
 the number of calls), and the float64 oracle timed on host cores on a bounded
-sample.
+sample.  Unless --no-extra: the other workloads' figures, one step's verify
+calls captured into a HIP graph and replayed (graph_replay), and the accept
+call at the c4 shape (accept).
 """
 from __future__ import annotations
 
@@ -172,7 +174,7 @@ def counted_traffic(workload: str):
 
 
 def run_workload(name, layout_override, steps, warmup, split_len, layers, depths_arg,
-                 copy_calibration_mib=0):
+                 copy_calibration_mib=0, graph=False):
     import torch
     import self_speculative_verify_ripe_amd as rp
     from workloads import device_kv_rows
@@ -338,9 +340,43 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
         "layout": layout,
         "dtype": case.dtype,
     }
+    if graph:
+        res["graph"] = graph_replay(one_step_verify_calls=lambda st: [
+            rp.ripe_verify_attn(desc, caches[layer], seq_len, packed_sets[gi], n_rows, 1.0, q, kv_new, out,
+                                lse, None, ws, ws_bytes, st)
+            for gi in range(len(group_sets)) for layer in range(L)], n_calls=n_calls, steps=steps)
     del caches, q, kv_new, out, lse, ws
     torch.cuda.empty_cache()
     return res
+
+
+def graph_replay(one_step_verify_calls, n_calls, steps):
+    """One step's verify calls (fixed lengths) captured into a HIP graph
+    (torch.cuda.CUDAGraph) and replayed: mean call time from HIP events, and
+    the host time per replay."""
+    import torch
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        one_step_verify_calls(st)  # warm the library's plan cache on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        one_step_verify_calls(st)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    h0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    host = time.perf_counter() - h0
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    return {"avg_call_us": round(t / (steps * n_calls) * 1e6, 2),
+            "host_us_per_replay": round(host / steps * 1e6, 1), "calls_per_replay": n_calls}
 
 
 def run_accept(calls: int = 50, warmup: int = 5, B: int = 16, k: int = 4, V: int = 65536,
@@ -396,7 +432,7 @@ def main():
     import torch
     torch.cuda.set_device(0)
     r = run_workload(args.workload, args.layout, args.steps, args.warmup, args.split_len,
-                     args.layers, args.depths, args.copy_calibration)
+                     args.layers, args.depths, args.copy_calibration, graph=not args.no_extra)
     workload_key = f"{args.workload}-{r['layout']}" if not args.workload.startswith("c5") \
         else args.workload
     traffic = counted_traffic(workload_key) if args.split_len == 0 and args.layers is None \
@@ -429,6 +465,8 @@ def main():
         "host_enqueue_us_per_call": round(r["host_us_per_call"], 1),
         "gpu_us_per_call": round(r["gpu_us_per_call"], 2),
     }
+    if "graph" in r:
+        result["graph_replay"] = r["graph"]
     if not args.no_extra:
         extra = {}
         for name, lay in EXTRA_WORKLOADS:

@@ -31,6 +31,11 @@
  *    error nothing is launched and no output (device or host) is modified.
  *  - Device pointers must be 16-byte aligned (workspace: 256-byte aligned).
  *  - Input values must be finite.
+ *  - A call launches kernels only (no allocation, no memset, no host
+ *    synchronisation), so ripe_verify_attn and ripe_accept can be captured
+ *    into a HIP graph; a captured call keeps the host arguments (sequence
+ *    lengths, groups) it was captured with.  ripe_commit updates seq_len on
+ *    the host, so a captured commit would replay the same positions.
  */
 #ifndef RIPE_H_
 #define RIPE_H_
