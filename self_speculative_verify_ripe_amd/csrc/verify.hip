@@ -448,9 +448,9 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     setup_columns();
     const GroupRec& g = p.grp[pc.gidx];
     const int Hd = p.H * D;
-    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
-    const T* vb = static_cast<const T*>(p.kv_new) +
-                  (size_t(p.R + pc.depth - 1) * p.n_rows + g.row_start) * Hd + size_t(h) * D;
+    const size_t row0 = size_t(g.row_start) + size_t(pc.c0);  // the piece's first row
+    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
+    const T* vb = static_cast<const T*>(p.kv_new) + (size_t(p.R + pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
     T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
     constexpr int CPR = D / VEC;  // 16-byte pieces per row
     const int len = pc.len;

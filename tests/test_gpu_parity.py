@@ -176,6 +176,15 @@ def test_long_draft_block_spans_steps():
         run_case(case, layout, case.groups_at(2), tag="k=40")
 
 
+@pytest.mark.parametrize("split_len", [32, 64])
+def test_draft_block_longer_than_a_piece(split_len):
+    """A group's own rows cut into several pieces (k = 80 rows, pieces of at
+    most 32 or 64): each piece reads its own rows and keeps the causal mask."""
+    case = make_case("c3", B=2, T_range=(60, 130), k=80, R=4, Hkv=2, Hq=4)
+    for layout in LAYOUTS:
+        run_case(case, layout, case.groups_at(2), split_len=split_len, tag=f"k=80 split={split_len}")
+
+
 def test_many_query_columns_per_kv_head():
     # GQA 32/1 with 8 rows: 256 columns per KV head -> eight column chunks
     case = make_case("c3", B=2, T_range=(150, 260), Hkv=1, Hq=32, R=5)
