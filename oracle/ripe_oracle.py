@@ -53,17 +53,26 @@ def layout_code(layout) -> int:
 
 def _group_fields(g) -> Tuple[int, int, int, int]:
     if isinstance(g, tuple):
-        return tuple(int(x) for x in g)  # type: ignore[return-value]
+        return tuple(int(x) for x in g[:4])  # type: ignore[return-value]
     return int(g.seq), int(g.depth), int(g.row_start), int(g.n_rows)
+
+
+def _parent_fields(g) -> Tuple[int, int]:
+    """(row_start, n_rows) of a group's in-flight parent block; (0, 0) if none."""
+    if isinstance(g, tuple):
+        return (int(g[4]), int(g[5])) if len(g) >= 6 else (0, 0)
+    return int(getattr(g, "parent_row_start", 0)), int(getattr(g, "parent_rows", 0))
 
 
 # ---------------------------------------------------------------------------
 # plane selection (RIPE abstract: full cache reads plane r; one shared plane
 # reads plane R; RIPE keeps the deepest plane except a recent window)
 # ---------------------------------------------------------------------------
-def plane_select(layout, R: int, W: int, T: int, r: int) -> np.ndarray:
+def plane_select(layout, R: int, W: int, T: int, r: int, parent_rows: int = 0) -> np.ndarray:
     """Plane (1..R) that a query issued at depth r reads for each committed
-    prefix position j in [0, T)."""
+    prefix position j in [0, T).  With a parent block of ``parent_rows`` rows
+    still in flight, the prefix is read as it will be once the parent is
+    committed: the window is the last W positions of T + parent_rows."""
     layout = layout_code(layout)
     if not 1 <= r <= R:
         raise ValueError("depth out of range")
@@ -74,7 +83,7 @@ def plane_select(layout, R: int, W: int, T: int, r: int) -> np.ndarray:
         elif layout == DEEPEST:
             out[j] = R
         else:
-            out[j] = r if j >= T - W else R
+            out[j] = r if j >= T + parent_rows - W else R
     return out
 
 
@@ -281,11 +290,13 @@ def commit(cache: LogicalCache, n_accept: Sequence[int], src_row: Sequence[int],
 # ---------------------------------------------------------------------------
 # verification attention
 # ---------------------------------------------------------------------------
-def gather_prefix(cache: LogicalCache, b: int, r: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def gather_prefix(cache: LogicalCache, b: int, r: int,
+                  parent_rows: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Keys, values [T, Hkv, D] and plane ids [T] that a depth-r query of
-    sequence b reads from the committed prefix."""
+    sequence b reads from the committed prefix (with ``parent_rows`` rows of
+    a parent block in flight, see plane_select)."""
     T = int(cache.seq_len[b])
-    sel = plane_select(cache.layout, cache.R, cache.W, T, r)
+    sel = plane_select(cache.layout, cache.R, cache.W, T, r, parent_rows)
     K = np.empty((T, cache.Hkv, cache.D))
     V = np.empty((T, cache.Hkv, cache.D))
     j = 0
@@ -319,6 +330,26 @@ def draft_rows(kv_new: np.ndarray, r: int, s: int, k: int) -> Tuple[np.ndarray, 
     return kv_new[0, r - 1, s:s + k], kv_new[1, r - 1, s:s + k]
 
 
+def parent_block(kv_new: np.ndarray, layout, R: int, W: int, T: int, r: int, s: int,
+                 k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """K, V [k, Hkv, D] of an in-flight parent block (draft rows s..s+k-1, to
+    become positions T..T+k-1), each row at the plane it will be read from
+    once committed: FULL depth r, DEEPEST depth R, RIPE depth r inside the
+    window of the last W positions of T + k and depth R before it."""
+    layout = layout_code(layout)
+    K = np.empty((k,) + kv_new.shape[3:])
+    V = np.empty((k,) + kv_new.shape[3:])
+    for i in range(k):
+        if layout == FULL:
+            d = r
+        elif layout == DEEPEST:
+            d = R
+        else:
+            d = r if T + i >= T + k - W else R
+        K[i], V[i] = kv_new[0, d - 1, s + i], kv_new[1, d - 1, s + i]
+    return K, V
+
+
 def visibility(T: int, k: int) -> np.ndarray:
     """[k, T + k] mask: every row sees the whole committed prefix; row i of the
     block sees the block's rows 0..i."""
@@ -339,7 +370,12 @@ def verify(cache: LogicalCache, groups: Iterable, q: np.ndarray, kv_new: np.ndar
     q is [n_rows, Hq, D]; kv_new is [2, R, n_rows, Hkv, D].  Group g (sequence
     b, depth r, rows [s, s + k)) attends, for query head h and KV head
     h // (Hq / Hkv), over the committed prefix read per the layout's plane
-    rule at depth r, then over its own rows s..s+i at depth r (row i).
+    rule at depth r, then over its own rows s..s+i at depth r (row i).  A
+    group with a parent block in flight (parent_rows > 0) reads the prefix and
+    then every parent row as they will be read once the parent is committed
+    (plane_select, parent_block), so the result equals committing the parent
+    first (LoopSpec summary: the next position's computation starts before
+    the current one is confirmed).
 
     Returns out [n_rows, Hq, D] (NaN for rows no group covers), lse
     [n_rows, Hq] and the plane ids each group read (int8 [T_b]).
@@ -353,8 +389,12 @@ def verify(cache: LogicalCache, groups: Iterable, q: np.ndarray, kv_new: np.ndar
     sels = []
     for g in groups:
         b, r, s, k = _group_fields(g)
-        Kp, Vp, sel = gather_prefix(cache, b, r)
+        ps, kp = _parent_fields(g)
+        Kp, Vp, sel = gather_prefix(cache, b, r, kp)
         sels.append(sel)
+        if kp:  # the in-flight parent block follows the committed prefix
+            Ka, Va = parent_block(kv_new, cache.layout, cache.R, cache.W, Kp.shape[0], r, ps, kp)
+            Kp, Vp = np.concatenate([Kp, Ka]), np.concatenate([Vp, Va])
         T = Kp.shape[0]
         Kn, Vn = draft_rows(kv_new, r, s, k)
         vis = visibility(T, k)

@@ -287,11 +287,12 @@ def test_memory_model():
 # ---------------------------------------------------------------------------
 # planted mistakes must fail a pin
 # ---------------------------------------------------------------------------
-def _plane_select_off_by_one(layout, R, W, T, r):
+def _plane_select_off_by_one(layout, R, W, T, r, parent_rows=0):
     layout = ro.layout_code(layout)
     out = np.empty(T, dtype=np.int8)
     for j in range(T):
-        out[j] = r if layout == ro.FULL else (R if layout == ro.DEEPEST else (r if j > T - W else R))
+        out[j] = r if layout == ro.FULL else (R if layout == ro.DEEPEST else
+                                              (r if j > T + parent_rows - W else R))
     return out
 
 

@@ -52,11 +52,15 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
 @dataclass(frozen=True)
 class Group:
     """One draft block or branch: rows [row_start, row_start + n_rows) of the
-    query tensor, issued for sequence ``seq`` at loop depth ``depth``."""
+    query tensor, issued for sequence ``seq`` at loop depth ``depth``.  A
+    group verified while its parent block is still in flight names the
+    parent's rows (parent_row_start, parent_rows) in the draft tensors."""
     seq: int
     depth: int
     row_start: int
     n_rows: int
+    parent_row_start: int = 0
+    parent_rows: int = 0
 
 
 class PlaneModel:
