@@ -183,6 +183,34 @@ ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const
                                size_t workspace_bytes, void* stream);
 
 /*
+ * Verification while each group's parent block is still in flight (LoopSpec
+ * summary: the computation of the next position starts from an early draft
+ * before the current one is confirmed).  As ripe_verify_attn, with
+ *
+ *  parents   host int32 [n_groups][2]: (row_start, n_rows) of the group's
+ *            parent block in q / kv_new; n_rows = 0 means none.  The parent's
+ *            rows are the n_rows positions that follow the committed prefix
+ *            (T_b .. T_b + n_rows - 1); the group's own rows follow them.
+ *            All groups of one sequence name the same parent
+ *            (RIPE_EUNSUPPORTED otherwise); rows must lie in [0, n_rows)
+ *            (RIPE_ERANGE).
+ *
+ * Every position is read as it will be once the parent is committed, so the
+ * result equals committing the parent first and verifying then: the RIPE
+ * window is the last W positions of T_b + n_rows(parent), committed
+ * positions before it are read at plane R, and each parent row is read from
+ * kv_new at the plane that rule gives it (FULL: the group's depth r;
+ * DEEPEST: R; RIPE: r inside the window, R before it).  Every parent row is
+ * visible to every row of the group.  plane_sel covers the committed
+ * positions only.
+ */
+ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                        const ripe_group_t* groups, const int32_t* parents, int32_t n_groups,
+                                        int32_t n_rows, float softmax_scale, const void* q, const void* kv_new,
+                                        void* out, float* lse, int8_t* plane_sel, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * Commit accepted draft rows (RIPE abstract: the window of recent positions
  * is kept at full depth, older positions collapse to the deepest plane;
  * LoopSpec summary: rejected continuations are dropped and decoding resumes

@@ -54,7 +54,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libripe.so not built ({LIB_PATH}); run "
-                          "python -m self_speculative_verify_ripe_amd.build")
+                          "python self_speculative_verify_ripe_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     lib.ripe_layout_bytes.argtypes = [ctypes.POINTER(ripe_desc_t), ctypes.c_int32]
@@ -63,6 +63,11 @@ def _load():
                                      ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ripe_verify_attn.restype = ctypes.c_int
+    lib.ripe_verify_attn_inflight.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ripe_group_t), ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P,
+                                              ctypes.c_size_t, P]
+    lib.ripe_verify_attn_inflight.restype = ctypes.c_int
     lib.ripe_commit.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), P,
                                 ctypes.c_int32, P]
@@ -146,10 +151,25 @@ def new_workspace(desc: ripe_desc_t, device="cuda"):
                        device=device)
 
 
+def pack_parents(groups: Iterable) -> np.ndarray:
+    """Each group's in-flight parent block as an int32 array [n, 2] of
+    (parent_row_start, parent_rows); (0, 0) for groups without one."""
+    rows = []
+    for g in groups:
+        if isinstance(g, tuple):
+            rows.append((g[4], g[5]) if len(g) >= 6 else (0, 0))
+        else:
+            rows.append((getattr(g, "parent_row_start", 0), getattr(g, "parent_rows", 0)))
+    return np.ascontiguousarray(np.array(rows, dtype=np.int32).reshape(-1, 2))
+
+
 def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
                      n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
-                     workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
-    """Launch verification attention (asynchronous on ``stream``)."""
+                     workspace=None, workspace_bytes: Optional[int] = None, stream=None,
+                     parents=None) -> None:
+    """Launch verification attention (asynchronous on ``stream``).  Groups
+    with an in-flight parent block (``parents`` [n, 2], or groups carrying
+    parent_row_start / parent_rows) go through ripe_verify_attn_inflight."""
     sl = seq_len if (isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32
                      and seq_len.flags["C_CONTIGUOUS"]) else _i32(seq_len, desc.batch)
     if sl.size != desc.batch:
@@ -157,13 +177,30 @@ def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: I
     gptr, ng, _keep = _groups(groups)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ripe_verify_attn(ctypes.byref(desc), _ptr(cache),
-                              sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr, ng,
-                              int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
-                              _ptr(lse), _ptr(plane_sel), _ptr(workspace), int(workspace_bytes),
-                              _stream(stream))
+    if parents is None and not isinstance(groups, np.ndarray):
+        parents = pack_parents(groups)
+        if not parents.any():
+            parents = None
+    if parents is None:
+        st = lib.ripe_verify_attn(ctypes.byref(desc), _ptr(cache),
+                                  sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr, ng,
+                                  int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
+                                  _ptr(lse), _ptr(plane_sel), _ptr(workspace), int(workspace_bytes),
+                                  _stream(stream))
+        what = "ripe_verify_attn"
+    else:
+        par = np.ascontiguousarray(parents, dtype=np.int32).reshape(-1, 2)
+        if par.shape[0] != ng:
+            raise ValueError("parents must have one (row_start, n_rows) pair per group")
+        st = lib.ripe_verify_attn_inflight(ctypes.byref(desc), _ptr(cache),
+                                           sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr,
+                                           par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ng,
+                                           int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new),
+                                           _ptr(out), _ptr(lse), _ptr(plane_sel), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream))
+        what = "ripe_verify_attn_inflight"
     if st != 0:
-        raise RipeError(st, "ripe_verify_attn")
+        raise RipeError(st, what)
 
 
 def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],

@@ -1,6 +1,7 @@
 """Build libripe.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-Usage: ``python -m self_speculative_verify_ripe_amd.build`` (or ``build()``).
+Usage: ``python self_speculative_verify_ripe_amd/build.py`` (or ``build()``); run it as a
+script, since importing the package loads the library it is about to rebuild.
 """
 from __future__ import annotations
 

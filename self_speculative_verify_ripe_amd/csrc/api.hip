@@ -122,6 +122,7 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tpieces;
   if (d.layout == RIPE_LAYOUT_RIPE) per_seq += std::min<int64_t>(groups, d.R - 1) * ((We + S - 1) / S);
   per_seq += groups + (rows + S - 1) / S;  // draft rows
+  per_seq += (1 + std::min<int64_t>(groups, d.R)) * ((rows + S - 1) / S);  // an in-flight parent's rows
   const int64_t col_chunks = (rows * G + 15) / 16 + nseq;
   const long double slots = (long double)d.n_kv_heads * col_chunks * per_seq;
   const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4 + 256;
@@ -172,6 +173,7 @@ struct VerifyScratch {
   int key_NB = 1;
   std::vector<int32_t> key_seq;
   std::vector<ripe_group_t> key_groups;
+  std::vector<int32_t> key_parents;  // empty: no parents
 };
 
 VerifyScratch& verify_scratch() {
@@ -192,11 +194,12 @@ extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
   return RIPE_EINVAL;
 }
 
-extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
-                                          const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
-                                          float softmax_scale, const void* q, const void* kv_new, void* out,
-                                          float* lse, int8_t* plane_sel, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+// Both verify entry points.  parents: host [n_groups][2] (row_start, n_rows)
+// of each group's in-flight parent block, or nullptr for none.
+static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                          const ripe_group_t* groups, const int32_t* parents, int32_t n_groups, int32_t n_rows,
+                          float softmax_scale, const void* q, const void* kv_new, void* out, float* lse,
+                          int8_t* plane_sel, void* workspace, size_t workspace_bytes, void* stream) {
   ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
@@ -241,7 +244,10 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   if (sc.have_key && std::memcmp(&sc.key_desc, &d, sizeof(d)) == 0 && sc.key_rows == n_rows &&
       std::memcmp(&sc.key_scale, &softmax_scale, sizeof(float)) == 0 && sc.key_groups.size() == size_t(n_groups) &&
       std::memcmp(sc.key_seq.data(), seq_len, sizeof(int32_t) * size_t(d.batch)) == 0 &&
-      std::memcmp(sc.key_groups.data(), groups, sizeof(ripe_group_t) * size_t(n_groups)) == 0)
+      std::memcmp(sc.key_groups.data(), groups, sizeof(ripe_group_t) * size_t(n_groups)) == 0 &&
+      (parents == nullptr ? sc.key_parents.empty()
+                          : sc.key_parents.size() == 2 * size_t(n_groups) &&
+                                std::memcmp(sc.key_parents.data(), parents, sizeof(int32_t) * 2 * size_t(n_groups)) == 0))
     return launch_all(sc.key_NB);
   sc.have_key = false;
   sc.spans.clear();
@@ -257,6 +263,13 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   std::sort(sc.spans.begin(), sc.spans.end());
   for (size_t i = 1; i < sc.spans.size(); ++i)
     if (sc.spans[i - 1].first + sc.spans[i - 1].second > sc.spans[i].first) return RIPE_EINVAL;
+  if (parents != nullptr)
+    for (int i = 0; i < n_groups; ++i) {
+      const int32_t ps = parents[2 * i], kp = parents[2 * i + 1];
+      if (kp < 0) return RIPE_EINVAL;
+      if (kp > 0 && (ps < 0 || int64_t(ps) + kp > n_rows)) return RIPE_ERANGE;
+      if (kp > 65535) return RIPE_EUNSUPPORTED;
+    }
 
   // groups of each sequence in the caller's order (counting sort by sequence)
   sc.count.assign(d.batch + 1, 0);
@@ -302,6 +315,7 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
     p.n_units = 0;
     p.n_grp = 0;
     p.n_pieces = 0;
+    p.inflight = 0;
     p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
     return lp;
   };
@@ -320,10 +334,23 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
       nq += g.n_rows * G;
     }
     const int T = seq_len[b];
+    // the sequence's in-flight parent block: the same for all its groups
+    int ps = 0, kp = 0;
+    if (parents != nullptr) {
+      const int i0 = sc.order[g0];
+      ps = parents[2 * i0];
+      kp = parents[2 * i0 + 1];
+      for (int k = 1; k < gc; ++k) {
+        const int i = sc.order[g0 + k];
+        if (parents[2 * i + 1] != kp || (kp > 0 && parents[2 * i] != ps)) return RIPE_EUNSUPPORTED;
+      }
+      if (kp == 0) ps = 0;
+    }
+    const InFlight fl = in_flight(d.layout, We, T, kp);
     // pieces of this sequence: every segment cut into near-equal runs of at
     // most S positions
     sc.pieces.clear();
-    enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, [&](const Seg& sg) {
+    enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, kp, [&](const Seg& sg) {
       const int pl = piece_len(sg.len, S);
       for (int c0 = 0; c0 < sg.len; c0 += pl)
         sc.pieces.push_back(Piece{c0, std::min(pl, sg.len - c0), uint8_t(sg.kind), uint8_t(sg.depth),
@@ -354,6 +381,13 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
       sr.g_count = uint8_t(gc);
       sr.part0 = p.n_wg;  // one partial per item
       sr.unit0 = p.n_units;
+      sr.tw = fl.tw;
+      sr.parent_row0 = ps;
+      sr.kp = uint16_t(kp);
+      sr.nd = uint16_t(fl.nd);
+      sr.hole = uint16_t(fl.hole);
+      sr.ring_base = uint16_t(fl.ring_base);
+      if (kp > 0) p.inflight = 1;
       for (int k = 0; k < gc; ++k) {
         p.grp[p.n_grp] = grp[k];
         p.grp[p.n_grp].seq = uint8_t(p.n_seq);
@@ -458,8 +492,32 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
   sc.key_NB = NB;
   sc.key_seq.assign(seq_len, seq_len + d.batch);
   sc.key_groups.assign(groups, groups + n_groups);
+  if (parents != nullptr)
+    sc.key_parents.assign(parents, parents + 2 * size_t(n_groups));
+  else
+    sc.key_parents.clear();
   sc.have_key = true;
   return launch_all(NB);
+}
+
+extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                          const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                                          float softmax_scale, const void* q, const void* kv_new, void* out,
+                                          float* lse, int8_t* plane_sel, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return verify_impl(desc, cache, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q, kv_new, out, lse,
+                     plane_sel, workspace, workspace_bytes, stream);
+}
+
+extern "C" ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cache,
+                                                   const int32_t* seq_len, const ripe_group_t* groups,
+                                                   const int32_t* parents, int32_t n_groups, int32_t n_rows,
+                                                   float softmax_scale, const void* q, const void* kv_new,
+                                                   void* out, float* lse, int8_t* plane_sel, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (parents == nullptr && n_groups > 0) return RIPE_EINVAL;
+  return verify_impl(desc, cache, seq_len, groups, parents, n_groups, n_rows, softmax_scale, q, kv_new, out, lse,
+                     plane_sel, workspace, workspace_bytes, stream);
 }
 
 extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,

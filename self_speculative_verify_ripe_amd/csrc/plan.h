@@ -42,7 +42,11 @@ constexpr int kMaxItems = 2048;  // verify work items (and merge units) per laun
 constexpr int kMaxPieces = 512;  // pieces per launch
 constexpr int kSoloSteps = 4;    // a piece of at most this many steps runs on one wavefront
 
-enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2 };
+// kinds 3 and 4: the rows of a parent block still in flight, read from the
+// draft tensors at the plane they will be read from once committed: rows
+// below the window at plane R (every group sees them), rows inside it at
+// each group's depth (kind 4, one segment per distinct depth).
+enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2, kSegParentDeep = 3, kSegParentWin = 4 };
 
 struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   int32_t T;           // committed prefix length
@@ -56,7 +60,45 @@ struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   uint8_t g_begin;     // first group record of this sequence
   uint8_t g_count;     // its number of groups
   uint16_t nq;         // query columns = sum(rows) * (Hq / Hkv)
+  // RIPE window and in-flight parent (see InFlight)
+  int32_t tw;          // prefix positions before the window (RIPE, depth < R)
+  int32_t parent_row0; // first draft row of the in-flight parent block
+  uint16_t kp;         // its rows (0: none)
+  uint16_t nd;         // its rows below the window (read at plane R)
+  uint16_t hole;       // oldest ring slots not read (now before the window)
+  uint16_t ring_base;  // ring slot of the oldest window position
 };
+
+// Where the window falls for a sequence with committed length T, ring width
+// We, layout and a parent block of kp rows in flight: the prefix is read as
+// it will be once the parent is committed, i.e. with the window covering the
+// last We positions of T + kp.  A = first position inside that window.
+struct InFlight {
+  int tw;    // committed positions read at plane R by groups at depth < R (RIPE)
+  int hole;  // ring positions (oldest first) that lie before the window
+  int nd;    // parent rows before the window
+  int ring_base;
+};
+
+RIPE_HD inline InFlight in_flight(int layout, int We, int T, int kp) {
+  InFlight f;
+  const int Wb = We < T ? We : T;
+  const int A0 = T + kp - We;
+  const int A = A0 > 0 ? A0 : 0;
+  const int ring_lo = T - Wb;  // oldest position held in the ring
+  f.ring_base = We > 0 ? ring_lo % We : 0;
+  if (layout == 2) {
+    f.tw = A < T ? A : T;
+    f.hole = f.tw - ring_lo;
+    const int nd = A - T;
+    f.nd = nd < 0 ? 0 : (nd > kp ? kp : nd);
+  } else {
+    f.tw = T;
+    f.hole = 0;
+    f.nd = layout == 1 ? kp : 0;  // DEEPEST reads every parent row at plane R, FULL at depth r
+  }
+  return f;
+}
 
 struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
   int32_t row_start;
@@ -131,6 +173,7 @@ struct VerifyParams {
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
   int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
+  int32_t inflight;      // some sequence of the launch has a parent block in flight
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];
@@ -161,40 +204,40 @@ RIPE_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Visit the segments of one sequence in canonical order (kind 0, then kind 1,
 // then kind 2); `visit` returns true to stop.  Distinct depths are visited in
 // ascending order.
-template <class Visit>
+template <typename Visit>
 RIPE_HD inline void enumerate_segments(int layout, int R, int We, int T, const GroupRec* g, int g_begin,
-                                       int g_count, Visit&& visit) {
+                                       int g_count, int kp, Visit&& visit) {
+  const InFlight f = in_flight(layout, We, T, kp);
   const int Wb = We < T ? We : T;
   bool anyR = false;
   for (int i = 0; i < g_count; ++i) anyR |= (g[g_begin + i].depth == R);
-  if (layout == 0) {  // FULL: one plane segment per distinct depth
+  // visit one segment per distinct depth d with lo < d <= hi, in increasing order
+  auto per_depth = [&](int kind, int hi, int len) -> bool {
     int cur = 0;
-    while (T > 0) {
+    while (len > 0) {
       int nxt = 1 << 30;
       for (int i = 0; i < g_count; ++i) {
         const int d = g[g_begin + i].depth;
-        if (d > cur && d < nxt) nxt = d;
+        if (d > cur && d <= hi && d < nxt) nxt = d;
       }
       if (nxt == (1 << 30)) break;
-      if (visit(Seg{kSegPlane, nxt, -1, T})) return;
+      if (visit(Seg{kind, nxt, -1, len})) return true;
       cur = nxt;
     }
+    return false;
+  };
+  if (layout == 0) {  // FULL: one plane segment per distinct depth
+    if (per_depth(kSegPlane, R, T)) return;
   } else if (layout == 1) {  // DEEPEST
     if (T > 0 && visit(Seg{kSegPlane, R, -1, T})) return;
   } else {  // RIPE
-    const int deep = anyR ? T : T - Wb;
+    const int deep = anyR ? T : f.tw;
     if (deep > 0 && visit(Seg{kSegPlane, R, -1, deep})) return;
-    int cur = 0;
-    while (Wb > 0) {
-      int nxt = 1 << 30;
-      for (int i = 0; i < g_count; ++i) {
-        const int d = g[g_begin + i].depth;
-        if (d > cur && d < R && d < nxt) nxt = d;
-      }
-      if (nxt == (1 << 30)) break;
-      if (visit(Seg{kSegRing, nxt, -1, Wb})) return;
-      cur = nxt;
-    }
+    if (Wb > f.hole && per_depth(kSegRing, R - 1, Wb)) return;
+  }
+  if (kp > 0) {
+    if (f.nd > 0 && visit(Seg{kSegParentDeep, R, -1, f.nd})) return;
+    if (kp > f.nd && per_depth(kSegParentWin, R, kp - f.nd)) return;
   }
   for (int i = 0; i < g_count; ++i) {
     const GroupRec& gr = g[g_begin + i];

@@ -205,8 +205,12 @@ struct Softmax {
 
   // scores of one 32-position step: sacc[mb][nb][j] is position 8*lg+4*mb+j
   // of column ln+16*nb; positions >= lim[nb] (step-local) are invisible.
+  // When `hole` is set (wave-uniform) the step is a run of ring slots and the
+  // slots whose age rank (slot - ring_base mod We) is below hole_len are
+  // invisible too; slot0 is this step's first slot.
   __device__ inline void update(const floatx4 (&sacc)[2][NB], const int (&lim)[NB], float sl2,
-                                typename O::P (&pf)[NB]) {
+                                typename O::P (&pf)[NB], bool hole = false, int slot0 = 0, int ring_base = 0,
+                                int hole_len = 0, int We = 0) {
     const int lg = (threadIdx.x & 63) >> 4;
     float x[NB][8];
     bool grow = false;
@@ -221,8 +225,17 @@ struct Softmax {
           const int e = 4 * mb + j;
           const float v = (8 * lg + e < lim[nb]) ? sacc[mb][nb][j] * sl2 : -INFINITY;
           x[nb][e] = v;
-          mx = fmaxf(mx, v);
         }
+      if (hole) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int rel = slot0 + 8 * lg + e - ring_base;
+          if (rel < 0) rel += We;
+          if (rel < hole_len) x[nb][e] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[nb][e]);
       mx = wave_max_lanegroups(mx);
       const bool g = (mx > m[nb] + kLazy) || (m[nb] == -INFINITY && mx != -INFINITY);
       mref[nb] = g ? mx : m[nb];
@@ -298,8 +311,10 @@ constexpr int verify_lds_bytes() {
 // spread over the four wavefronts and merged through LDS, or up to four short
 // items, one per wavefront, each wavefront writing its own partial.  The
 // host's work-group table says which; the hardware dispatches work-groups in
-// grid order.
-template <typename T, int D, int NB>
+// grid order.  INF: the launch has in-flight parent blocks (parent segments,
+// ring slots hidden by the parent); launches without them use the kernel
+// compiled without that code, whose step loop it would otherwise slow down.
+template <typename T, int D, int NB, bool INF>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
 void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
@@ -361,11 +376,15 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       if (pc.kind == kSegPlane)
         hv = (p.layout == 0) ? (gd == pc.depth ? sr.T : 0)
              : (p.layout == 1) ? sr.T
-                               : (gd == p.R ? sr.T : sr.T - Wb);
+                               : (gd == p.R ? sr.T : sr.tw);
       else if (pc.kind == kSegRing)
         hv = (gd == pc.depth) ? Wb : 0;
-      else
+      else if (!INF || pc.kind == kSegDraft)
         hv = (gi == pc.gidx) ? row + 1 : 0;
+      else if (pc.kind == kSegParentDeep)  // in-flight parent rows: all visible
+        hv = pc.c0 + pc.len;
+      else
+        hv = (gd == pc.depth) ? pc.c0 + pc.len : 0;
       hi[nb] = valid ? hv - pc.c0 : 0;
     }
   };
@@ -376,7 +395,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   u32x4 kf[2][KC], vf[DB][VCH];
 
   // Wavefront w runs steps w, w + 4, ... of the piece.
-  if (pc.kind != kSegDraft) {
+  if (INF ? (pc.kind == kSegPlane || pc.kind == kSegRing) : pc.kind != kSegDraft) {
     // ---- prefix plane or window ring: raw buffer loads ------------------
     // The buffer resources span the piece only: loads past its end return
     // zeros.
@@ -417,6 +436,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
 #pragma unroll
         for (int c = 0; c < VCH; ++c) v[db][c] = bload16(vrs, base + (16 * db * bw + c * VEC) * E);
     };
+    const bool hole = INF && pc.kind == kSegRing && sr.hole > 0;
     // first step's loads go out before the query setup
     load_k(st0, st0 < nsteps, kf);
     load_v(st0, st0 < nsteps, vf);
@@ -429,8 +449,13 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       int lim[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - st * kStep;
+      // a ring whose oldest slots now lie before the window (a parent block
+      // in flight) does not read those slots
       typename O::P pf[NB];
-      sm.update(sacc, lim, sl2, pf);
+      if constexpr (INF)
+        sm.update(sacc, lim, sl2, pf, hole, pc.c0 + st * kStep, sr.ring_base, sr.hole, p.We);
+      else
+        sm.update(sacc, lim, sl2, pf);
       // a step reaching past the piece's end: zero the V values of the
       // missing positions (they may hold anything, even NaN)
       if ((st + 1) * kStep > pc.len) {
@@ -446,9 +471,13 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     // in MFMA order directly; V rows are staged in this wavefront's LDS slice
     // with 16-byte loads and read back transposed.
     setup_columns();
-    const GroupRec& g = p.grp[pc.gidx];
+    // the piece's first row: the group's own rows, or the in-flight parent's
+    // (the rows before its window first, then the window's)
     const int Hd = p.H * D;
-    const size_t row0 = size_t(g.row_start) + size_t(pc.c0);  // the piece's first row
+    const size_t row0 = (!INF || pc.kind == kSegDraft
+                             ? size_t(p.grp[pc.gidx].row_start)
+                             : size_t(sr.parent_row0) + (pc.kind == kSegParentWin ? sr.nd : 0)) +
+                        size_t(pc.c0);
     const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
     const T* vb = static_cast<const T*>(p.kv_new) + (size_t(p.R + pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
     T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
@@ -595,7 +624,6 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
   const int h = un.h;
   const size_t stride = size_t(CQ) * (D + 2);
   const float* const part_base = p.ws + (size_t(sr.part0) + size_t(hl * n_cc + cc) * sr.n_split) * stride;
-  const int Wb = min(p.We, sr.T);
   const int col = threadIdx.x / TPC;
   const int d0 = slice * SLICE + (threadIdx.x % TPC) * DPT;
   const bool col_valid = cc * CQ + col < sr.nq;
@@ -679,7 +707,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int j = j0 + e;
-          const int pl = (p.layout == 0) ? r : (p.layout == 1) ? p.R : ((j >= sr.T - Wb) ? r : p.R);
+          const int pl = (p.layout == 0) ? r : (p.layout == 1) ? p.R : ((j >= sr.tw) ? r : p.R);
           v[e] = int8_t(pl);
         }
         if (j0 + 16 <= sr.T) {
@@ -701,8 +729,9 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
   if (p.n_wg <= 0) return hipSuccess;
   const int grid = p.n_blocks;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>), dim3(grid),
-                                 dim3(kThreads), args, 0, stream);
+  const void* kern = p.inflight ? reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true>)
+                                : reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false>);
+  hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
   if (p.n_units * (D / 32) <= 1024)
@@ -727,7 +756,7 @@ template <typename T, int D, int NB>
 static int blocks_per_cu_t() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false>),
                                                      kThreads, 0) != hipSuccess)
       b = 0;
     return b;

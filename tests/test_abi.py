@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_layout_bytes",
-                     "ripe_verify_attn"]
+                     "ripe_verify_attn", "ripe_verify_attn_inflight"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -222,3 +222,33 @@ def test_accept_empty_batch_is_noop():
 def test_commit_args_from_accept_result():
     n, src = rp.commit_args([0, 3, 2], [0, 0, 1], [10, 20, 30], [14, 24, 34])
     assert list(n) == [0, 3, 2] and list(src) == [0, 20, 34]
+
+
+# ---------------------------------------------------------------------------
+# ripe_verify_attn_inflight: parent-block checks (no HIP call on these paths)
+# ---------------------------------------------------------------------------
+def call_inflight(groups, parents, seq_len=(10, 20), n_rows=16, ws_bytes=1 << 40):
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    garr, ng, _keep = binding._groups(groups)
+    par = None if parents is None else np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(-1, 2))
+    return binding.lib.ripe_verify_attn_inflight(
+        ctypes.byref(desc2()), FAKE, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr,
+        None if par is None else par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ng, n_rows, 1.0,
+        FAKE, FAKE, FAKE, None, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("groups,parents,status", [
+    ([(0, 1, 4, 4)], None, -1),                               # parents missing
+    ([(0, 1, 4, 4)], [(0, -1)], -1),                          # negative parent length
+    ([(0, 1, 4, 4)], [(-1, 2)], -2),                          # parent row before 0
+    ([(0, 1, 4, 4)], [(14, 4)], -2),                          # parent rows past n_rows
+    ([(0, 1, 4, 4), (0, 2, 8, 4)], [(0, 4), (0, 3)], -4),     # siblings with different parents
+    ([(0, 1, 4, 4), (0, 2, 8, 4)], [(0, 4), (1, 4)], -4),
+    ([(0, 1, 4, 4), (0, 2, 8, 4)], [(0, 4), (0, 0)], -4),     # one sibling without the parent
+])
+def test_inflight_rejects(groups, parents, status):
+    assert call_inflight(groups, parents) == status
+
+
+def test_inflight_no_groups_is_noop():
+    assert call_inflight(np.zeros((0, 4), np.int32), None) == 0
