@@ -173,11 +173,11 @@ struct VerifyParams {
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
   int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
-  int32_t inflight;      // some sequence of the launch has a parent block in flight
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];
   uint16_t gorig[kMaxGroups];  // index of each group in the caller's array
+  int32_t inflight;      // some sequence of the launch has a parent block in flight
 };
 
 struct CommitJob {     // rows of one sequence written to one region (20 bytes)
