@@ -9,6 +9,9 @@ benchmark configurations c1..c5 of this repository; the values are synthetic:
 * deepest plane K_R, V_R ~ N(0, 1);
 * plane p = plane R + decay**(R - p) * N(0, 1) (noise term times ``tail_mult``
   at a seeded 1% of positions in c2, to mimic heavy-tail error positions);
+  with ``convention="pages"`` the noise scale is decay**(p - 1) instead, so
+  that the planes approach the deepest one as the loops proceed (plane 1 at
+  unit distance, each loop closer by the factor decay);
 * draft-row K/V for every depth follow the same model;
 * queries ~ N(0, 1) / sqrt(D) with softmax scale 1 (the 1/sqrt(D) folded in).
 
@@ -72,9 +75,11 @@ class PlaneModel:
     """
 
     def __init__(self, key: int, R: int, Hkv: int, D: int, decay: float, dtype: str,
-                 tail: Optional[dict] = None, tail_mult: float = 1.0):
+                 tail: Optional[dict] = None, tail_mult: float = 1.0, convention: str = "workload"):
         self.key, self.R, self.Hkv, self.D = key, R, Hkv, D
         self.decay, self.dtype = decay, dtype
+        self.convention = convention
+        self.noise_scale = noise_scale(decay, R, convention)
         self.tail = tail or {}
         self.tail_mult = tail_mult
 
@@ -95,7 +100,7 @@ class PlaneModel:
             lo, hi = max(j0, blk * BLOCK), min(j1, (blk + 1) * BLOCK)
             base = self._normal(kind, b, 0, blk)
             if p < self.R:
-                noise = self._normal(kind, b, p, blk) * self.decay ** (self.R - p)
+                noise = self._normal(kind, b, p, blk) * self.noise_scale(p)
                 if tail is not None:
                     pos = np.arange(blk * BLOCK, (blk + 1) * BLOCK)
                     mult = np.where(np.isin(pos, tail), self.tail_mult, 1.0)
@@ -150,14 +155,26 @@ def _uniform_lengths(rng, B, lo, hi):
     return rng.integers(lo, hi + 1, size=B).astype(np.int64)
 
 
-def _draft_kv(key, R, n_rows, Hkv, D, decay, dtype):
+def noise_scale(decay: float, R: int, convention: str = "workload"):
+    """Scale of plane p's difference from plane R (p < R): decay**(R - p)
+    ("workload": the plane next to the deepest differs most) or
+    decay**(p - 1) ("pages": the planes approach the deepest geometrically)."""
+    if convention == "workload":
+        return lambda p: decay ** (R - p)
+    if convention == "pages":
+        return lambda p: decay ** (p - 1)
+    raise ValueError(convention)
+
+
+def _draft_kv(key, R, n_rows, Hkv, D, decay, dtype, convention="workload"):
+    scale = noise_scale(decay, R, convention)
     rng = np.random.default_rng(np.random.SeedSequence(key, spawn_key=(3,)))
     base = rng.standard_normal((2, n_rows, Hkv, D))
     kv = np.empty((2, R, n_rows, Hkv, D))
     kv[:, R - 1] = round_to(base, dtype)
     for p in range(1, R):
         noise = rng.standard_normal((2, n_rows, Hkv, D))
-        kv[:, p - 1] = round_to(base + decay ** (R - p) * noise, dtype)
+        kv[:, p - 1] = round_to(base + scale(p) * noise, dtype)
     return kv
 
 
@@ -166,9 +183,10 @@ def make_case(name: str, layout: Optional[str] = None, *, B: Optional[int] = Non
               W: Optional[int] = None, R: Optional[int] = None, seed_offset: int = 0,
               dtype: Optional[str] = None, k: Optional[int] = None,
               Hkv: Optional[int] = None, Hq: Optional[int] = None,
-              D: Optional[int] = None) -> Case:
+              D: Optional[int] = None, convention: str = "workload") -> Case:
     """Build workload ``name`` (c1..c5).  Keyword overrides shrink a workload
-    for oracle-speed tests while keeping its structure."""
+    for oracle-speed tests while keeping its structure; ``convention`` picks
+    the direction of the plane decay (see noise_scale)."""
     idx = CONFIG_NAMES.index(name)
     key = ROOT_SEED + 1 + idx + 1000 * seed_offset
     rng = np.random.default_rng(np.random.SeedSequence(key, spawn_key=(1,)))
@@ -252,8 +270,9 @@ def make_case(name: str, layout: Optional[str] = None, *, B: Optional[int] = Non
         else:
             n_accept[:] = rng.integers(0, kk + 1, size=Bv)
         src_row[:] = [blk[0] for blk in blocks]
-    planes = PlaneModel(key, Rv, cfg["Hkv"], cfg["D"], cfg["decay"], cfg["dtype"], tail, tail_mult)
-    kv_new = _draft_kv(key, Rv, n_rows, cfg["Hkv"], cfg["D"], cfg["decay"], cfg["dtype"])
+    planes = PlaneModel(key, Rv, cfg["Hkv"], cfg["D"], cfg["decay"], cfg["dtype"], tail, tail_mult,
+                        convention)
+    kv_new = _draft_kv(key, Rv, n_rows, cfg["Hkv"], cfg["D"], cfg["decay"], cfg["dtype"], convention)
     qrng = np.random.default_rng(np.random.SeedSequence(key, spawn_key=(4,)))
     q = round_to(qrng.standard_normal((n_rows, cfg["Hq"], cfg["D"])) / np.sqrt(cfg["D"]),
                  cfg["dtype"])
