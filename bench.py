@@ -15,8 +15,9 @@ verified draft tokens per second, the roofline of the verify kernel
 events on the launch stream that bracket each step's verify calls, divided by
 the number of calls), and the float64 oracle timed on host cores on a bounded
 sample.  Unless --no-extra: the other workloads' figures, one step's verify
-calls captured into a HIP graph and replayed (graph_replay), and the accept
-call at the c4 shape (accept).
+calls captured into a HIP graph and replayed (graph_replay), the accept
+call at the c4 shape (accept), and the per-position substitution error on c2
+with its tail statistics under both plane-decay directions (side_stats).
 """
 from __future__ import annotations
 
@@ -418,6 +419,96 @@ def run_accept(calls: int = 50, warmup: int = 5, B: int = 16, k: int = 4, V: int
             "n_accept_histogram": np.bincount(outs[0].cpu().numpy(), minlength=k + 1).tolist()}
 
 
+def run_side_stats(reps: int = 20, warmup: int = 3, depths=(4, 16, 28)):
+    """Side statistics on c2 (one sequence, T = 1024, R = 32, Hq = Hkv = 40,
+    D = 128, bf16, k = 8 rows, 1% of the positions with 8x plane noise), under
+    both directions of the plane decay.  Per depth r: ripe_position_error on
+    the FULL cache (mean call time with HIP events on the launch stream, its
+    algorithmic bytes: the verify pass's K/V of plane r, then K/V of planes r
+    and R per (position, KV head), plus queries, outputs and error rows), the
+    tail statistics of its error row, and the exact squared output errors of
+    the DEEPEST and RIPE caches against the FULL fp32 output, beside the
+    squared error of rounding that output to bf16."""
+    import torch
+    import self_speculative_verify_ripe_amd as rp
+    from self_speculative_verify_ripe_amd.side_stats import tail_statistics
+    from workloads import make_case
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    res, nbytes, describe = {}, 0, ""
+    for conv in ("workload", "pages"):
+        case = make_case("c2", layout="full", convention=conv)
+        T, R, H, D, Hq = int(case.seq_len[0]), case.R, case.Hkv, case.D, case.Hq
+        describe = (f"c2 FULL/DEEPEST/RIPE: B=1, T={T}, R={R}, Hq/Hkv={Hq}/{H}, D={D}, bf16, k={case.n_rows}, "
+                    f"W={case.W}, {len(case.planes.tail[0])} tail positions with 8x plane noise")
+        rows = torch.zeros((2, R, T, H, D), dtype=torch.bfloat16, device=dev)
+        for p in sorted(set(depths) | {R}):
+            for kind in (0, 1):
+                v = case.planes.values(kind, 0, p, 0, T).astype(np.float32)
+                rows[kind, p - 1] = torch.from_numpy(v).to(dev).to(torch.bfloat16)
+        caches = {}
+        for lay in ("full", "deepest", "ripe"):
+            d = rp.make_desc(lay, "bf16", R, case.W, 1, case.t_max, H, D, Hq, max_rows=case.n_rows,
+                             max_groups=1)
+            c = torch.zeros(rp.ripe_layout_bytes(d), dtype=torch.uint8, device=dev)
+            rp.ripe_commit(d, c, np.zeros(1, np.int32), np.array([T], np.int32), np.zeros(1, np.int32), rows, T)
+            caches[lay] = (d, c, rp.new_workspace(d, dev))
+        del rows
+        q = torch.from_numpy(case.q.astype(np.float32)).to(dev).to(torch.bfloat16)
+        kv = torch.from_numpy(case.kv_new.astype(np.float32)).to(dev).to(torch.bfloat16)
+        dF, cF, _ = caches["full"]
+        err = torch.zeros((1, case.t_max), dtype=torch.float32, device=dev)
+        cond = torch.zeros_like(err)
+        o32 = torch.zeros((case.n_rows, Hq, D), dtype=torch.float32, device=dev)
+        lse = torch.zeros((case.n_rows, Hq), dtype=torch.float32, device=dev)
+        ws = torch.zeros(rp.ripe_layout_bytes(dF, rp.RIPE_BYTES_POSERR_WORKSPACE), dtype=torch.uint8, device=dev)
+        per_depth = {}
+        for r in depths:
+            groups = case.groups_at(r)
+            g4 = [(g.seq, g.depth, g.row_start, g.n_rows) for g in groups]
+            nbytes = (kv_read_bytes("full", R, case.W, case.seq_len, g4, H, D, 2)        # verify pass
+                      + case.n_rows * Hq * D * (2 + 4) + case.n_rows * Hq * 4
+                      + 4 * T * H * D * 2                                                 # planes r, R
+                      + case.n_rows * Hq * (D * (2 + 4) + 4) + 2 * case.t_max * 4)
+
+            def call():
+                rp.ripe_position_error(dF, cF, case.seq_len, groups, case.n_rows, case.scale, q, kv, err, cond,
+                                       o32, lse, ws, None, stream)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            st = tail_statistics(err[0].cpu().numpy(), T, case.W, cond=cond[0].cpu().numpy())
+            exact = {}
+            for lay in ("deepest", "ripe"):
+                d, c, wsv = caches[lay]
+                ob = torch.zeros((case.n_rows, Hq, D), dtype=torch.bfloat16, device=dev)
+                rp.ripe_verify_attn(d, c, case.seq_len, groups, case.n_rows, case.scale, q, kv, ob, None, None,
+                                    wsv, None, stream)
+                torch.cuda.synchronize()
+                exact[lay] = float(((ob.float() - o32) ** 2).sum())
+            floor = float(((o32.to(torch.bfloat16).float() - o32) ** 2).sum())
+            rnd = lambda x: None if x is None else (round(x, 6) if isinstance(x, float) else x)
+            per_depth[f"r={r}"] = {
+                "call_us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                **{k: rnd(v) for k, v in st.items() if k != "positions"},
+                "first_order_sq_err": float(err[0, :T].sum()),
+                "deepest_sq_err": exact["deepest"], "ripe_sq_err": exact["ripe"],
+                "bf16_rounding_sq_err": floor}
+        res[conv] = per_depth
+        del caches, ws
+        torch.cuda.empty_cache()
+    return {"workload": describe, "alg_bytes_per_call": nbytes, "by_convention": res}
+
+
 EXTRA_WORKLOADS = [("c2", "ripe"), ("c2", "full"), ("c2", "deepest"), ("c4", None),
                    ("c5-ripe", None), ("c5-full", None), ("c5-deepest", None)]
 
@@ -483,6 +574,7 @@ def main():
         result["by_workload"] = extra
     if not args.no_extra:
         result["accept"] = run_accept()
+        result["side_stats"] = run_side_stats()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(r["case"], r["layout"], args.cpu_seconds)
     line = json.dumps(result)

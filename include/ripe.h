@@ -66,7 +66,11 @@ typedef enum {
   RIPE_EHIP = -6           /* a HIP launch failed */
 } ripe_status_t;
 
-typedef enum { RIPE_BYTES_CACHE = 0, RIPE_BYTES_WORKSPACE = 1 } ripe_bytes_kind_t;
+typedef enum {
+  RIPE_BYTES_CACHE = 0,
+  RIPE_BYTES_WORKSPACE = 1,
+  RIPE_BYTES_POSERR_WORKSPACE = 2
+} ripe_bytes_kind_t;
 
 /*
  * One recurrent layer's cache (callers allocate one buffer per layer).
@@ -144,7 +148,9 @@ typedef struct ripe_group {
  *
  * kind = RIPE_BYTES_CACHE returns the cache size above; kind =
  * RIPE_BYTES_WORKSPACE returns a workspace size sufficient for any verify
- * call within the descriptor's max_rows / max_groups bounds.  Returns a
+ * call within the descriptor's max_rows / max_groups bounds; kind =
+ * RIPE_BYTES_POSERR_WORKSPACE one sufficient for any ripe_position_error
+ * call within them (with out_f32 and lse left to the library).  Returns a
  * negative ripe_status_t on an invalid descriptor or kind.
  */
 int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind);
@@ -324,6 +330,59 @@ ripe_status_t ripe_accept(const ripe_accept_desc_t* desc, const float* target_lo
                           const float* draft_logits, const int32_t* tokens, const uint8_t* has_fallback,
                           const uint32_t* rand, int32_t* n_accept, int32_t* branch, int32_t* next_token,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ripe_position_error -- side statistic: how much each committed prefix
+ * position contributes to the error of storing only the deepest plane.
+ *
+ * Source: RIPE abstract (zhuanzhiai.com paper page): whether the deepest
+ * plane alone suffices depends on how close the late planes are to it; on
+ * one model a small set of positions (1%) carries most of its error, and a
+ * window of recent positions at full depth removes most of those tail
+ * positions.  The pages name this error without defining it; here it is:
+ * for group g (sequence b, depth r, rows [row_start, row_start + n_rows)),
+ *
+ *   err[g][j] = sum over the group's rows and query heads of
+ *               || O^(j) - O ||^2,      j < T_b,
+ *
+ * O being the verify output over the FULL cache (every prefix position at
+ * plane r, the group's own rows at depth r, as ripe_verify_attn computes it)
+ * and O^(j) the same output with prefix position j alone read at plane R.
+ * It is computed from the single-term softmax update, in fp32.  Summed over
+ * j it is the first-order estimate of the DEEPEST output's squared error;
+ * the sum over j < T_b - W that of RIPE with window W.
+ *
+ * The update's sensitivity to the FULL output and LSE it starts from is
+ * kappa = a / (1 - a + c), a and c being position j's softmax weights at
+ * planes r and R in a row.  kappa <= 1 unless position j holds more than half
+ * of some row's attention at plane r; there the fp32 result has a relative
+ * error up to about kappa times that of the FULL output (1e-4 .. 1e-3 for
+ * bf16 caches) and is an estimate only.  cond reports kappa per position.
+ *
+ *  desc       a FULL descriptor (RIPE_EUNSUPPORTED otherwise); max_rows /
+ *             max_groups size RIPE_BYTES_POSERR_WORKSPACE.
+ *  cache ... kv_new   as for ripe_verify_attn (plane_sel is not produced).
+ *  err        device float [n_groups][t_max]; entries j >= T_b are set to 0.
+ *  cond       optional device float [n_groups][t_max]: kappa of each
+ *             position, the largest over the group's rows and heads (0 for
+ *             j >= T_b); NULL: not written.
+ *  out_f32    optional device float [n_rows][Hq][D]: receives the FULL
+ *             outputs in fp32 (rows no group covers are not written);
+ *             NULL: kept in the workspace.
+ *  lse        optional device float [n_rows][Hq]: their natural-log LSE.
+ *  workspace  device, 256-byte aligned; at least
+ *             ripe_layout_bytes(desc, RIPE_BYTES_POSERR_WORKSPACE) bytes
+ *             (RIPE_EWORKSPACE if smaller than the call needs).  Scratch
+ *             only; owned by the caller.
+ *
+ * Validation and errors as for ripe_verify_attn; err, cond and lse must be
+ * 4-byte aligned, out_f32 16-byte aligned.  Asynchronous on stream; launches kernels only.
+ */
+ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                  const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                                  float softmax_scale, const void* q, const void* kv_new, float* err,
+                                  float* cond, float* out_f32, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

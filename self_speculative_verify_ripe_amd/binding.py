@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("RIPE_LIB", os.path.join(_PKG, "libripe.so"))
 
 RIPE_LAYOUT_FULL, RIPE_LAYOUT_DEEPEST, RIPE_LAYOUT_RIPE = 0, 1, 2
 RIPE_F32, RIPE_BF16 = 0, 1
-RIPE_BYTES_CACHE, RIPE_BYTES_WORKSPACE = 0, 1
+RIPE_BYTES_CACHE, RIPE_BYTES_WORKSPACE, RIPE_BYTES_POSERR_WORKSPACE = 0, 1, 2
 STATUS = {0: "RIPE_OK", -1: "RIPE_EINVAL", -2: "RIPE_ERANGE", -3: "RIPE_ECAPACITY",
           -4: "RIPE_EUNSUPPORTED", -5: "RIPE_EWORKSPACE", -6: "RIPE_EHIP"}
 LAYOUTS = {"full": RIPE_LAYOUT_FULL, "deepest": RIPE_LAYOUT_DEEPEST, "ripe": RIPE_LAYOUT_RIPE}
@@ -76,6 +76,10 @@ def _load():
     lib.ripe_accept_workspace_bytes.restype = ctypes.c_int64
     lib.ripe_accept.argtypes = [ctypes.POINTER(ripe_accept_desc_t)] + [P] * 9 + [ctypes.c_size_t, P]
     lib.ripe_accept.restype = ctypes.c_int
+    lib.ripe_position_error.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_float, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ripe_position_error.restype = ctypes.c_int
     return lib
 
 
@@ -201,6 +205,26 @@ def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: I
         what = "ripe_verify_attn_inflight"
     if st != 0:
         raise RipeError(st, what)
+
+
+def ripe_position_error(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
+                        n_rows: int, softmax_scale: float, q, kv_new, err, cond=None, out_f32=None,
+                        lse=None, workspace=None, workspace_bytes: Optional[int] = None,
+                        stream=None) -> None:
+    """Per-position substitution error of a FULL cache (asynchronous on
+    ``stream``): err and cond [n_groups, t_max] float32 on the device."""
+    sl = _i32(seq_len, desc.batch)
+    if sl.size != desc.batch:
+        raise ValueError("seq_len must have one entry per sequence")
+    gptr, ng, _keep = _groups(groups)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ripe_position_error(ctypes.byref(desc), _ptr(cache), sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 gptr, ng, int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(err),
+                                 _ptr(cond), _ptr(out_f32), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                 _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_position_error")
 
 
 def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],

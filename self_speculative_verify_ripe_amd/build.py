@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libripe.so")
-SOURCES = ("api.hip", "verify.hip", "commit.hip", "accept.hip")
+SOURCES = ("api.hip", "verify.hip", "commit.hip", "accept.hip", "side_stats.hip")
 ARCH = os.environ.get("RIPE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -19,6 +19,7 @@
 #include "accept.h"
 #include "plan.h"
 #include "ripe.h"
+#include "side_stats.h"
 
 namespace ripe {
 hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
@@ -130,6 +131,19 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   return int64_t(bytes);
 }
 
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Buffers of ripe_position_error ahead of the verify workspace: the FULL
+// output (fp32) and its LSE unless the caller passes them, and the per-KV-head
+// sums and condition numbers.  -1 on overflow.
+int64_t poserr_extra(const ripe_desc_t& d, int64_t rows, int64_t groups, bool own_out, bool own_lse) {
+  const long double o = own_out ? (long double)rows * d.n_q_heads * d.head_dim * 4 : 0;
+  const long double l = own_lse ? (long double)rows * d.n_q_heads * 4 : 0;
+  const long double s = (long double)groups * d.n_kv_heads * d.t_max * 4;
+  if (o + l + 2 * s + 1024 > (long double)kMaxBytes) return -1;
+  return align256(int64_t(o)) + align256(int64_t(l)) + 2 * align256(int64_t(s));
+}
+
 struct LaunchPlan {
   VerifyParams p;
   ItemTable t;
@@ -191,6 +205,12 @@ extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
     const int64_t b = workspace_bound(*desc);
     return b < 0 ? int64_t(RIPE_EUNSUPPORTED) : b;
   }
+  if (kind == RIPE_BYTES_POSERR_WORKSPACE) {
+    const int64_t groups = std::max<int64_t>(desc->max_groups, 1);
+    const int64_t rows = std::max<int64_t>(desc->max_rows, groups);
+    const int64_t b = workspace_bound(*desc), x = poserr_extra(*desc, rows, groups, true, true);
+    return (b < 0 || x < 0 || b + x > kMaxBytes) ? int64_t(RIPE_EUNSUPPORTED) : b + x;
+  }
   return RIPE_EINVAL;
 }
 
@@ -199,7 +219,8 @@ extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
 static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
                           const ripe_group_t* groups, const int32_t* parents, int32_t n_groups, int32_t n_rows,
                           float softmax_scale, const void* q, const void* kv_new, void* out, float* lse,
-                          int8_t* plane_sel, void* workspace, size_t workspace_bytes, void* stream) {
+                          int8_t* plane_sel, void* workspace, size_t workspace_bytes, void* stream,
+                          bool out_f32 = false) {
   ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
@@ -225,6 +246,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.q = q;
     p.kv_new = kv_new;
     p.out = out;
+    p.out_f32 = out_f32 ? 1 : 0;
     p.lse = lse;
     p.plane_sel = plane_sel;
     p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
@@ -518,6 +540,76 @@ extern "C" ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, cons
   if (parents == nullptr && n_groups > 0) return RIPE_EINVAL;
   return verify_impl(desc, cache, seq_len, groups, parents, n_groups, n_rows, softmax_scale, q, kv_new, out, lse,
                      plane_sel, workspace, workspace_bytes, stream);
+}
+
+// Side statistic on a FULL cache: the FULL outputs at each group's depth
+// (a verify pass written in fp32), then the substitution error per prefix
+// position and KV head, then the sum over KV heads.
+extern "C" ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                             const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                                             float softmax_scale, const void* q, const void* kv_new, float* err,
+                                             float* cond, float* out_f32, float* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  const ripe_status_t st = check_desc(desc);
+  if (st != RIPE_OK) return st;
+  const ripe_desc_t& d = *desc;
+  if (d.layout != RIPE_LAYOUT_FULL) return RIPE_EUNSUPPORTED;
+  if (n_groups < 0) return RIPE_EINVAL;
+  if (n_groups == 0) return RIPE_OK;
+  if (err == nullptr || !aligned(err, 4) || (cond && !aligned(cond, 4)) || (out_f32 && !aligned(out_f32, 16)) ||
+      (lse && !aligned(lse, 4)))
+    return RIPE_EINVAL;
+  if (groups == nullptr || seq_len == nullptr || n_rows < 1) return RIPE_EINVAL;
+  if (workspace == nullptr) return RIPE_EWORKSPACE;
+  if (!aligned(workspace, 256)) return RIPE_EINVAL;
+  const int64_t extra = poserr_extra(d, n_rows, n_groups, out_f32 == nullptr, lse == nullptr);
+  if (extra < 0) return RIPE_EUNSUPPORTED;
+  if (size_t(extra) > workspace_bytes) return RIPE_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t ob = out_f32 ? 0 : align256(int64_t(n_rows) * d.n_q_heads * d.head_dim * 4);
+  const int64_t lb = lse ? 0 : align256(int64_t(n_rows) * d.n_q_heads * 4);
+  float* O = out_f32 ? out_f32 : reinterpret_cast<float*>(ws);
+  float* L = lse ? lse : reinterpret_cast<float*>(ws + ob);
+  const int64_t sb = align256(int64_t(n_groups) * d.n_kv_heads * d.t_max * 4);
+  float* part = reinterpret_cast<float*>(ws + ob + lb);
+  float* part_cond = reinterpret_cast<float*>(ws + ob + lb + sb);
+  // verify_impl validates the groups, lengths and pointers before launching
+  const ripe_status_t vs = verify_impl(desc, cache, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q,
+                                       kv_new, O, L, nullptr, ws + extra, workspace_bytes - size_t(extra), stream,
+                                       true);
+  if (vs != RIPE_OK) return vs;
+  PosErrParams p;
+  p.cache_k = cache;
+  p.cache_v = static_cast<const char*>(cache) + size_t(region_elems(d)) * elem_bytes(d.dtype);
+  p.q = q;
+  p.o = O;
+  p.lse = L;
+  p.part = part;
+  p.part_cond = part_cond;
+  p.err = err;
+  p.cond = cond;
+  p.R = d.R;
+  p.H = d.n_kv_heads;
+  p.Hq = d.n_q_heads;
+  p.G = d.n_q_heads / d.n_kv_heads;
+  p.t_max = d.t_max;
+  p.scale = softmax_scale;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (int g0 = 0; g0 < n_groups; g0 += kPeGroups) {
+    p.g0 = g0;
+    p.n_grp = std::min(kPeGroups, n_groups - g0);
+    for (int k = 0; k < p.n_grp; ++k) {
+      const ripe_group_t& g = groups[g0 + k];
+      p.grp[k].row_start = g.row_start;
+      p.grp[k].n_rows = g.n_rows;
+      p.grp[k].T = seq_len[g.seq];
+      p.grp[k].b = uint16_t(g.seq);
+      p.grp[k].depth = uint16_t(g.depth);
+    }
+    const ripe_status_t ls = hip_status(launch_position_error(p, d.dtype, d.head_dim, hs), "ripe_position_error");
+    if (ls != RIPE_OK) return ls;
+  }
+  return RIPE_OK;
 }
 
 extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,

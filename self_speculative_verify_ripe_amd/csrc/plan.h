@@ -178,6 +178,7 @@ struct VerifyParams {
   GroupRec grp[kMaxGroups];
   uint16_t gorig[kMaxGroups];  // index of each group in the caller's array
   int32_t inflight;      // some sequence of the launch has a parent block in flight
+  int32_t out_f32;       // out is fp32 (else the storage dtype)
 };
 
 struct CommitJob {     // rows of one sequence written to one region (20 bytes)

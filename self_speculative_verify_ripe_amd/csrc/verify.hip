@@ -694,7 +694,10 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
     float res[DPT];
 #pragma unroll
     for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
-    O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
+    if (p.out_f32)
+      Op<float>::store(static_cast<float*>(p.out) + orow * D + d0, res, DPT);
+    else
+      O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
     if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
   }
   // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0), slice 0

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_layout_bytes",
-                     "ripe_verify_attn", "ripe_verify_attn_inflight"]
+                     "ripe_position_error", "ripe_verify_attn", "ripe_verify_attn_inflight"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -252,3 +252,57 @@ def test_inflight_rejects(groups, parents, status):
 
 def test_inflight_no_groups_is_noop():
     assert call_inflight(np.zeros((0, 4), np.int32), None) == 0
+
+
+# ---------------------------------------------------------------------------
+# ripe_position_error: host checks (no HIP call on these paths)
+# ---------------------------------------------------------------------------
+def desc_full(**kw):
+    args = dict(max_rows=16, max_groups=4)
+    args.update(kw)
+    return rp.make_desc("full", "bf16", 4, 0, 2, 64, 2, 64, 4, **args)
+
+
+def call_poserr(desc=None, seq_len=(10, 20), groups=((0, 1, 0, 4), (1, 2, 4, 4)), n_rows=16, err=FAKE,
+                cond=None, out=None, lse=None, ws=FAKE, ws_bytes=1 << 40, q=FAKE):
+    desc = desc_full() if desc is None else desc
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    garr, ng, _keep = binding._groups(list(groups) if len(groups) else np.zeros((0, 4), np.int32))
+    return binding.lib.ripe_position_error(
+        ctypes.byref(desc), FAKE, sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), garr, ng, n_rows, 1.0,
+        q, FAKE, err, cond, out, lse, ws, ws_bytes, None)
+
+
+def test_position_error_workspace_bound():
+    d = desc_full()
+    verify = rp.ripe_layout_bytes(d, rp.RIPE_BYTES_WORKSPACE)
+    pe = rp.ripe_layout_bytes(d, rp.RIPE_BYTES_POSERR_WORKSPACE)
+    a = lambda x: (x + 255) // 256 * 256
+    # fp32 outputs + LSE of max_rows rows, per-KV-head sums and condition
+    # numbers of max_groups groups
+    assert pe == verify + a(16 * 4 * 64 * 4) + a(16 * 4 * 4) + 2 * a(4 * 2 * 64 * 4)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(desc=rp.make_desc("ripe", "bf16", 4, 8, 2, 64, 2, 64, 4, max_rows=16, max_groups=4)), -4),
+    (dict(desc=rp.make_desc("deepest", "bf16", 4, 0, 2, 64, 2, 64, 4, max_rows=16, max_groups=4)), -4),
+    (dict(err=0), -1),
+    (dict(err=FAKE + 2), -1),
+    (dict(cond=FAKE + 2), -1),
+    (dict(out=FAKE + 4), -1),
+    (dict(lse=FAKE + 2), -1),
+    (dict(ws=0, ws_bytes=0), -5),
+    (dict(ws=FAKE + 16), -1),
+    (dict(ws_bytes=1024), -5),           # smaller than the fp32 outputs alone
+    (dict(seq_len=(10, 65)), -2),        # checked by the verify pass before any launch
+    (dict(groups=((0, 5, 0, 4),)), -2),
+    (dict(groups=((0, 1, 0, 4), (1, 2, 2, 4))), -1),
+    (dict(q=0), -1),
+    (dict(n_rows=0), -1),
+])
+def test_position_error_rejects(case, status):
+    assert call_poserr(**case) == status
+
+
+def test_position_error_no_groups_is_noop():
+    assert call_poserr(groups=()) == 0

@@ -1,0 +1,35 @@
+"""Host-side summary of the substitution-error rows (package side_stats):
+hand-worked arrays."""
+import numpy as np
+
+from self_speculative_verify_ripe_amd.side_stats import tail_statistics
+
+
+def test_hand_worked_row():
+    # 200 positions: two large errors (at 10 and 190), the rest 1.0
+    e = np.ones(200)
+    e[10], e[190] = 99.0, 101.0
+    s = tail_statistics(e, 200, 20)
+    assert s["tail_positions"] == 2
+    assert np.isclose(s["tail_share"], 200.0 / 398.0)
+    assert s["tail_in_window"] == 0.5                 # 190 is in [180, 200), 10 is not
+    assert np.isclose(s["window_share"], (19 + 101) / 398.0)
+    assert s["ill_conditioned"] is None
+
+
+def test_condition_counts_and_padding_ignored():
+    e = np.array([4.0, 1.0, 3.0, 2.0, 77.0, 77.0])    # entries past T are ignored
+    cond = np.array([0.2, 3.0, 0.5, 1.5, 9.0, 9.0])
+    s = tail_statistics(e, 4, 1, cond=cond, tail_frac=0.5)
+    assert s["tail_positions"] == 2 and np.isclose(s["tail_share"], 0.7)
+    assert s["tail_in_window"] == 0.0                 # positions 0 and 2; the window is {3}
+    assert s["ill_conditioned"] == 2 and np.isclose(s["ill_conditioned_share"], 0.3)
+
+
+def test_ties_and_degenerate_rows():
+    s = tail_statistics(np.full(150, 2.0), 150, 50)
+    assert s["tail_positions"] == 1 and s["tail_in_window"] == 0.0   # the lowest of equal values
+    z = tail_statistics(np.zeros(64), 64, 8)
+    assert z["tail_share"] is None and z["window_share"] is None
+    empty = tail_statistics(np.zeros(0), 0, 8)
+    assert empty["tail_positions"] == 0 and empty["tail_in_window"] is None
