@@ -25,7 +25,7 @@
 // and each thread keeps a 1/8 slice of one position's four rows in
 // registers.  The group's query columns and their FULL outputs are staged
 // 16 at a time and read back by broadcast; the two dot products per column
-// are reduced over the position's 8 lanes.  A second kernel sums the KV
+// are reduced over the position's 8 lanes with DPP moves.  A second kernel sums the KV
 // heads in a fixed order.  The work is a streaming read of 4 rows per
 // (position, KV head): bound by HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -40,14 +40,42 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPeThreads = 256;
 constexpr int kParts = kPeThreads / kPeTile;  // threads per position
+static_assert(kParts == 8, "the lane reductions below combine 8 consecutive lanes");
+
+// DPP lane moves (VALU, no LDS round trip).  quad_perm(a,b,c,d) encodes
+// a | b << 2 | c << 4 | d << 6; row_half_mirror (0x141) reverses each group of
+// 8 lanes.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+constexpr int kHalfMirror = 0x141;
+template <int L>
+constexpr int kQuadBcast = L | (L << 2) | (L << 4) | (L << 6);
+
+// Sum over each aligned group of 8 lanes, the same bits in all 8: after the
+// two quad steps every lane of a quad holds the quad's sum, and the mirror
+// brings in the other quad's (a + b = b + a, so both quads agree).
+__device__ inline float sum8(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  return x + dpp<kHalfMirror>(x);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErrParams p) {
   constexpr int E = sizeof(T);
   constexpr int VE = 16 / E;         // elements per 16-byte chunk
   constexpr int DP = D / kParts;     // head-dim slice per thread
-  constexpr int RS = D + VE;         // LDS row stride (one chunk of padding)
-  __shared__ __align__(16) T skv[4][kPeTile][RS];  // k_r, k_R, v_r, v_R, position-major
+  constexpr int RSK = D + VE;        // K rows: one 16-byte chunk of padding
+  // V rows: D + 2 elements, so that a transposing store's 4 (bf16) or 8
+  // (fp32) position rows start 8 banks apart and its head dimensions fill
+  // the rest: 2-way bank conflicts at most, against 8 to 16 with 16-byte rows
+  constexpr int RSV = D + 2;
+  __shared__ __align__(16) T sk[2][kPeTile][RSK];  // k_r, k_R, position-major
+  __shared__ __align__(16) T sv[2][kPeTile][RSV];  // v_r, v_R, position-major
   __shared__ float sq[kPeCols][D];
   __shared__ float so[kPeCols][D];
   __shared__ float sl[kPeCols];
@@ -59,32 +87,79 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
   if (j0 >= grp.T) return;  // whole work-group
 
   // ---- stage the tile: rows j0 .. j0 + 31 (in the allocation: t_max is a
-  // multiple of 32 and j0 < T <= t_max) --------------------------------------
+  // multiple of 32 and j0 < T <= t_max), and the first chunk of query
+  // columns.  Every global load is issued before the first LDS store, so the
+  // work-group waits for memory once.
   const int tid = threadIdx.x;
+  constexpr int NC = D * E / 128;  // 16-byte chunks per thread per array (32 x D elements)
+  constexpr int CR = D / VE;       // K: chunks per row
+  constexpr int CD = 32 / VE;      // V: chunks per head dimension
+  u32x4 buf[4][NC];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int plane = (a & 1) ? p.R : grp.depth;
     const size_t head = (size_t(grp.b) * p.R + (plane - 1)) * p.H + h;
-    if (a < 2) {  // K [t][D]: row-major, copied as is
-      const T* src = static_cast<const T*>(p.cache_k) + (head * p.t_max + j0) * D;
-      constexpr int CR = D / VE;  // chunks per row
-      for (int c = tid; c < kPeTile * CR; c += kPeThreads) {
-        const int row = c / CR, cc = c % CR;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(row) * D + cc * VE);
-        *reinterpret_cast<u32x4*>(&skv[a][row][cc * VE]) = v;
-      }
-    } else {  // V [D][32] per block: transposed into [t][D]
-      const T* src = static_cast<const T*>(p.cache_v) + (head * (p.t_max / 32) + j0 / 32) * size_t(D) * 32;
-      constexpr int CD = 32 / VE;  // chunks per head dimension
-      for (int c = tid; c < D * CD; c += kPeThreads) {
-        const int d = c / CD, t0 = (c % CD) * VE;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(d) * 32 + t0);
-        const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-        for (int x = 0; x < VE; ++x) skv[a][t0 + x][d] = e[x];
+    for (int c = 0; c < NC; ++c) {
+      const int idx = tid + c * kPeThreads;
+      if (a < 2) {  // K [t][D]: row-major
+        const T* src = static_cast<const T*>(p.cache_k) + (head * p.t_max + j0) * D;
+        buf[a][c] = *reinterpret_cast<const u32x4*>(src + size_t(idx / CR) * D + (idx % CR) * VE);
+      } else {      // V [D][32] per block
+        const T* src = static_cast<const T*>(p.cache_v) + (head * (p.t_max / 32) + j0 / 32) * size_t(D) * 32;
+        buf[a][c] = *reinterpret_cast<const u32x4*>(src + size_t(idx / CD) * 32 + (idx % CD) * VE);
       }
     }
   }
+  const int nq = grp.n_rows * p.G;
+  constexpr int QN = kPeCols * D / kPeThreads;  // staged query values per thread
+  // Column loads are unconditional (columns past nq read column nq - 1, in
+  // range since nq >= 1) and zeroed when stored, so that no load waits for
+  // the one before it.
+  T qv[QN];
+  float ov[QN], lv;
+  auto col_index = [&](int col) {
+    col = min(col, nq - 1);
+    return size_t(grp.row_start + col / p.G) * p.Hq + size_t(h) * p.G + col % p.G;
+  };
+  int c_loaded = 0;
+  auto load_cols = [&](int c0) {
+    c_loaded = c0;
+#pragma unroll
+    for (int x = 0; x < QN; ++x) {
+      const int idx = tid + x * kPeThreads;
+      const size_t qi = col_index(c0 + idx / D) * D + idx % D;
+      qv[x] = static_cast<const T*>(p.q)[qi];
+      ov[x] = p.o[qi];
+    }
+    lv = p.lse[col_index(c0 + (tid % kPeCols))];
+  };
+  auto store_cols = [&]() {
+#pragma unroll
+    for (int x = 0; x < QN; ++x) {
+      const int idx = tid + x * kPeThreads;
+      const bool ok = c_loaded + idx / D < nq;
+      sq[idx / D][idx % D] = ok ? static_cast<float>(qv[x]) : 0.f;
+      so[idx / D][idx % D] = ok ? ov[x] : 0.f;
+    }
+    if (tid < kPeCols) sl[tid] = c_loaded + tid < nq ? lv : 0.f;
+  };
+  load_cols(0);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = tid + c * kPeThreads;
+      if (a < 2) {
+        *reinterpret_cast<u32x4*>(&sk[a][idx / CR][(idx % CR) * VE]) = buf[a][c];
+      } else {  // transposed into [t][D]
+        const T* e = reinterpret_cast<const T*>(&buf[a][c]);
+        const int d = idx / CD, t0 = (idx % CD) * VE;
+#pragma unroll
+        for (int x = 0; x < VE; ++x) sv[a - 2][t0 + x][d] = e[x];
+      }
+    }
+  store_cols();
   __syncthreads();
 
   const int jl = tid / kParts, part = tid % kParts;
@@ -93,36 +168,23 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
   float kr[DP], dk[DP], dv[DP], vR[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    kr[e] = static_cast<float>(skv[0][jl][d0 + e]);
-    dk[e] = static_cast<float>(skv[1][jl][d0 + e]) - kr[e];
-    const float vr = static_cast<float>(skv[2][jl][d0 + e]);
-    vR[e] = static_cast<float>(skv[3][jl][d0 + e]);
+    kr[e] = static_cast<float>(sk[0][jl][d0 + e]);
+    dk[e] = static_cast<float>(sk[1][jl][d0 + e]) - kr[e];
+    const float vr = static_cast<float>(sv[0][jl][d0 + e]);
+    vR[e] = static_cast<float>(sv[1][jl][d0 + e]);
     dv[e] = vR[e] - vr;
   }
 
   // ---- query columns (row i, head h*G + x) in chunks of kPeCols ------------
-  const int nq = grp.n_rows * p.G;
   float acc = 0.f;
   float kappa = 0.f;
   for (int c0 = 0; c0 < nq; c0 += kPeCols) {
-    __syncthreads();  // the previous chunk's readers are done
-    for (int idx = tid; idx < kPeCols * D; idx += kPeThreads) {
-      const int cl = idx / D, dd = idx % D;
-      const int col = c0 + cl;
-      float qv = 0.f, ov = 0.f;
-      if (col < nq) {
-        const size_t qi = (size_t(grp.row_start + col / p.G) * p.Hq + size_t(h) * p.G + col % p.G) * D + dd;
-        qv = static_cast<float>(static_cast<const T*>(p.q)[qi]);
-        ov = p.o[qi];
-      }
-      sq[cl][dd] = qv;
-      so[cl][dd] = ov;
+    if (c0 > 0) {
+      load_cols(c0);
+      __syncthreads();  // the previous chunk's readers are done
+      store_cols();
+      __syncthreads();
     }
-    if (tid < kPeCols) {
-      const int col = c0 + tid;
-      sl[tid] = col < nq ? p.lse[size_t(grp.row_start + col / p.G) * p.Hq + size_t(h) * p.G + col % p.G] : 0.f;
-    }
-    __syncthreads();
     const int nc = min(kPeCols, nq - c0);
     for (int cl = 0; cl < nc; ++cl) {
       float s = 0.f, ds = 0.f;
@@ -132,11 +194,8 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
         s = fmaf(qe, kr[e], s);
         ds = fmaf(qe, dk[e], ds);
       }
-#pragma unroll
-      for (int m = 1; m < kParts; m <<= 1) {
-        s += __shfl_xor(s, m);
-        ds += __shfl_xor(ds, m);
-      }
+      s = sum8(s);
+      ds = sum8(ds);
       const float a = expf(p.scale * s - sl[cl]);
       const float g = a * expm1f(p.scale * ds);
       float sum = 0.f;
@@ -150,8 +209,7 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
       kappa = fmaxf(kappa, a * inv);
     }
   }
-#pragma unroll
-  for (int m = 1; m < kParts; m <<= 1) acc += __shfl_xor(acc, m);
+  acc = sum8(acc);
   if (part == 0 && j < grp.T) {
     const size_t at = (size_t(p.g0 + gl) * p.H + h) * p.t_max + j;
     p.part[at] = acc;
@@ -159,22 +217,36 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
   }
 }
 
-// e[g][j] = sum over KV heads in order, cond[g][j] = their largest kappa
-// (both 0 for j >= T).
+// e[g][j] = sum over KV heads, cond[g][j] = their largest kappa (both 0 for
+// j >= T).  64 positions per work-group, four lanes per position: lane s
+// sums heads s, s + 4, ... in order, then the four sums are added in lane
+// order (a fixed order: the result does not depend on the launch).
+constexpr int kSumPos = 64;
 __global__ __launch_bounds__(256) void position_error_sum_kernel(const PosErrParams p) {
   const int gl = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= p.t_max) return;
+  const int j = blockIdx.x * kSumPos + (threadIdx.x >> 2);
+  const int s = threadIdx.x & 3;
   const int g = p.g0 + gl;
   const int T = p.grp[gl].T;
-  float s = 0.f, k = 0.f;
-  if (j < T)
-    for (int h = 0; h < p.H; ++h) {
-      s += p.part[(size_t(g) * p.H + h) * p.t_max + j];
-      k = fmaxf(k, p.part_cond[(size_t(g) * p.H + h) * p.t_max + j]);
+  float e = 0.f, k = 0.f;
+  if (j < T) {
+    const float* pe = p.part + size_t(g) * p.H * p.t_max + j;
+    const float* pk = p.part_cond + size_t(g) * p.H * p.t_max + j;
+#pragma unroll 4
+    for (int h = s; h < p.H; h += 4) {
+      e += pe[size_t(h) * p.t_max];
+      k = fmaxf(k, pk[size_t(h) * p.t_max]);
     }
-  p.err[size_t(g) * p.t_max + j] = s;
-  if (p.cond != nullptr) p.cond[size_t(g) * p.t_max + j] = k;
+  }
+  // the position's four lanes form one DPP quad: broadcast each lane's value
+  const float e0 = dpp<kQuadBcast<0>>(e), e1 = dpp<kQuadBcast<1>>(e), e2 = dpp<kQuadBcast<2>>(e),
+              e3 = dpp<kQuadBcast<3>>(e);
+  const float k0 = dpp<kQuadBcast<0>>(k), k1 = dpp<kQuadBcast<1>>(k), k2 = dpp<kQuadBcast<2>>(k),
+              k3 = dpp<kQuadBcast<3>>(k);
+  if (s == 0 && j < p.t_max) {
+    p.err[size_t(g) * p.t_max + j] = ((e0 + e1) + e2) + e3;
+    if (p.cond != nullptr) p.cond[size_t(g) * p.t_max + j] = fmaxf(fmaxf(k0, k1), fmaxf(k2, k3));
+  }
 }
 
 template <typename T, int D>
@@ -184,7 +256,7 @@ hipError_t launch_t(const PosErrParams& p, hipStream_t stream) {
                                  dim3(p.t_max / kPeTile, p.H, p.n_grp), dim3(kPeThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&position_error_sum_kernel),
-                         dim3((p.t_max + 255) / 256, p.n_grp), dim3(256), args, 0, stream);
+                         dim3((p.t_max + kSumPos - 1) / kSumPos, p.n_grp), dim3(256), args, 0, stream);
 }
 
 }  // namespace
