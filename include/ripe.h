@@ -95,6 +95,12 @@ typedef enum {
  *              on that sequence's own groups and length, never on the other
  *              sequences of the call, so a group's results are bit-identical
  *              whether it is verified alone or batched.
+ *  page_len    0: one contiguous region per sequence (the layouts below).
+ *              Otherwise positions per page of a paged cache, a positive
+ *              multiple of 32 dividing t_max: the positions of every
+ *              sequence live in pages of a shared pool, found through a
+ *              block table (see "Paged caches" below).
+ *  n_pages     pages in the pool (page_len > 0), >= 1; ignored otherwise.
  */
 typedef struct ripe_desc {
   int32_t layout;
@@ -109,6 +115,8 @@ typedef struct ripe_desc {
   int32_t max_rows;
   int32_t max_groups;
   int32_t split_len;
+  int32_t page_len;
+  int32_t n_pages;
 } ripe_desc_t;
 
 /*
@@ -145,6 +153,23 @@ typedef struct ripe_group {
  *   RIPE    2*B*Hkv*D*E * (T + We*(R-1))
  * bytes: one plane plus W*(R-1) window slots per sequence (RIPE abstract,
  * memory statement).
+ *
+ * Paged caches (page_len = P > 0; the block table of a call maps block k of
+ * sequence b, positions [kP, kP + P), to a page of the pool).  The main
+ * region (FULL: every plane; DEEPEST and RIPE: the deep plane) becomes a pool
+ * of N = n_pages pages, with the same order inside a page:
+ *
+ *   FULL     K [N][R][Hkv][P][D]            V [N][R][Hkv][P/32][D][32]
+ *   DEEPEST  K [N][Hkv][P][D]               V [N][Hkv][P/32][D][32]
+ *   RIPE     K pool [N][Hkv][P][D]          V pool [N][Hkv][P/32][D][32]
+ *            then the ring exactly as above, one per sequence
+ *
+ * (K pool, K ring, V pool, V ring), costing 2*Hkv*D*E*(N*P*planes +
+ * B*We*(R-1)) bytes.  Sequences may share pages, e.g. two LoopSpec branches
+ * forked from one confirmed prefix: they read the shared pages and each
+ * keeps its own window ring; a commit must not write a page slot that
+ * another sequence of the same call writes.  With P = t_max and block 0 of
+ * sequence b on page b, the bytes equal those of the unpaged layout.
  *
  * kind = RIPE_BYTES_CACHE returns the cache size above; kind =
  * RIPE_BYTES_WORKSPACE returns a workspace size sufficient for any verify
@@ -248,6 +273,35 @@ ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cac
 ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,
                           const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
                           int32_t n_rows, void* stream);
+
+/*
+ * Paged caches (desc->page_len > 0; the calls above return RIPE_EINVAL for
+ * such a descriptor, these two RIPE_EINVAL for an unpaged one).  They do what
+ * ripe_verify_attn_inflight (parents may be NULL: no parent in flight) and
+ * ripe_commit do, reading and writing position j of sequence b in page
+ * block_table[b * (t_max / page_len) + j / page_len] at slot j mod page_len.
+ *
+ *  block_table  host int32 [batch][t_max / page_len].  Verify reads the
+ *               entries of blocks holding positions < T_b of every sequence
+ *               with groups; commit those of the blocks it writes.  Such an
+ *               entry outside [0, n_pages) is RIPE_ERANGE; other entries are
+ *               not read.
+ *
+ * Verify cuts prefix pieces at page boundaries (one page per split-K work
+ * item), so pages shorter than the split length add work items; results
+ * equal the unpaged call's when the cut points coincide (e.g. P = t_max).
+ * A commit in which two sequences write one (page, slot) is RIPE_EINVAL.
+ * The RIPE ring is per sequence and unpaged.
+ */
+ripe_status_t ripe_verify_attn_paged(const ripe_desc_t* desc, const void* cache, const int32_t* block_table,
+                                     const int32_t* seq_len, const ripe_group_t* groups, const int32_t* parents,
+                                     int32_t n_groups, int32_t n_rows, float softmax_scale, const void* q,
+                                     const void* kv_new, void* out, float* lse, int8_t* plane_sel,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+ripe_status_t ripe_commit_paged(const ripe_desc_t* desc, void* cache, const int32_t* block_table,
+                                int32_t* seq_len, const int32_t* n_accept, const int32_t* src_row,
+                                const void* kv_new, int32_t n_rows, void* stream);
 
 /*
  * Accept / rollback after verification (LoopSpec summary, rit.work blog,

@@ -17,6 +17,13 @@ V is stored transposed in blocks of 32 positions (each head dimension's 32
 values contiguous).  Plane p is stored at index p - 1 (plane R deepest);
 RIPE keeps position j's planes 1..R-1 in ring slot j mod We.
 
+Paged caches (page length P, N pages): the main region becomes a pool,
+K [N][planes][Hkv][P][D] and V [N][planes][Hkv][P/32][D][32] (planes = R for
+FULL, the plane index dropped otherwise), and block k of sequence b
+(positions [kP, kP + P)) lives in page table[b][k]; the RIPE ring stays one
+per sequence.  encode_paged builds it by moving each block of the unpaged
+encoding to its page.
+
 The memory model follows the RIPE abstract (zhuanzhiai.com paper page):
 one shared plane costs T positions per sequence, the full cache R*T, RIPE
 T + W*(R-1).
@@ -171,3 +178,114 @@ def decode(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: i
                     cache.put(b, p, j, val(kring[b, p - 1, :, s]),
                               val(vring[b, p - 1, :, s // BW, :, s % BW]))
     return cache
+
+
+def paged_layout_elements(layout, R: int, W: int, B: int, t_max: int, Hkv: int, D: int, page_len: int,
+                          n_pages: int) -> int:
+    """Elements (K and V together) of a paged cache."""
+    layout = layout_code(layout)
+    planes = R if layout == FULL else 1
+    ring = B * ring_width(W, t_max) * (R - 1) if layout == RIPE else 0
+    return 2 * Hkv * D * (n_pages * page_len * planes + ring)
+
+
+def _pool_views(elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, Hkv: int, D: int, P: int, N: int):
+    """K/V views of a paged buffer: pools [N, planes, H, P, D] and
+    [N, planes, H, P/32, D, 32] (planes = 1 unless FULL), rings as unpaged."""
+    layout = layout_code(layout)
+    planes = R if layout == FULL else 1
+    We = ring_width(W, t_max) if layout == RIPE else 0
+    pool = (N, planes, Hkv, P, D)
+    ring = (B, R - 1, Hkv, We, D)
+    n_pool, n_ring = int(np.prod(pool)), (int(np.prod(ring)) if We > 0 else 0)
+    views, off = {}, 0
+    for kind in ("K", "V"):
+        views[(kind, "pool")] = elems[off:off + n_pool].reshape(pool) if kind == "K" else \
+            elems[off:off + n_pool].reshape(N, planes, Hkv, P // 32, D, 32)
+        off += n_pool
+        if We > 0:
+            flat = elems[off:off + n_ring]
+            views[(kind, "ring")] = flat.reshape(ring) if kind == "K" else \
+                flat.reshape(B, R - 1, Hkv, We // min(32, We), D, min(32, We))
+            off += n_ring
+    assert off == elems.size
+    return views
+
+
+def encode_paged(cache: LogicalCache, table, page_len: int, n_pages: int) -> np.ndarray:
+    """Bytes of the paged layout: the unpaged encoding's main-region block k
+    of sequence b moved to page table[b][k] (negative entries: block not
+    stored), the ring unchanged.  Two blocks mapped to one page must agree
+    wherever both hold a value (ValueError otherwise); page slots no block
+    holds are quiet NaNs."""
+    B, R, T, H, D, P, N = cache.B, cache.R, cache.t_max, cache.Hkv, cache.D, page_len, n_pages
+    if P <= 0 or T % P or P % 32:
+        raise ValueError("page length")
+    table = np.asarray(table).reshape(B, T // P)
+    flat = encode(cache).view(np.uint32 if cache.dtype == "f32" else np.uint16)
+    src = _region_views(flat, cache.layout, R, cache.W, B, T, H, D)
+    n = paged_layout_elements(cache.layout, R, cache.W, B, T, H, D, P, N)
+    nan = 0x7FC00000 if cache.dtype == "f32" else 0x7FC0
+    out = np.full(n, nan, dtype=flat.dtype)
+    dst = _pool_views(out, cache.layout, R, cache.W, B, T, H, D, P, N)
+    written = np.zeros((N, R if cache.layout == FULL else 1, P), dtype=bool)
+    main_planes = list(range(1, R + 1)) if cache.layout == FULL else [R]
+    for b in range(B):
+        for k in range(T // P):
+            pg = int(table[b, k])
+            if pg < 0:
+                continue
+            if pg >= N:
+                raise ValueError("page out of range")
+            for pi, p in enumerate(main_planes):
+                if (b, p) not in cache._dense:
+                    continue
+                held = cache._dense[(b, p)][2][k * P:(k + 1) * P]
+                ks = src[("K", "main")][b, p - 1] if cache.layout == FULL else src[("K", "main")][b]
+                vs = src[("V", "main")][b, p - 1] if cache.layout == FULL else src[("V", "main")][b]
+                kblk = ks[:, k * P:(k + 1) * P]                        # [H, P, D]
+                vblk = vs[:, k * P // 32:(k + 1) * P // 32]            # [H, P/32, D, 32]
+                kd, vd = dst[("K", "pool")][pg, pi], dst[("V", "pool")][pg, pi]
+                both = held & written[pg, pi]
+                vmask = held.reshape(P // 32, 32)
+                if both.any():
+                    bv = both.reshape(P // 32, 32)
+                    if not (np.array_equal(kd[:, both], kblk[:, both]) and
+                            np.array_equal(np.where(bv[None, :, None, :], vd, 0),
+                                           np.where(bv[None, :, None, :], vblk, 0))):
+                        raise ValueError(f"page {pg} shared with different contents")
+                kd[:, held] = kblk[:, held]
+                vd[...] = np.where(vmask[None, :, None, :], vblk, vd)
+                written[pg, pi] |= held
+    if ("K", "ring") in src:
+        dst[("K", "ring")][...] = src[("K", "ring")]
+        dst[("V", "ring")][...] = src[("V", "ring")]
+    return out.view(np.uint8)
+
+
+def decode_paged(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: int, Hkv: int, D: int,
+                 seq_len, table, page_len: int, n_pages: int) -> LogicalCache:
+    """Inverse of encode_paged for the committed positions: the blocks are
+    gathered back to the unpaged layout, which decode reads."""
+    P, N, T = page_len, n_pages, t_max
+    table = np.asarray(table).reshape(B, T // P)
+    elems = np.ascontiguousarray(buf, dtype=np.uint8).view(np.uint32 if dtype == "f32" else np.uint16)
+    src = _pool_views(elems, layout, R, W, B, T, Hkv, D, P, N)
+    flat = np.full(layout_elements(layout, R, W, B, T, Hkv, D), 0x7FC00000 if dtype == "f32" else 0x7FC0,
+                   dtype=elems.dtype)
+    dst = _region_views(flat, layout, R, W, B, T, Hkv, D)
+    full = layout_code(layout) == FULL
+    for b in range(B):
+        for k in range(T // P):
+            if k * P >= int(seq_len[b]):
+                break
+            pg = int(table[b, k])
+            for pi in range(R if full else 1):
+                kd = dst[("K", "main")][b, pi] if full else dst[("K", "main")][b]
+                vd = dst[("V", "main")][b, pi] if full else dst[("V", "main")][b]
+                kd[:, k * P:(k + 1) * P] = src[("K", "pool")][pg, pi]
+                vd[:, k * P // 32:(k + 1) * P // 32] = src[("V", "pool")][pg, pi]
+    if ("K", "ring") in src:
+        dst[("K", "ring")][...] = src[("K", "ring")]
+        dst[("V", "ring")][...] = src[("V", "ring")]
+    return decode(flat.view(np.uint8), layout, dtype, R, W, B, T, Hkv, D, seq_len)

@@ -34,7 +34,7 @@ class RipeError(RuntimeError):
 class ripe_desc_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "layout", "dtype", "R", "W", "batch", "t_max", "n_kv_heads", "head_dim", "n_q_heads",
-        "max_rows", "max_groups", "split_len")]
+        "max_rows", "max_groups", "split_len", "page_len", "n_pages")]
 
 
 class ripe_group_t(ctypes.Structure):
@@ -80,6 +80,14 @@ def _load():
                                         ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ripe_position_error.restype = ctypes.c_int
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    lib.ripe_verify_attn_paged.argtypes = [ctypes.POINTER(ripe_desc_t), P, I32P, I32P,
+                                           ctypes.POINTER(ripe_group_t), I32P, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ripe_verify_attn_paged.restype = ctypes.c_int
+    lib.ripe_commit_paged.argtypes = [ctypes.POINTER(ripe_desc_t), P, I32P, I32P, I32P, I32P, P,
+                                      ctypes.c_int32, P]
+    lib.ripe_commit_paged.restype = ctypes.c_int
     return lib
 
 
@@ -87,11 +95,21 @@ lib = _load()
 
 
 def make_desc(layout, dtype, R, W, batch, t_max, n_kv_heads, head_dim, n_q_heads,
-              max_rows=0, max_groups=0, split_len=0) -> ripe_desc_t:
+              max_rows=0, max_groups=0, split_len=0, page_len=0, n_pages=0) -> ripe_desc_t:
     layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     return ripe_desc_t(layout, dtype, R, W, batch, t_max, n_kv_heads, head_dim, n_q_heads,
-                       max_rows, max_groups, split_len)
+                       max_rows, max_groups, split_len, page_len, n_pages)
+
+
+def _table(desc: ripe_desc_t, block_table) -> np.ndarray:
+    """A block table as a C-contiguous int32 array [batch, t_max / page_len]."""
+    if desc.page_len <= 0:
+        raise ValueError("block_table given for an unpaged descriptor")
+    tab = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    if tab.size != desc.batch * (desc.t_max // desc.page_len):
+        raise ValueError("block_table must have batch * (t_max / page_len) entries")
+    return tab
 
 
 def _ptr(x) -> Optional[int]:
@@ -170,10 +188,11 @@ def pack_parents(groups: Iterable) -> np.ndarray:
 def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
                      n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
                      workspace=None, workspace_bytes: Optional[int] = None, stream=None,
-                     parents=None) -> None:
+                     parents=None, block_table=None) -> None:
     """Launch verification attention (asynchronous on ``stream``).  Groups
     with an in-flight parent block (``parents`` [n, 2], or groups carrying
-    parent_row_start / parent_rows) go through ripe_verify_attn_inflight."""
+    parent_row_start / parent_rows) go through ripe_verify_attn_inflight;
+    a paged cache (``block_table``) through ripe_verify_attn_paged."""
     sl = seq_len if (isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32
                      and seq_len.flags["C_CONTIGUOUS"]) else _i32(seq_len, desc.batch)
     if sl.size != desc.batch:
@@ -185,7 +204,20 @@ def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: I
         parents = pack_parents(groups)
         if not parents.any():
             parents = None
-    if parents is None:
+    if block_table is not None:
+        tab = _table(desc, block_table)
+        par = None if parents is None else np.ascontiguousarray(parents, dtype=np.int32).reshape(-1, 2)
+        if par is not None and par.shape[0] != ng:
+            raise ValueError("parents must have one (row_start, n_rows) pair per group")
+        I32P = ctypes.POINTER(ctypes.c_int32)
+        st = lib.ripe_verify_attn_paged(ctypes.byref(desc), _ptr(cache), tab.ctypes.data_as(I32P),
+                                        sl.ctypes.data_as(I32P), gptr,
+                                        None if par is None else par.ctypes.data_as(I32P), ng,
+                                        int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
+                                        _ptr(lse), _ptr(plane_sel), _ptr(workspace), int(workspace_bytes),
+                                        _stream(stream))
+        what = "ripe_verify_attn_paged"
+    elif parents is None:
         st = lib.ripe_verify_attn(ctypes.byref(desc), _ptr(cache),
                                   sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr, ng,
                                   int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
@@ -228,21 +260,28 @@ def ripe_position_error(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups
 
 
 def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],
-                src_row: Sequence[int], kv_new, n_rows: int, stream=None) -> np.ndarray:
+                src_row: Sequence[int], kv_new, n_rows: int, stream=None, block_table=None) -> np.ndarray:
     """Commit accepted rows; returns the updated committed lengths (an int32
-    array; ``seq_len`` is updated in place when it is an int32 NumPy array)."""
+    array; ``seq_len`` is updated in place when it is an int32 NumPy array).
+    A paged cache takes its ``block_table`` (ripe_commit_paged)."""
     inplace = isinstance(seq_len, np.ndarray) and seq_len.dtype == np.int32 and \
         seq_len.flags["C_CONTIGUOUS"]
     sl = seq_len if inplace else _i32(seq_len, desc.batch).copy()
     na = _i32(n_accept, desc.batch)
     sr = _i32(src_row, desc.batch)
-    st = lib.ripe_commit(ctypes.byref(desc), _ptr(cache),
-                         sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                         na.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                         sr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(kv_new),
-                         int(n_rows), _stream(stream))
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    if block_table is not None:
+        tab = _table(desc, block_table)
+        st = lib.ripe_commit_paged(ctypes.byref(desc), _ptr(cache), tab.ctypes.data_as(I32P),
+                                   sl.ctypes.data_as(I32P), na.ctypes.data_as(I32P), sr.ctypes.data_as(I32P),
+                                   _ptr(kv_new), int(n_rows), _stream(stream))
+        what = "ripe_commit_paged"
+    else:
+        st = lib.ripe_commit(ctypes.byref(desc), _ptr(cache), sl.ctypes.data_as(I32P), na.ctypes.data_as(I32P),
+                             sr.ctypes.data_as(I32P), _ptr(kv_new), int(n_rows), _stream(stream))
+        what = "ripe_commit"
     if st != 0:
-        raise RipeError(st, "ripe_commit")
+        raise RipeError(st, what)
     return sl
 
 

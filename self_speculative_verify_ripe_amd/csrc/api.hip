@@ -80,13 +80,23 @@ inline int piece_len(int len, int S) {
   return ((len + n - 1) / n + kStep - 1) / kStep * kStep;
 }
 
+// Positions of the main region (FULL: per plane; otherwise the deep plane):
+// t_max per sequence, or the page pool of a paged cache.
+long double main_positions(const ripe_desc_t& d) {
+  return d.page_len > 0 ? (long double)d.n_pages * d.page_len : (long double)d.batch * d.t_max;
+}
+
+// Elements from a region's start to its RIPE ring.
+uint64_t ring_offset(const ripe_desc_t& d) {
+  return uint64_t(main_positions(d)) * uint64_t(d.n_kv_heads) * uint64_t(d.head_dim);
+}
+
 // Elements of one region (K or V) of the cache, or -1 on overflow.
 int64_t region_elems(const ripe_desc_t& d) {
-  const long double per_seq =
-      d.layout == RIPE_LAYOUT_FULL ? (long double)d.R * d.t_max
-      : d.layout == RIPE_LAYOUT_DEEPEST ? (long double)d.t_max
-                                        : (long double)d.t_max + (long double)ring_width(d) * (d.R - 1);
-  const long double n = per_seq * d.batch * d.n_kv_heads * d.head_dim;
+  const long double main = main_positions(d) * (d.layout == RIPE_LAYOUT_FULL ? d.R : 1);
+  const long double ring =
+      d.layout == RIPE_LAYOUT_RIPE ? (long double)d.batch * ring_width(d) * (d.R - 1) : 0.0L;
+  const long double n = (main + ring) * d.n_kv_heads * d.head_dim;
   if (n * 2 * elem_bytes(d.dtype) > (long double)kMaxBytes) return -1;
   return int64_t(n);
 }
@@ -96,12 +106,15 @@ ripe_status_t check_desc(const ripe_desc_t* d) {
   if (d->layout < RIPE_LAYOUT_FULL || d->layout > RIPE_LAYOUT_RIPE) return RIPE_EINVAL;
   if (d->dtype != RIPE_F32 && d->dtype != RIPE_BF16) return RIPE_EINVAL;
   if (d->R < 1 || d->W < 0 || d->batch < 1 || d->t_max < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
-      d->n_q_heads < 1 || d->max_rows < 0 || d->max_groups < 0 || d->split_len < 0)
+      d->n_q_heads < 1 || d->max_rows < 0 || d->max_groups < 0 || d->split_len < 0 || d->page_len < 0 ||
+      d->n_pages < 0)
     return RIPE_EINVAL;
+  if (d->page_len > 0 && d->n_pages < 1) return RIPE_EINVAL;
   if (d->n_q_heads % d->n_kv_heads != 0) return RIPE_EINVAL;
   if (d->R > 127 || d->batch > 65535) return RIPE_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return RIPE_EUNSUPPORTED;
   if (d->t_max % 32 != 0 || d->split_len % 32 != 0) return RIPE_EUNSUPPORTED;
+  if (d->page_len > 0 && (d->page_len % 32 != 0 || d->t_max % d->page_len != 0)) return RIPE_EUNSUPPORTED;
   if (d->n_q_heads / d->n_kv_heads > 65535) return RIPE_EUNSUPPORTED;
   const int We = ring_width(*d);
   if (!(We == 0 || (We < 32 && We % 8 == 0) || We % 32 == 0)) return RIPE_EUNSUPPORTED;
@@ -119,7 +132,8 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   const int64_t groups = std::max<int64_t>(d.max_groups, 1);
   const int64_t rows = std::max<int64_t>(d.max_rows, groups);
   const int64_t nseq = std::min<int64_t>(d.batch, groups);
-  const int64_t tpieces = (int64_t(d.t_max) + S - 1) / S;
+  // a paged cache also cuts prefix pieces at page boundaries
+  const int64_t tpieces = (int64_t(d.t_max) + S - 1) / S + (d.page_len > 0 ? d.t_max / d.page_len : 0);
   int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tpieces;
   if (d.layout == RIPE_LAYOUT_RIPE) per_seq += std::min<int64_t>(groups, d.R - 1) * ((We + S - 1) / S);
   per_seq += groups + (rows + S - 1) / S;  // draft rows
@@ -188,6 +202,8 @@ struct VerifyScratch {
   std::vector<int32_t> key_seq;
   std::vector<ripe_group_t> key_groups;
   std::vector<int32_t> key_parents;  // empty: no parents
+  std::vector<int32_t> key_table;    // paged caches: the block table
+  std::vector<int32_t> piece_page;   // per piece of a sequence: its pool page (-1: none)
 };
 
 VerifyScratch& verify_scratch() {
@@ -214,9 +230,11 @@ extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
   return RIPE_EINVAL;
 }
 
-// Both verify entry points.  parents: host [n_groups][2] (row_start, n_rows)
-// of each group's in-flight parent block, or nullptr for none.
-static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+// Every verify entry point.  parents: host [n_groups][2] (row_start, n_rows)
+// of each group's in-flight parent block, or nullptr for none.  table: the
+// block table of a paged cache (nullptr for an unpaged one).
+static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, const int32_t* table,
+                          const int32_t* seq_len,
                           const ripe_group_t* groups, const int32_t* parents, int32_t n_groups, int32_t n_rows,
                           float softmax_scale, const void* q, const void* kv_new, void* out, float* lse,
                           int8_t* plane_sel, void* workspace, size_t workspace_bytes, void* stream,
@@ -224,6 +242,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
   ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
+  if ((d.page_len > 0) != (table != nullptr)) return RIPE_EINVAL;
   if (n_groups < 0) return RIPE_EINVAL;
   if (n_groups == 0) return RIPE_OK;
   if (groups == nullptr || seq_len == nullptr || n_rows < 1) return RIPE_EINVAL;
@@ -269,7 +288,9 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       std::memcmp(sc.key_groups.data(), groups, sizeof(ripe_group_t) * size_t(n_groups)) == 0 &&
       (parents == nullptr ? sc.key_parents.empty()
                           : sc.key_parents.size() == 2 * size_t(n_groups) &&
-                                std::memcmp(sc.key_parents.data(), parents, sizeof(int32_t) * 2 * size_t(n_groups)) == 0))
+                                std::memcmp(sc.key_parents.data(), parents, sizeof(int32_t) * 2 * size_t(n_groups)) == 0) &&
+      (table == nullptr ||
+       std::memcmp(sc.key_table.data(), table, sizeof(int32_t) * sc.key_table.size()) == 0))
     return launch_all(sc.key_NB);
   sc.have_key = false;
   sc.spans.clear();
@@ -291,6 +312,13 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       if (kp < 0) return RIPE_EINVAL;
       if (kp > 0 && (ps < 0 || int64_t(ps) + kp > n_rows)) return RIPE_ERANGE;
       if (kp > 65535) return RIPE_EUNSUPPORTED;
+    }
+  const int nblk = d.page_len > 0 ? d.t_max / d.page_len : 0;  // block-table row length
+  if (table != nullptr)
+    for (int i = 0; i < n_groups; ++i) {  // the pages holding the prefix of every sequence read
+      const int b = groups[i].seq;
+      for (int k = 0; k * d.page_len < seq_len[b]; ++k)
+        if (table[b * nblk + k] < 0 || table[b * nblk + k] >= d.n_pages) return RIPE_ERANGE;
     }
 
   // groups of each sequence in the caller's order (counting sort by sequence)
@@ -322,7 +350,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     if (sc.plans.size() <= size_t(sc.n_plans)) sc.plans.emplace_back();
     LaunchPlan& lp = sc.plans[sc.n_plans++];
     VerifyParams& p = lp.p;
-    p.ring_off = uint64_t(d.batch) * d.n_kv_heads * uint64_t(d.t_max) * D;
+    p.ring_off = ring_offset(d);
+    p.page_len = d.page_len;
     p.layout = d.layout;
     p.R = d.R;
     p.We = We;
@@ -370,13 +399,23 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     }
     const InFlight fl = in_flight(d.layout, We, T, kp);
     // pieces of this sequence: every segment cut into near-equal runs of at
-    // most S positions
+    // most S positions; in a paged cache, prefix-plane runs are also cut at
+    // page boundaries and remember their page
     sc.pieces.clear();
+    sc.piece_page.clear();
     enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, kp, [&](const Seg& sg) {
       const int pl = piece_len(sg.len, S);
-      for (int c0 = 0; c0 < sg.len; c0 += pl)
-        sc.pieces.push_back(Piece{c0, std::min(pl, sg.len - c0), uint8_t(sg.kind), uint8_t(sg.depth),
-                                  uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
+      for (int c0 = 0; c0 < sg.len; c0 += pl) {
+        const int c1 = std::min(c0 + pl, sg.len);
+        const bool paged = table != nullptr && sg.kind == kSegPlane;
+        for (int a = c0; a < c1;) {
+          const int e = paged ? std::min(c1, (a / d.page_len + 1) * d.page_len) : c1;
+          sc.pieces.push_back(Piece{a, e - a, uint8_t(sg.kind), uint8_t(sg.depth),
+                                    uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
+          sc.piece_page.push_back(paged ? table[b * nblk + a / d.page_len] : -1);
+          a = e;
+        }
+      }
       return false;
     });
     const int n_piece = int(sc.pieces.size());
@@ -421,6 +460,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
         Piece pc = sc.pieces[k];
         pc.s = uint8_t(p.n_seq);
         if (pc.kind == kSegDraft) pc.gidx = uint8_t(sr.g_begin + pc.gidx);
+        cur->t.page[p.n_pieces] = sc.piece_page[k];
         cur->t.piece[p.n_pieces++] = pc;
       }
       // items of unit (h, cc): one per piece; partial slot = part0 + unit *
@@ -518,6 +558,10 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     sc.key_parents.assign(parents, parents + 2 * size_t(n_groups));
   else
     sc.key_parents.clear();
+  if (table != nullptr)
+    sc.key_table.assign(table, table + size_t(d.batch) * nblk);
+  else
+    sc.key_table.clear();
   sc.have_key = true;
   return launch_all(NB);
 }
@@ -527,8 +571,8 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
                                           float softmax_scale, const void* q, const void* kv_new, void* out,
                                           float* lse, int8_t* plane_sel, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  return verify_impl(desc, cache, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q, kv_new, out, lse,
-                     plane_sel, workspace, workspace_bytes, stream);
+  return verify_impl(desc, cache, nullptr, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q, kv_new,
+                     out, lse, plane_sel, workspace, workspace_bytes, stream);
 }
 
 extern "C" ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cache,
@@ -538,8 +582,19 @@ extern "C" ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, cons
                                                    void* out, float* lse, int8_t* plane_sel, void* workspace,
                                                    size_t workspace_bytes, void* stream) {
   if (parents == nullptr && n_groups > 0) return RIPE_EINVAL;
-  return verify_impl(desc, cache, seq_len, groups, parents, n_groups, n_rows, softmax_scale, q, kv_new, out, lse,
-                     plane_sel, workspace, workspace_bytes, stream);
+  return verify_impl(desc, cache, nullptr, seq_len, groups, parents, n_groups, n_rows, softmax_scale, q, kv_new,
+                     out, lse, plane_sel, workspace, workspace_bytes, stream);
+}
+
+extern "C" ripe_status_t ripe_verify_attn_paged(const ripe_desc_t* desc, const void* cache, const int32_t* block_table,
+                                                const int32_t* seq_len, const ripe_group_t* groups,
+                                                const int32_t* parents, int32_t n_groups, int32_t n_rows,
+                                                float softmax_scale, const void* q, const void* kv_new, void* out,
+                                                float* lse, int8_t* plane_sel, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  if (block_table == nullptr) return RIPE_EINVAL;
+  return verify_impl(desc, cache, block_table, seq_len, groups, parents, n_groups, n_rows, softmax_scale, q,
+                     kv_new, out, lse, plane_sel, workspace, workspace_bytes, stream);
 }
 
 // Side statistic on a FULL cache: the FULL outputs at each group's depth
@@ -553,7 +608,7 @@ extern "C" ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void
   const ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
-  if (d.layout != RIPE_LAYOUT_FULL) return RIPE_EUNSUPPORTED;
+  if (d.layout != RIPE_LAYOUT_FULL || d.page_len > 0) return RIPE_EUNSUPPORTED;
   if (n_groups < 0) return RIPE_EINVAL;
   if (n_groups == 0) return RIPE_OK;
   if (err == nullptr || !aligned(err, 4) || (cond && !aligned(cond, 4)) || (out_f32 && !aligned(out_f32, 16)) ||
@@ -574,7 +629,7 @@ extern "C" ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void
   float* part = reinterpret_cast<float*>(ws + ob + lb);
   float* part_cond = reinterpret_cast<float*>(ws + ob + lb + sb);
   // verify_impl validates the groups, lengths and pointers before launching
-  const ripe_status_t vs = verify_impl(desc, cache, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q,
+  const ripe_status_t vs = verify_impl(desc, cache, nullptr, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q,
                                        kv_new, O, L, nullptr, ws + extra, workspace_bytes - size_t(extra), stream,
                                        true);
   if (vs != RIPE_OK) return vs;
@@ -612,12 +667,15 @@ extern "C" ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void
   return RIPE_OK;
 }
 
-extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,
-                                     const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
-                                     int32_t n_rows, void* stream) {
+// Both commit entry points (table: the block table of a paged cache, or
+// nullptr).
+static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int32_t* table, int32_t* seq_len,
+                                 const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
+                                 int32_t n_rows, void* stream) {
   ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
+  if ((d.page_len > 0) != (table != nullptr)) return RIPE_EINVAL;
   if (seq_len == nullptr || n_accept == nullptr || src_row == nullptr || n_rows < 0) return RIPE_EINVAL;
   bool any = false;
   for (int b = 0; b < d.batch; ++b) {
@@ -631,6 +689,29 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
   }
   if (!any) return RIPE_OK;
   if (cache == nullptr || kv_new == nullptr || !aligned(cache, 16) || !aligned(kv_new, 16)) return RIPE_EINVAL;
+  const int P = d.page_len;
+  const int nblk = P > 0 ? d.t_max / P : 0;
+  if (table != nullptr) {
+    // the pages written must exist, and no (page, slot) may be written twice
+    struct Span {
+      int page, lo, hi;
+    };
+    std::vector<Span> spans;
+    for (int b = 0; b < d.batch; ++b) {
+      const int n = n_accept[b];
+      if (n == 0) continue;
+      const int T = seq_len[b];
+      for (int k = T / P; k * P < T + n; ++k) {
+        const int pg = table[b * nblk + k];
+        if (pg < 0 || pg >= d.n_pages) return RIPE_ERANGE;
+        spans.push_back(Span{pg, std::max(T, k * P) - k * P, std::min(T + n, (k + 1) * P) - k * P});
+      }
+    }
+    std::sort(spans.begin(), spans.end(),
+              [](const Span& x, const Span& y) { return x.page != y.page ? x.page < y.page : x.lo < y.lo; });
+    for (size_t i = 1; i < spans.size(); ++i)
+      if (spans[i].page == spans[i - 1].page && spans[i].lo < spans[i - 1].hi) return RIPE_EINVAL;
+  }
 
   const int D = d.head_dim;
   const int We = ring_width(d);
@@ -639,16 +720,26 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
   const int64_t per_row_plane = int64_t(d.n_kv_heads) * (D / 8);  // items per (row, plane)
 
   struct Job {
-    int b, j0, src0, n, plane_lo, n_planes;
+    int b, j0, src0, n, plane_lo, n_planes, page;
   };
   std::vector<Job> jobs;
-  auto add = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes) {
+  auto add_cut = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes, int page) {
     // cut rows so that no job exceeds the per-launch item budget
     const int64_t per_row = per_row_plane * n_planes;
     const int max_rows = int(std::max<int64_t>(1, kMaxCommitItems / per_row));
     for (int r0 = 0; r0 < n; r0 += max_rows) {
       const int cnt = std::min(max_rows, n - r0);
-      jobs.push_back(Job{b, j0 + r0, src0 + r0, cnt, plane_lo, n_planes});
+      jobs.push_back(Job{b, j0 + r0, src0 + r0, cnt, plane_lo, n_planes, page});
+    }
+  };
+  // main-region rows of a paged cache: one job per page touched
+  auto add = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes) {
+    const bool main_region = !(d.layout == RIPE_LAYOUT_RIPE && plane_lo < d.R);
+    if (table == nullptr || !main_region) return add_cut(b, j0, src0, n, plane_lo, n_planes, 0);
+    for (int a = j0; a < j0 + n;) {
+      const int e = std::min(j0 + n, (a / P + 1) * P);
+      add_cut(b, a, src0 + (a - j0), e - a, plane_lo, n_planes, table[b * nblk + a / P]);
+      a = e;
     }
   };
   for (int b = 0; b < d.batch; ++b) {
@@ -674,7 +765,8 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
     p.cache_k = cache;
     p.cache_v = static_cast<char*>(cache) + size_t(reg) * E;
     p.kv_new = kv_new;
-    p.ring_off = uint64_t(d.batch) * d.n_kv_heads * uint64_t(d.t_max) * D;
+    p.ring_off = ring_offset(d);
+    p.page_len = P;
     p.layout = d.layout;
     p.R = d.R;
     p.We = We;
@@ -696,6 +788,7 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
       cj.b = uint16_t(jb.b);
       cj.plane_lo = uint8_t(jb.plane_lo);
       cj.n_planes = uint8_t(jb.n_planes);
+      cj.page = jb.page;
       items += cnt;
     }
     p.n_jobs = nj;
@@ -707,6 +800,19 @@ extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32
     if (hip_status(launch_commit(p, d.dtype, D, hs), "ripe_commit") != RIPE_OK) return RIPE_EHIP;
   for (int b = 0; b < d.batch; ++b) seq_len[b] += n_accept[b];
   return RIPE_OK;
+}
+
+extern "C" ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len,
+                                     const int32_t* n_accept, const int32_t* src_row, const void* kv_new,
+                                     int32_t n_rows, void* stream) {
+  return commit_impl(desc, cache, nullptr, seq_len, n_accept, src_row, kv_new, n_rows, stream);
+}
+
+extern "C" ripe_status_t ripe_commit_paged(const ripe_desc_t* desc, void* cache, const int32_t* block_table,
+                                           int32_t* seq_len, const int32_t* n_accept, const int32_t* src_row,
+                                           const void* kv_new, int32_t n_rows, void* stream) {
+  if (block_table == nullptr) return RIPE_EINVAL;
+  return commit_impl(desc, cache, block_table, seq_len, n_accept, src_row, kv_new, n_rows, stream);
 }
 
 extern "C" int64_t ripe_accept_workspace_bytes(const ripe_accept_desc_t* desc) {

@@ -11,7 +11,8 @@
 //
 // One thread copies 8 consecutive head-dim elements of one (row, plane,
 // head): a 16- or 32-byte K row piece, and 8 V elements into the transposed
-// 32-position V blocks.  Destinations (position, plane, head, element) are
+// 32-position V blocks.  Paged caches: the host cuts jobs at page boundaries
+// and gives each main-region job its page.  Destinations (position, plane, head, element) are
 // distinct across threads, so the writes never race.
 #include <hip/hip_runtime.h>
 
@@ -55,6 +56,11 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
     off = p.ring_off + ((size_t(jb.b) * (p.R - 1) + (pl - 1)) * p.H + h) * size_t(p.We) * D;
     slot = j % p.We;
     bw = p.BW;
+  } else if (p.page_len > 0) {  // paged main region: the job's rows share one page
+    off = (((p.layout == 0) ? size_t(jb.page) * p.R + (pl - 1) : size_t(jb.page)) * p.H + h) *
+          size_t(p.page_len) * D;
+    slot = j % p.page_len;
+    bw = 32;
   } else if (p.layout == 0) {
     off = ((size_t(jb.b) * p.R + (pl - 1)) * p.H + h) * size_t(p.t_max) * D;
     slot = j;

@@ -140,6 +140,7 @@ struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];
   uint16_t wg[kMaxItems];
+  int32_t page[kMaxPieces];  // paged caches: the pool page of each prefix-plane piece
 };
 
 // (sequence, KV head, column chunk) of each merge work-group (8 bytes).
@@ -179,9 +180,10 @@ struct VerifyParams {
   uint16_t gorig[kMaxGroups];  // index of each group in the caller's array
   int32_t inflight;      // some sequence of the launch has a parent block in flight
   int32_t out_f32;       // out is fp32 (else the storage dtype)
+  int32_t page_len;      // paged cache: positions per page (0: unpaged)
 };
 
-struct CommitJob {     // rows of one sequence written to one region (20 bytes)
+struct CommitJob {     // rows of one sequence written to one region (24 bytes)
   int32_t item0;       // first work item
   int32_t j0;          // destination position of the job's first row
   int32_t src0;        // kv_new row of the job's first row
@@ -189,6 +191,7 @@ struct CommitJob {     // rows of one sequence written to one region (20 bytes)
   uint16_t b;
   uint8_t plane_lo;    // first plane written (1-based)
   uint8_t n_planes;
+  int32_t page;        // paged cache, main region: the page holding all the job's rows
 };
 
 struct CommitParams {
@@ -197,6 +200,7 @@ struct CommitParams {
   const void* kv_new;
   uint64_t ring_off;
   int32_t layout, R, We, BW, t_max, H, n_rows, n_jobs, n_items;
+  int32_t page_len;         // paged cache: positions per page (0: unpaged)
   CommitJob job[kMaxJobs];  // a RIPE job with plane_lo < R writes the ring
 };
 

@@ -402,15 +402,20 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     size_t off;
     int bw = kStep;
     if (pc.kind == kSegPlane) {
-      if (p.layout == 0)
-        off = ((size_t(sr.b) * p.R + (pc.depth - 1)) * p.H + h) * size_t(p.t_max) * D;
-      else
-        off = (size_t(sr.b) * p.H + h) * size_t(p.t_max) * D;
+      if (p.page_len > 0) {  // paged: the piece lies inside one page of the pool
+        const size_t page = size_t(tab.page[it.piece]);
+        off = (((p.layout == 0) ? page * p.R + (pc.depth - 1) : page) * p.H + h) * size_t(p.page_len) * D +
+              size_t(pc.c0 % p.page_len) * D;
+      } else {
+        off = (((p.layout == 0) ? size_t(sr.b) * p.R + (pc.depth - 1) : size_t(sr.b)) * p.H + h) *
+                  size_t(p.t_max) * D +
+              size_t(pc.c0) * D;
+      }
     } else {
-      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D;
+      off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D +
+            size_t(pc.c0) * D;  // c0 is a multiple of 32, and of the ring's block width
       bw = p.BW;
     }
-    off += size_t(pc.c0) * D;  // c0 is a multiple of 32, and of the ring's block width
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.cache_k) + off, uint32_t(pc.len) * D * E);
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(static_cast<const T*>(p.cache_v) + off, uint32_t(ceil_div(pc.len, bw)) * bw * D * E);

@@ -27,15 +27,16 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_layout_bytes",
-                     "ripe_position_error", "ripe_verify_attn", "ripe_verify_attn_inflight"]
+    assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_commit_paged",
+                     "ripe_layout_bytes", "ripe_position_error", "ripe_verify_attn", "ripe_verify_attn_inflight",
+                     "ripe_verify_attn_paged"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(rp.ripe_desc_t) == 12 * 4
+    assert ctypes.sizeof(rp.ripe_desc_t) == 14 * 4
     assert ctypes.sizeof(rp.ripe_group_t) == 16
     assert ctypes.sizeof(rp.ripe_accept_desc_t) == 16
 
@@ -306,3 +307,76 @@ def test_position_error_rejects(case, status):
 
 def test_position_error_no_groups_is_noop():
     assert call_poserr(groups=()) == 0
+
+
+# ---------------------------------------------------------------------------
+# paged caches: descriptor, size, host checks (no HIP call on these paths)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N", [(32, 5), (64, 40), (1024, 3)])
+def test_paged_cache_bytes_closed_form(layout, dtype, P, N):
+    d = rp.make_desc(layout, dtype, 32, 64, 4, 1024, 8, 128, 32, page_len=P, n_pages=N)
+    want = oracle_layout.paged_layout_elements(layout, 32, 64, 4, 1024, 8, 128, P, N) * (4 if dtype == "f32" else 2)
+    assert rp.ripe_layout_bytes(d) == want
+
+
+@pytest.mark.parametrize("P,N,status", [(48, 4, -4), (128, 4, -4), (-32, 4, -1), (32, 0, -1), (32, -1, -1)])
+def test_paged_bad_descriptor(P, N, status):
+    d = rp.make_desc("ripe", "bf16", 4, 8, 2, 192, 2, 64, 4, page_len=P, n_pages=N)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) == status
+
+
+def paged_desc():
+    return rp.make_desc("ripe", "bf16", 4, 8, 2, 64, 2, 64, 4, max_rows=16, max_groups=4, page_len=32, n_pages=4)
+
+
+def call_verify_paged(desc, table, seq_len=(10, 40), groups=((0, 1, 0, 4), (1, 2, 4, 4))):
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    garr, ng, _keep = binding._groups(list(groups))
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    tab = None if table is None else np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    return binding.lib.ripe_verify_attn_paged(
+        ctypes.byref(desc), FAKE, None if tab is None else tab.ctypes.data_as(I32P), sl.ctypes.data_as(I32P),
+        garr, None, ng, 16, 1.0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+
+
+@pytest.mark.parametrize("table,seq_len,status", [
+    (None, (10, 40), -1),                       # table missing
+    ([[0, -1], [1, 4]], (10, 40), -2),          # page 4 of 4 read by sequence 1 (positions 32..39)
+    ([[-1, 9], [1, 2]], (10, 40), -2),          # sequence 0's first block unmapped
+])
+def test_paged_verify_rejects(table, seq_len, status):
+    assert call_verify_paged(paged_desc(), table, seq_len) == status
+
+
+def test_paged_entry_points_need_matching_descriptor():
+    assert call_verify_paged(desc2(), [[0, 1], [2, 3]]) == -1           # unpaged descriptor
+    assert call_verify(paged_desc(), [10, 20], [(0, 1, 0, 4)]) == -1      # paged descriptor, no table
+    d = rp.make_desc("full", "bf16", 4, 0, 2, 64, 2, 64, 4, max_rows=16, max_groups=4, page_len=32, n_pages=4)
+    assert call_poserr(desc=d) == -4
+
+
+def call_commit_paged(table, seq_len=(10, 40), n_accept=(4, 4), src_row=(0, 4)):
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    sl = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int32))
+    na = np.ascontiguousarray(np.asarray(n_accept, dtype=np.int32))
+    sr = np.ascontiguousarray(np.asarray(src_row, dtype=np.int32))
+    tab = np.ascontiguousarray(np.asarray(table, dtype=np.int32))
+    st = binding.lib.ripe_commit_paged(ctypes.byref(paged_desc()), FAKE, tab.ctypes.data_as(I32P),
+                                       sl.ctypes.data_as(I32P), na.ctypes.data_as(I32P), sr.ctypes.data_as(I32P),
+                                       FAKE, 16, None)
+    return st, sl
+
+
+@pytest.mark.parametrize("table,seq_len,n_accept,status", [
+    ([[0, 1], [2, 9]], (10, 40), (4, 4), -2),       # sequence 1 writes block 1: page 9 of 4
+    ([[0, 1], [0, 3]], (10, 8), (4, 4), -1),        # both write page 0, slots 10..13 and 8..11
+    # sequence 0 writes positions 30..33 (page 0 slots 30, 31; page 1 slots 0, 1),
+    # sequence 1 positions 32..35 (its block 1: page 1 slots 0..3)
+    ([[0, 1], [2, 1]], (30, 32), (4, 4), -1),
+])
+def test_paged_commit_rejects(table, seq_len, n_accept, status):
+    st, sl = call_commit_paged(table, seq_len, n_accept)
+    assert st == status
+    assert list(sl) == list(seq_len)  # untouched on error
