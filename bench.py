@@ -44,6 +44,8 @@ def parse():
                                                        "c5-deepest"])
     ap.add_argument("--layout", default=None, help="override the workload's layout")
     ap.add_argument("--split-len", type=int, default=0)
+    ap.add_argument("--page-len", type=int, default=0,
+                    help="paged cache with pages of this many positions, in a seeded random pool order")
     ap.add_argument("--layers", type=int, default=None, help="recurrent layers (default: workload's)")
     ap.add_argument("--depths", default="workload",
                     help="'workload' (the workload's depths), 'all' or a comma list")
@@ -175,7 +177,7 @@ def counted_traffic(workload: str):
 
 
 def run_workload(name, layout_override, steps, warmup, split_len, layers, depths_arg,
-                 copy_calibration_mib=0, graph=False):
+                 copy_calibration_mib=0, graph=False, page_len=0):
     import torch
     import self_speculative_verify_ripe_amd as rp
     from workloads import device_kv_rows
@@ -189,6 +191,14 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     k = case.blocks[0][1]
     growth = (steps + warmup) * int(case.n_accept.max())
     t_max = int(-(-(int(case.seq_len.max()) + growth + case.n_rows) // 32) * 32)
+    table, n_pages = None, 0
+    if page_len:
+        # every block of every sequence gets its own page, placed in a seeded
+        # random order over the pool
+        t_max = -(-t_max // page_len) * page_len
+        nb = t_max // page_len
+        n_pages = B * nb
+        table = np.random.default_rng(7).permutation(n_pages).astype(np.int32).reshape(B, nb)
     if depths_arg == "all":
         depths = list(range(1, R + 1))
     elif depths_arg in (None, "workload"):
@@ -203,7 +213,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     packed_sets = [rp.pack_groups(gs) for gs in group_sets]
     n_rows = case.n_rows
     desc = rp.make_desc(layout, case.dtype, R, W, B, t_max, Hkv, D, Hq, max_rows=n_rows,
-                        max_groups=2 * B, split_len=split_len)
+                        max_groups=2 * B, split_len=split_len, page_len=page_len, n_pages=n_pages)
     cache_bytes = rp.ripe_layout_bytes(desc)
     ws_bytes = rp.ripe_layout_bytes(desc, rp.RIPE_BYTES_WORKSPACE)
     stream = torch.cuda.current_stream()
@@ -223,7 +233,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
                                   planes=need)
             na = np.zeros(B, dtype=np.int32)
             na[b] = T
-            rp.ripe_commit(desc, cache, sl, na, np.zeros(B, dtype=np.int32), rows, T)
+            rp.ripe_commit(desc, cache, sl, na, np.zeros(B, dtype=np.int32), rows, T, block_table=table)
             del rows
         caches.append(cache)
     seq_len0 = case.seq_len.astype(np.int32).copy()
@@ -260,13 +270,13 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
             gs = packed_sets[gi]
             for layer in range(L):
                 rp.ripe_verify_attn(desc, caches[layer], seq_len, gs, n_rows, 1.0, q, kv_new, out,
-                                    lse, None, ws, ws_bytes, stream)
+                                    lse, None, ws, ws_bytes, stream, block_table=table)
         if events is not None:
             events[1].record(stream)
         sl = seq_len
         for layer in range(L):
             sl = seq_len.copy()
-            rp.ripe_commit(desc, caches[layer], sl, n_accept, src_row, kv_new, n_rows, stream)
+            rp.ripe_commit(desc, caches[layer], sl, n_accept, src_row, kv_new, n_rows, stream, block_table=table)
         seq_len = sl
 
     # Python's cyclic garbage collector can pause the host for tens of
@@ -336,7 +346,8 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
         "gpu_us_per_call": elapsed / (n_calls * steps) * 1e6,
         "describe": f"{case.name} {layout}: B={B}, T~U[{int(case.seq_len.min())},"
                     f"{int(case.seq_len.max())}], R={R}, layers={L}, Hq/Hkv={Hq}/{Hkv}, D={D}, "
-                    f"k={k}, W={W}, depths/step={len(depths) if case.fixed_groups is None else 'mixed'}",
+                    f"k={k}, W={W}, depths/step={len(depths) if case.fixed_groups is None else 'mixed'}"
+                    + (f", paged: {page_len}-position pages in random pool order" if page_len else ""),
         "case": case,
         "layout": layout,
         "dtype": case.dtype,
@@ -344,7 +355,7 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     if graph:
         res["graph"] = graph_replay(one_step_verify_calls=lambda st: [
             rp.ripe_verify_attn(desc, caches[layer], seq_len, packed_sets[gi], n_rows, 1.0, q, kv_new, out,
-                                lse, None, ws, ws_bytes, st)
+                                lse, None, ws, ws_bytes, st, block_table=table)
             for gi in range(len(group_sets)) for layer in range(L)], n_calls=n_calls, steps=steps)
     del caches, q, kv_new, out, lse, ws
     torch.cuda.empty_cache()
@@ -511,6 +522,8 @@ def run_side_stats(reps: int = 20, warmup: int = 3, depths=(4, 16, 28)):
 
 EXTRA_WORKLOADS = [("c2", "ripe"), ("c2", "full"), ("c2", "deepest"), ("c4", None),
                    ("c5-ripe", None), ("c5-full", None), ("c5-deepest", None)]
+# the headline workload again over a paged cache (pages of 256 and 1024 positions)
+PAGED_WORKLOADS = [("c3", 256), ("c3", 1024)]
 
 
 def main():
@@ -523,11 +536,12 @@ def main():
     import torch
     torch.cuda.set_device(0)
     r = run_workload(args.workload, args.layout, args.steps, args.warmup, args.split_len,
-                     args.layers, args.depths, args.copy_calibration, graph=not args.no_extra)
+                     args.layers, args.depths, args.copy_calibration, graph=not args.no_extra,
+                     page_len=args.page_len)
     workload_key = f"{args.workload}-{r['layout']}" if not args.workload.startswith("c5") \
         else args.workload
     traffic = counted_traffic(workload_key) if args.split_len == 0 and args.layers is None \
-        and args.depths in (None, "workload") else None
+        and args.depths in (None, "workload") and args.page_len == 0 else None
     result = {
         "metric": "verify-attn KV read GB/s (% of HBM peak) and verified draft tokens/s, 1 GPU",
         "value": round(r["value"], 2),
@@ -571,6 +585,12 @@ def main():
                 "tokens_extrapolated": e["tokens_extrapolated"],
                 "ms_per_step": round(e["ms_per_step"], 3), "calls_per_step": e["calls_per_step"],
                 "workload": e["describe"]}
+        for name, P in PAGED_WORKLOADS:
+            e = run_workload(name, None, max(2, min(args.steps, 3)), 1, 0, None, None, page_len=P)
+            extra[f"{name}-{e['layout']}-paged{P}"] = {
+                "GB/s": round(e["value"], 1), "hbm_frac": round(e["value"] / HBM_PEAK_GBS, 4),
+                "call_GB/s": round(e["achieved"], 1), "avg_call_us": round(e["avg_call_us"], 2),
+                "ms_per_step": round(e["ms_per_step"], 3), "workload": e["describe"]}
         result["by_workload"] = extra
     if not args.no_extra:
         result["accept"] = run_accept()

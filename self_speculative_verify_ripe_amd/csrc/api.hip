@@ -399,22 +399,22 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     }
     const InFlight fl = in_flight(d.layout, We, T, kp);
     // pieces of this sequence: every segment cut into near-equal runs of at
-    // most S positions; in a paged cache, prefix-plane runs are also cut at
-    // page boundaries and remember their page
+    // most S positions; in a paged cache a prefix-plane segment is first cut
+    // at page boundaries, each page's run then into near-equal pieces, and
+    // every piece remembers its page
     sc.pieces.clear();
     sc.piece_page.clear();
     enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, kp, [&](const Seg& sg) {
-      const int pl = piece_len(sg.len, S);
-      for (int c0 = 0; c0 < sg.len; c0 += pl) {
-        const int c1 = std::min(c0 + pl, sg.len);
-        const bool paged = table != nullptr && sg.kind == kSegPlane;
-        for (int a = c0; a < c1;) {
-          const int e = paged ? std::min(c1, (a / d.page_len + 1) * d.page_len) : c1;
-          sc.pieces.push_back(Piece{a, e - a, uint8_t(sg.kind), uint8_t(sg.depth),
+      const bool paged = table != nullptr && sg.kind == kSegPlane;
+      for (int a0 = 0; a0 < sg.len;) {
+        const int a1 = paged ? std::min(sg.len, (a0 / d.page_len + 1) * d.page_len) : sg.len;
+        const int pl = piece_len(a1 - a0, S);
+        for (int c0 = a0; c0 < a1; c0 += pl) {
+          sc.pieces.push_back(Piece{c0, std::min(pl, a1 - c0), uint8_t(sg.kind), uint8_t(sg.depth),
                                     uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
-          sc.piece_page.push_back(paged ? table[b * nblk + a / d.page_len] : -1);
-          a = e;
+          sc.piece_page.push_back(paged ? table[b * nblk + a0 / d.page_len] : -1);
         }
+        a0 = a1;
       }
       return false;
     });
