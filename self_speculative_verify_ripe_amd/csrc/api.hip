@@ -476,6 +476,9 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
             it.cc = uint16_t(cc);
           }
           Unit& un = cur->u.unit[p.n_units + unit];
+          un.part = sr.part0 + unit * n_split;
+          un.n_split = uint16_t(n_split);
+          un.pad = 0;
           un.s = uint16_t(p.n_seq);
           un.h = uint16_t(h + hh);
           un.cc = uint16_t(cc);

@@ -143,12 +143,18 @@ struct ItemTable {
   int32_t page[kMaxPieces];  // paged caches: the pool page of each prefix-plane piece
 };
 
-// (sequence, KV head, column chunk) of each merge work-group (8 bytes).
+// (sequence, KV head, column chunk) of each merge work-group (16 bytes).
+// part and n_split let the merge issue its partial loads after this one
+// record, before it reads the sequence and group records it needs only to
+// place its outputs.
 struct Unit {
+  int32_t part;        // partial slot of the unit's split 0 (splits are consecutive)
+  uint16_t n_split;    // its splits
   uint16_t s;          // launch-local sequence
   uint16_t h;          // KV head
   uint16_t cc;         // query-column chunk
   uint16_t hl;         // KV head within the sequence record's range
+  uint16_t pad;
 };
 
 struct UnitTable {

@@ -622,20 +622,18 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
   typedef typename FloatN<DPT>::type VecT;
   const int slice = blockIdx.x % NS;
   const Unit un = ut.unit[blockIdx.x / NS];
-  const SeqRec sr = p.seq[un.s];
-  const int n_cc = sr.n_cc;
   const int cc = un.cc;
-  const int hl = un.hl;  // KV head within this launch's range
   const int h = un.h;
   const size_t stride = size_t(CQ) * (D + 2);
-  const float* const part_base = p.ws + (size_t(sr.part0) + size_t(hl * n_cc + cc) * sr.n_split) * stride;
+  const float* const part_base = p.ws + size_t(un.part) * stride;
   const int col = threadIdx.x / TPC;
   const int d0 = slice * SLICE + (threadIdx.x % TPC) * DPT;
-  const bool col_valid = cc * CQ + col < sr.nq;
-  if (col_valid) {
-    int row = 0, hh = 0;
-    const int gi = column_group(p, sr, cc * CQ + col, row, hh);
-    const int ns = sr.n_split;
+  {
+    // Every column of the chunk is merged (a padding column's partials exist
+    // and are merged harmlessly); only the sequence's columns are stored.
+    // The loads need nothing but the unit record, so they go out before the
+    // sequence and group records that place the outputs are read.
+    const int ns = un.n_split;
     // Global maximum first, then the splits' weighted sums in split order.
     // Up to kFast splits are loaded in one round and kept in registers.
     constexpr int kFast = DPT <= 4 ? 16 : 8;
@@ -694,17 +692,23 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
         }
       }
     }
-    const GroupRec& g = p.grp[gi];
-    const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
-    float res[DPT];
+    const SeqRec sr = p.seq[un.s];
+    int row = 0, hh = 0;
+    const int gi = column_group(p, sr, cc * CQ + col, row, hh);
+    if (gi >= 0) {
+      const GroupRec& g = p.grp[gi];
+      const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
+      float res[DPT];
 #pragma unroll
-    for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
-    if (p.out_f32)
-      Op<float>::store(static_cast<float*>(p.out) + orow * D + d0, res, DPT);
-    else
-      O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
-    if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
+      for (int d = 0; d < DPT; ++d) res[d] = o[d] / L;
+      if (p.out_f32)
+        Op<float>::store(static_cast<float*>(p.out) + orow * D + d0, res, DPT);
+      else
+        O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
+      if (p.lse != nullptr && d0 == 0) p.lse[orow] = (M + log2f(L)) * 0.69314718055994530942f;
+    }
   }
+  const SeqRec sr = p.seq[un.s];
   // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0), slice 0
   if (p.plane_sel != nullptr && h == 0 && cc == 0 && slice == 0) {
     for (int gi = sr.g_begin; gi < sr.g_begin + sr.g_count; ++gi) {
