@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB before the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--side-stats-only", action="store_true",
+                    help="run only the side-statistics leg and print its JSON")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
@@ -535,6 +537,9 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.side_stats_only:
+        print(json.dumps({"side_stats": run_side_stats()}), flush=True)
+        return
     r = run_workload(args.workload, args.layout, args.steps, args.warmup, args.split_len,
                      args.layers, args.depths, args.copy_calibration, graph=not args.no_extra,
                      page_len=args.page_len)
