@@ -287,9 +287,12 @@ ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len
  *               entry outside [0, n_pages) is RIPE_ERANGE; other entries are
  *               not read.
  *
- * Verify cuts prefix pieces at page boundaries (one page per split-K work
- * item), so pages shorter than the split length add work items; results
- * equal the unpaged call's when the cut points coincide (e.g. P = t_max).
+ * Pages shorter than the split length (desc->split_len, or the library's
+ * default): verify uses the unpaged call's work plan and reads each
+ * 32-position step from its page, so results are bit-identical to the
+ * unpaged call's.  Pages of at least the split length: prefix pieces are
+ * cut at page boundaries, so each lies in one page (results equal the
+ * unpaged call's where the cut points coincide, e.g. P = t_max).
  * A commit in which two sequences write one (page, slot) is RIPE_EINVAL.
  * The RIPE ring is per sequence and unpaged.
  */

@@ -132,8 +132,8 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   const int64_t groups = std::max<int64_t>(d.max_groups, 1);
   const int64_t rows = std::max<int64_t>(d.max_rows, groups);
   const int64_t nseq = std::min<int64_t>(d.batch, groups);
-  // a paged cache also cuts prefix pieces at page boundaries
-  const int64_t tpieces = (int64_t(d.t_max) + S - 1) / S + (d.page_len > 0 ? d.t_max / d.page_len : 0);
+  // (a paged cache with pages of at least S positions also cuts at pages)
+  const int64_t tpieces = (int64_t(d.t_max) + S - 1) / S + (d.page_len >= S ? d.t_max / d.page_len : 0);
   int64_t per_seq = (d.layout == RIPE_LAYOUT_FULL ? std::min<int64_t>(groups, d.R) : 1) * tpieces;
   if (d.layout == RIPE_LAYOUT_RIPE) per_seq += std::min<int64_t>(groups, d.R - 1) * ((We + S - 1) / S);
   per_seq += groups + (rows + S - 1) / S;  // draft rows
@@ -203,7 +203,6 @@ struct VerifyScratch {
   std::vector<ripe_group_t> key_groups;
   std::vector<int32_t> key_parents;  // empty: no parents
   std::vector<int32_t> key_table;    // paged caches: the block table
-  std::vector<int32_t> piece_page;   // per piece of a sequence: its pool page (-1: none)
 };
 
 VerifyScratch& verify_scratch() {
@@ -352,6 +351,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     VerifyParams& p = lp.p;
     p.ring_off = ring_offset(d);
     p.page_len = d.page_len;
+    p.page_mode = d.page_len == 0 ? 0 : d.page_len >= S ? 1 : 2;  // see the piece cuts below
     p.layout = d.layout;
     p.R = d.R;
     p.We = We;
@@ -366,6 +366,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.n_units = 0;
     p.n_grp = 0;
     p.n_pieces = 0;
+    p.n_refs = 0;
     p.inflight = 0;
     p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
     return lp;
@@ -399,26 +400,32 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     }
     const InFlight fl = in_flight(d.layout, We, T, kp);
     // pieces of this sequence: every segment cut into near-equal runs of at
-    // most S positions; in a paged cache a prefix-plane segment is first cut
-    // at page boundaries, each page's run then into near-equal pieces, and
-    // every piece remembers its page
+    // most S positions.  Paged caches: with pages of at least S positions a
+    // prefix-plane segment is first cut at page boundaries (every piece then
+    // lies in one page); with shorter pages the plan is the unpaged one and
+    // the kernel reads each step of a piece from its page.
+    const bool cut_at_pages = table != nullptr && d.page_len >= S;
     sc.pieces.clear();
-    sc.piece_page.clear();
     enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, kp, [&](const Seg& sg) {
-      const bool paged = table != nullptr && sg.kind == kSegPlane;
+      const bool cut = cut_at_pages && sg.kind == kSegPlane;
       for (int a0 = 0; a0 < sg.len;) {
-        const int a1 = paged ? std::min(sg.len, (a0 / d.page_len + 1) * d.page_len) : sg.len;
+        const int a1 = cut ? std::min(sg.len, (a0 / d.page_len + 1) * d.page_len) : sg.len;
         const int pl = piece_len(a1 - a0, S);
-        for (int c0 = a0; c0 < a1; c0 += pl) {
+        for (int c0 = a0; c0 < a1; c0 += pl)
           sc.pieces.push_back(Piece{c0, std::min(pl, a1 - c0), uint8_t(sg.kind), uint8_t(sg.depth),
                                     uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
-          sc.piece_page.push_back(paged ? table[b * nblk + a0 / d.page_len] : -1);
-        }
         a0 = a1;
       }
       return false;
     });
     const int n_piece = int(sc.pieces.size());
+    // page entries past the first that the sequence's prefix-plane pieces
+    // need (paged caches)
+    int n_refs = 0;
+    if (table != nullptr)
+      for (const Piece& pc : sc.pieces)
+        if (pc.kind == kSegPlane) n_refs += (pc.c0 + pc.len - 1) / d.page_len - pc.c0 / d.page_len;
+    if (n_refs > kMaxPageRefs) return RIPE_EUNSUPPORTED;  // one sequence's pages must fit a launch
     const int n_split = n_piece;
     const int n_cc = (nq + CQ - 1) / CQ;
     const int64_t per_head = int64_t(n_split) * n_cc;
@@ -426,7 +433,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     int h = 0;
     while (h < d.n_kv_heads) {
       if (cur == nullptr || cur->p.n_seq == kMaxSeq || cur->p.n_grp + gc > kMaxGroups ||
-          cur->p.n_wg + per_head > kMaxItems || cur->p.n_pieces + n_piece > kMaxPieces)
+          cur->p.n_wg + per_head > kMaxItems || cur->p.n_pieces + n_piece > kMaxPieces ||
+          cur->p.n_refs + n_refs > kMaxPageRefs)
         cur = &new_plan();
       VerifyParams& p = cur->p;
       const int hc = int(std::min<int64_t>((kMaxItems - p.n_wg) / per_head, d.n_kv_heads - h));
@@ -460,7 +468,14 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
         Piece pc = sc.pieces[k];
         pc.s = uint8_t(p.n_seq);
         if (pc.kind == kSegDraft) pc.gidx = uint8_t(sr.g_begin + pc.gidx);
-        cur->t.page[p.n_pieces] = sc.piece_page[k];
+        cur->t.pref[p.n_pieces] = uint16_t(p.n_refs);
+        cur->t.pages[p.n_pieces] = 0;
+        if (table != nullptr && pc.kind == kSegPlane) {
+          const int blk0 = pc.c0 / d.page_len;
+          cur->t.pages[p.n_pieces] = table[b * nblk + blk0];
+          for (int blk = blk0 + 1; blk * d.page_len < pc.c0 + pc.len; ++blk)
+            cur->t.pages[kMaxPieces + p.n_refs++] = table[b * nblk + blk];
+        }
         cur->t.piece[p.n_pieces++] = pc;
       }
       // items of unit (h, cc): one per piece; partial slot = part0 + unit *

@@ -40,6 +40,7 @@ constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
 constexpr int kMaxItems = 2048;  // verify work items (and merge units) per launch
 constexpr int kMaxPieces = 512;  // pieces per launch
+constexpr int kMaxPageRefs = 512;   // paged caches: pages after a piece's first, per launch
 constexpr int kSoloSteps = 4;    // a piece of at most this many steps runs on one wavefront
 
 // kinds 3 and 4: the rows of a parent block still in flight, read from the
@@ -140,7 +141,11 @@ struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];
   uint16_t wg[kMaxItems];
-  int32_t page[kMaxPieces];  // paged caches: the pool page of each prefix-plane piece
+  // paged caches: prefix-plane piece i starts in page pages[i] (read with the
+  // piece itself); a piece spanning pages continues in pages[kMaxPieces +
+  // pref[i]], pages[kMaxPieces + pref[i] + 1], ...
+  uint16_t pref[kMaxPieces];
+  int32_t pages[kMaxPieces + kMaxPageRefs];
 };
 
 // (sequence, KV head, column chunk) of each merge work-group (16 bytes).
@@ -187,6 +192,8 @@ struct VerifyParams {
   int32_t inflight;      // some sequence of the launch has a parent block in flight
   int32_t out_f32;       // out is fp32 (else the storage dtype)
   int32_t page_len;      // paged cache: positions per page (0: unpaged)
+  int32_t page_mode;     // 0 unpaged, 1 every prefix-plane piece in one page, 2 pieces may span pages
+  int32_t n_refs;        // paged cache: entries of ItemTable::pages used past kMaxPieces
 };
 
 struct CommitJob {     // rows of one sequence written to one region (24 bytes)

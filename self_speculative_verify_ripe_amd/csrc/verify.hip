@@ -314,7 +314,11 @@ constexpr int verify_lds_bytes() {
 // grid order.  INF: the launch has in-flight parent blocks (parent segments,
 // ring slots hidden by the parent); launches without them use the kernel
 // compiled without that code, whose step loop it would otherwise slow down.
-template <typename T, int D, int NB, bool INF>
+// PG, paged caches: 1 when every prefix-plane piece lies inside one page
+// (read from that page), 2 when pieces may span pages (such a piece is read
+// step by step: each 32-position step lies inside one page); 0 unpaged.  The
+// step-by-step code is compiled only into PG = 2, whose loop it slows.
+template <typename T, int D, int NB, bool INF, int PG = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
 void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
@@ -401,16 +405,22 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     // zeros.
     size_t off;
     int bw = kStep;
-    if (pc.kind == kSegPlane) {
-      if (p.page_len > 0) {  // paged: the piece lies inside one page of the pool
-        const size_t page = size_t(tab.page[it.piece]);
-        off = (((p.layout == 0) ? page * p.R + (pc.depth - 1) : page) * p.H + h) * size_t(p.page_len) * D +
-              size_t(pc.c0 % p.page_len) * D;
-      } else {
-        off = (((p.layout == 0) ? size_t(sr.b) * p.R + (pc.depth - 1) : size_t(sr.b)) * p.H + h) *
-                  size_t(p.t_max) * D +
-              size_t(pc.c0) * D;
-      }
+    // a paged prefix-plane piece inside one page is addressed like an
+    // unpaged one; one that spans pages is read step by step (below)
+    const int P = PG > 0 ? p.page_len : 1;
+    const bool plane_paged = PG > 0 && pc.kind == kSegPlane;
+    const bool per_step = PG == 2 && plane_paged && (pc.c0 + pc.len - 1) / P != pc.c0 / P;
+    auto page_base = [&](int pos) -> size_t {  // element offset of position pos of the piece's pages
+      const int k = pos / P - pc.c0 / P;      // page of the piece
+      const size_t pg = size_t(k == 0 ? tab.pages[it.piece] : tab.pages[kMaxPieces + tab.pref[it.piece] + k - 1]);
+      return (((p.layout == 0) ? pg * p.R + (pc.depth - 1) : pg) * p.H + h) * size_t(P) * D + size_t(pos % P) * D;
+    };
+    if (plane_paged) {
+      off = page_base(pc.c0);
+    } else if (pc.kind == kSegPlane) {
+      off = (((p.layout == 0) ? size_t(sr.b) * p.R + (pc.depth - 1) : size_t(sr.b)) * p.H + h) *
+                size_t(p.t_max) * D +
+            size_t(pc.c0) * D;
     } else {
       off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D +
             size_t(pc.c0) * D;  // c0 is a multiple of 32, and of the ring's block width
@@ -425,21 +435,36 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     // those loads return zeros without touching memory, so the prefetch
     // below is unconditional and the wait counts stay exact.
     constexpr uint32_t kOutOfRange = 0x80000000u;
+    // A piece spanning pages: the step's K rows are one 32-row run of its
+    // page and its V values one [D][32] block, so each step gets resources of
+    // its own (a step past the piece reads the piece's last page, out of range).
+    auto step_base = [&](int st) -> size_t { return page_base(pc.c0 + min(st, nsteps - 1) * kStep); };
     auto load_k = [&](int st, bool live, u32x4 (&k)[2][KC]) {
-      const uint32_t base = live ? uint32_t(st * kStep) * D * E + koff : kOutOfRange;
+      __amdgpu_buffer_rsrc_t rs = krs;
+      uint32_t base = live ? uint32_t(st * kStep) * D * E + koff : kOutOfRange;
+      if (PG == 2 && per_step) {
+        rs = make_rsrc(static_cast<const T*>(p.cache_k) + step_base(st),
+                       uint32_t(min(kStep, pc.len - min(st, nsteps - 1) * kStep)) * D * E);
+        base = live ? koff : kOutOfRange;
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int c = 0; c < KC; ++c) k[mb][c] = bload16(krs, base + (4 * mb * D + c * 4 * VEC) * E);
+        for (int c = 0; c < KC; ++c) k[mb][c] = bload16(rs, base + (4 * mb * D + c * 4 * VEC) * E);
     };
     auto load_v = [&](int st, bool live, u32x4 (&v)[DB][VCH]) {
+      __amdgpu_buffer_rsrc_t rs = vrs;
       const int slot0 = st * kStep + 8 * lg;
       const int blk = slot0 / bw;
-      const uint32_t base = live ? uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E : kOutOfRange;
+      uint32_t base = live ? uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E : kOutOfRange;
+      if (PG == 2 && per_step) {  // bw = 32: the step is one whole V block
+        rs = make_rsrc(static_cast<const T*>(p.cache_v) + step_base(st), uint32_t(kStep) * D * E);
+        base = live ? uint32_t(ln * kStep + 8 * lg) * E : kOutOfRange;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) v[db][c] = bload16(vrs, base + (16 * db * bw + c * VEC) * E);
+        for (int c = 0; c < VCH; ++c) v[db][c] = bload16(rs, base + (16 * db * bw + c * VEC) * E);
     };
     const bool hole = INF && pc.kind == kSegRing && sr.hole > 0;
     // first step's loads go out before the query setup
@@ -741,8 +766,14 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
   if (p.n_wg <= 0) return hipSuccess;
   const int grid = p.n_blocks;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  const void* kern = p.inflight ? reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true>)
-                                : reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false>);
+  const void* const kerns[2][3] = {
+      {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0>),
+       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1>),
+       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2>)},
+      {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0>),
+       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1>),
+       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2>)}};
+  const void* kern = kerns[p.inflight ? 1 : 0][p.page_mode];
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
@@ -768,7 +799,7 @@ template <typename T, int D, int NB>
 static int blocks_per_cu_t() {
   static const int n = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0>),
                                                      kThreads, 0) != hipSuccess)
       b = 0;
     return b;

@@ -380,3 +380,19 @@ def test_paged_commit_rejects(table, seq_len, n_accept, status):
     st, sl = call_commit_paged(table, seq_len, n_accept)
     assert st == status
     assert list(sl) == list(seq_len)  # untouched on error
+
+
+def test_paged_page_list_capacity():
+    # one sequence of 69632 positions in 32-position pages: its prefix pieces
+    # need 2176 page entries, more than one launch holds
+    t_max, P = 69632, 32
+    d = rp.make_desc("deepest", "bf16", 2, 0, 1, t_max, 1, 64, 1, max_rows=4, max_groups=1, page_len=P,
+                     n_pages=t_max // P)
+    table = np.arange(t_max // P, dtype=np.int32)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    sl = np.array([t_max - 4], np.int32)
+    garr, ng, _keep = binding._groups([(0, 2, 0, 4)])
+    st = binding.lib.ripe_verify_attn_paged(ctypes.byref(d), FAKE, table.ctypes.data_as(I32P),
+                                            sl.ctypes.data_as(I32P), garr, None, ng, 4, 1.0, FAKE, FAKE, FAKE,
+                                            None, None, FAKE, 1 << 40, None)
+    assert st == -4

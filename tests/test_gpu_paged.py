@@ -3,9 +3,11 @@
 * verify through a random block table against the float64 oracle, every
   layout, pages of 32, 64 and 256 positions, ragged lengths, spare pages
   left NaN (a wrong page address shows up as NaN);
-* the physical placement does not matter: two different tables give
-  bit-identical results; one page per sequence (P = t_max) gives the
-  unpaged call's results bit for bit (same pieces, same order);
+* with pages shorter than the split length (256 positions for these
+  shapes), paging changes only where a step is read from: for every such
+  page size and placement the results equal the unpaged call's bit for bit
+  (the same pieces in the same order); pages of 256 positions and more are
+  cut at page boundaries and checked against the oracle;
 * commit through the table: the cache bytes equal the oracle's commit
   encoded by the oracle's paged encoder, rows crossing page boundaries and
   RIPE windows shorter than the rows committed included;
@@ -65,33 +67,26 @@ def test_paged_verify_matches_oracle(layout, P):
         check(case, groups, gpu, ref, tag=f"paged {layout} P={P} r={r}")
 
 
-@pytest.mark.parametrize("layout", ["full", "ripe"])
-def test_placement_does_not_matter(layout):
+@pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
+def test_paged_equals_unpaged_bitexact(layout):
     case = make_case("c3", B=4, T_range=(100, 500), R=4, Hkv=2, Hq=8, t_max=512)
-    print(f"[case] placement {layout}", flush=True)
+    print(f"[case] paged == unpaged {layout}", flush=True)
     dev = Device(case)
-    groups = case.groups_at(3)
-    res = []
-    for seed in (1, 2):
-        oc, desc, table, N = paged_cache(case, layout, 64, seed=seed)
-        cache = upload(olay.encode_paged(oc, table, 64, N))
-        res.append(verify_paged(desc, cache, table, case, dev, groups))
-    for x, y in zip(res[0], res[1]):
-        assert torch.equal(x, y)
-    # one page per sequence: the unpaged call's pieces, bit for bit
     oc = oracle_cache(case, layout)
-    d1 = rp.make_desc(layout, case.dtype, case.R, case.W, case.B, case.t_max, case.Hkv, case.D, case.Hq,
-                      max_rows=case.n_rows, max_groups=2 * case.B + 8, page_len=case.t_max, n_pages=case.B)
-    ident = np.arange(case.B, dtype=np.int32).reshape(case.B, 1)
-    paged = verify_paged(d1, upload(olay.encode_paged(oc, ident, case.t_max, case.B)), ident, case, dev, groups)
-    d0 = rp.make_desc(layout, case.dtype, case.R, case.W, case.B, case.t_max, case.Hkv, case.D, case.Hq,
-                      max_rows=case.n_rows, max_groups=2 * case.B + 8)
-    out = torch.full_like(paged[0], float("nan"))
-    lse = torch.full_like(paged[1], float("nan"))
-    rp.ripe_verify_attn(d0, upload(olay.encode(oc)), case.seq_len, groups, case.n_rows, case.scale, dev.q,
-                        dev.kv_new, out, lse, None, rp.new_workspace(d0, DEV))
-    torch.cuda.synchronize()
-    assert torch.equal(paged[0], out) and torch.equal(paged[1], lse)
+    res = {}
+    for r in (2, 4):
+        groups = case.groups_at(r)
+        d0 = rp.make_desc(layout, case.dtype, case.R, case.W, case.B, case.t_max, case.Hkv, case.D, case.Hq,
+                          max_rows=case.n_rows, max_groups=2 * case.B + 8)
+        out = torch.full((case.n_rows, case.Hq, case.D), float("nan"), dtype=TORCH_DT[case.dtype], device=DEV)
+        lse = torch.full((case.n_rows, case.Hq), float("nan"), dtype=torch.float32, device=DEV)
+        rp.ripe_verify_attn(d0, upload(olay.encode(oc)), case.seq_len, groups, case.n_rows, case.scale, dev.q,
+                            dev.kv_new, out, lse, None, rp.new_workspace(d0, DEV))
+        torch.cuda.synchronize()
+        for P, seed in ((32, 1), (64, 2), (64, 3), (128, 4)):
+            _, desc, table, N = paged_cache(case, layout, P, seed=seed, oc=oc)
+            po, pl, _ = verify_paged(desc, upload(olay.encode_paged(oc, table, P, N)), table, case, dev, groups)
+            assert torch.equal(po, out) and torch.equal(pl, lse), (layout, r, P, seed)
 
 
 @pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
