@@ -21,8 +21,7 @@ Sources (cited by page and passage):
 * RIPE abstract (zhuanzhiai.com paper page): the verify pass runs the draft
   block through all R loops, so the target distributions come from depth R.
 
-The scheme written out (readings where the page is silent; each is listed in
-DESIGN.md):
+The scheme written out (with the readings taken where the page is silent):
 
 * Per sequence there is a primary chain of k draft tokens x_0..x_{k-1} and,
   optionally, a fallback chain y_0..y_{k-1} that replaces the primary from

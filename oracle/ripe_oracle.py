@@ -20,7 +20,7 @@ Sources (the pages are cited by page and passage):
   at different recurrent depths are processed in one batched call; a rejected
   branch is dropped and decoding rolls back to the confirmed prefix.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * depth r is 1-based, plane R is the deepest;
 * the window is anchored at the committed length T: prefix position j is read
