@@ -628,8 +628,8 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
 // head-dim slice of SLICE values.  It combines the unit's split partials in
 // split order, normalises and writes its slice of out; slice 0 also writes
 // lse, and (KV head 0, chunk 0, slice 0) the sequence's plane_sel rows.
-// Narrow slices give small batches more work-groups (and room to load up to
-// 16 splits in one round); large batches use whole rows.
+// 32-wide slices give small batches more work-groups (and room to load up to
+// 16 splits in one round); larger batches use 64-wide ones.
 constexpr int kMergeThreads = 256;  // threads per merge work-group
 
 template <int N>
@@ -776,12 +776,17 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
   const void* kern = kerns[p.inflight ? 1 : 0][p.page_mode];
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
+  // Merge: 64-wide head-dim slices while they still give one work-group per
+  // compute unit, else 32-wide ones (more work-groups for few units).
+  // Measured against 32-wide slices up to 1024 work-groups and whole rows
+  // beyond: c3 and c4 -0.5 us, c5 RIPE -1.6 us per call, c5 FULL (32 units)
+  // unchanged.
   void* margs[] = {const_cast<VerifyParams*>(&p), const_cast<UnitTable*>(&u)};
-  if (p.n_units * (D / 32) <= 1024)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, 32>),
-                           dim3(p.n_units * (D / 32)), dim3(kMergeThreads), margs, 0, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, D>), dim3(p.n_units),
-                         dim3(kMergeThreads), margs, 0, stream);
+  if (p.n_units * (D / 64) >= 256)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, 64>),
+                           dim3(p.n_units * (D / 64)), dim3(kMergeThreads), margs, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&verify_merge_kernel<T, D, NB, 32>),
+                         dim3(p.n_units * (D / 32)), dim3(kMergeThreads), margs, 0, stream);
 }
 
 hipError_t launch_verify(const VerifyParams& p, const ItemTable& t, const UnitTable& u, int dtype, int D, int NB,
