@@ -682,9 +682,9 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
       for (int u = 0; u < kFast; ++u) {
         const bool ok = u < ns;
         const float* part = part_base + size_t(ok ? u : 0) * stride;
-        ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
-        ls[u] = part[size_t(CQ) * D + CQ + col];
-        ov[u] = *reinterpret_cast<const VecT*>(part + size_t(col) * D + d0);
+        ms[u] = ok ? __builtin_nontemporal_load(part + size_t(CQ) * D + col) : -INFINITY;
+        ls[u] = __builtin_nontemporal_load(part + size_t(CQ) * D + CQ + col);
+        ov[u] = __builtin_nontemporal_load(reinterpret_cast<const VecT*>(part + size_t(col) * D + d0));
       }
 #pragma unroll
       for (int u = 0; u < kFast; ++u) M = fmaxf(M, ms[u]);
@@ -712,9 +712,9 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
         for (int u = 0; u < U; ++u) {
           const bool ok = sp + u < ns;
           const float* part = part_base + size_t(ok ? sp + u : 0) * stride;
-          ms[u] = ok ? part[size_t(CQ) * D + col] : -INFINITY;
-          ls[u] = part[size_t(CQ) * D + CQ + col];
-          ov[u] = *reinterpret_cast<const VecT*>(part + size_t(col) * D + d0);
+          ms[u] = ok ? __builtin_nontemporal_load(part + size_t(CQ) * D + col) : -INFINITY;
+          ls[u] = __builtin_nontemporal_load(part + size_t(CQ) * D + CQ + col);
+          ov[u] = __builtin_nontemporal_load(reinterpret_cast<const VecT*>(part + size_t(col) * D + d0));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
