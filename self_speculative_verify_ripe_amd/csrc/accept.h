@@ -9,6 +9,7 @@ namespace ripe {
 constexpr int kAcceptTile = 64;        // vocabulary indices per tile of a draw
 constexpr int kAcceptSliceMin = 4096;  // at least this many indices per work-group slice
 constexpr int kAcceptMaxSplit = 64;    // slices per row at most
+constexpr int kPartsPerSlice = 4;      // parts per slice of the per-sequence sweeps (residual masses, draw weights)
 
 struct RowStat {
   double S;     // sum over the row (or a slice of it) of exp((z - M) * inv_tau)
@@ -41,9 +42,9 @@ struct AcceptParams {
   RowStat* part;           // [B][4k+2][split]: per-slice statistics
   RowStat* stats;          // [B][4k+2]
   SeqState* state;         // [B]
-  double* sums;            // [B][split][2]: per-slice residual masses
+  double* sums;            // [B][split * kPartsPerSlice][2]: residual masses per part
   double* tiles;           // [B][n_tiles]: tile sums of the final draw's weights
-  int32_t* last;           // [B][split]: last index with weight > 0 per slice
+  int32_t* last;           // [B][split * kPartsPerSlice]: last index with weight > 0 per part
   int32_t B, k, V;
   int32_t greedy;          // temperature == 0
   double inv_tau;          // 1 / temperature
@@ -72,9 +73,9 @@ inline AcceptLayout accept_layout(int64_t B, int64_t k, int64_t V) {
   L.off_part = off;  off += accept_align(B * rows * split * int64_t(sizeof(RowStat)));
   L.off_stats = off; off += accept_align(B * rows * int64_t(sizeof(RowStat)));
   L.off_state = off; off += accept_align(B * int64_t(sizeof(SeqState)));
-  L.off_sums = off;  off += accept_align(B * split * 2 * int64_t(sizeof(double)));
+  L.off_sums = off;  off += accept_align(B * split * kPartsPerSlice * 2 * int64_t(sizeof(double)));
   L.off_tiles = off; off += accept_align(B * L.n_tiles * int64_t(sizeof(double)));
-  L.off_last = off;  off += accept_align(B * split * int64_t(sizeof(int32_t)));
+  L.off_last = off;  off += accept_align(B * split * kPartsPerSlice * int64_t(sizeof(int32_t)));
   L.bytes = off;
   return L;
 }

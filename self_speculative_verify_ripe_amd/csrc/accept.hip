@@ -19,10 +19,10 @@
 //   accept_decide_kernel    per sequence: combines the slices into each row's
 //                           statistics; greedy decisions (final), or the
 //                           primary chain's speculative tests
-//   accept_fbsum_kernel     per (sequence, slice), only after a first-token
+//   accept_fbsum_kernel     per (sequence, quarter slice), only after a first-token
 //                           rejection with a fallback: the residual masses
 //   accept_fallback_kernel  per sequence: the fallback's tests
-//   accept_drawsum_kernel   per (sequence, slice): sums of the final draw's
+//   accept_drawsum_kernel   per (sequence, quarter slice): sums of the final draw's
 //                           weights over tiles of 64 indices
 //   accept_pick_kernel      per sequence: the tile where the running sum
 //                           crosses u * total, then the index inside it
@@ -48,6 +48,21 @@ __device__ inline const float* row_ptr(const AcceptParams& p, int b, int r) {
   const int k = p.k;
   if (r < 2 * (k + 1)) return p.target + (size_t(b) * 2 * (k + 1) + r) * p.V;
   return p.draft + (size_t(b) * 2 * k + (r - 2 * (k + 1))) * p.V;
+}
+
+// Loads per thread issued together by the per-index loops, so that each
+// thread has several reads in flight instead of waiting on every element.
+constexpr int kLoadBatch = 8;
+// Logits per thread the row statistics keep in registers: a slice of up to
+// kHeld * 256 indices (every slice up to a 256K vocabulary) is read once.
+constexpr int kHeld = kAcceptSliceMin / kAcceptThreads;
+
+// z[t] for t < t1, else `other`.  The load itself is unconditional, from
+// index min(t, t1 - 1) (callers have t1 > 0), so the compiler keeps the
+// batch's loads together instead of branching around each one.
+__device__ inline float load_or(const float* z, int t, int t1, float other) {
+  const float v = z[min(t, t1 - 1)];
+  return t < t1 ? v : other;
 }
 
 // ---------------------------------------------------------------------------
@@ -95,9 +110,11 @@ struct Dist {           // softmax of one row: exp((z - M) * inv_tau) / S
   double M, S;
 };
 
-__device__ inline double prob(const Dist& d, double inv_tau, int t) {
-  return exp((double(d.z[t]) - d.M) * inv_tau) / d.S;
+__device__ inline double prob_of(const Dist& d, double inv_tau, float z) {
+  return exp((double(z) - d.M) * inv_tau) / d.S;
 }
+
+__device__ inline double prob(const Dist& d, double inv_tau, int t) { return prob_of(d, inv_tau, d.z[t]); }
 
 // The weights a final draw uses, as a function of the index.  With the
 // fallback's residual target r(t) = max(0, a - c) / Wr (a itself when Wr = 0)
@@ -125,18 +142,27 @@ __device__ inline double fallback_q(const DrawSpec& s, double inv_tau, int t) {
   return s.Wm > 0.0 ? fmax(prob(s.m, inv_tau, t) - prob(s.c, inv_tau, t), 0.0) / s.Wm : 0.0;
 }
 
-__device__ inline double weight(const DrawSpec& s, double inv_tau, int t) {
+// The weight of one index from its logits in rows a, c and m (rows a kind
+// does not use alias a, so every load is valid).
+__device__ inline double weight_of(const DrawSpec& s, double inv_tau, float za, float zc, float zm) {
   switch (s.kind) {
-    case kDrawRow: return prob(s.a, inv_tau, t);
-    case kDrawResidual: return fmax(prob(s.a, inv_tau, t) - prob(s.c, inv_tau, t), 0.0);
-    case kDrawFallbackR: return fallback_r(s, inv_tau, t);
+    case kDrawRow: return prob_of(s.a, inv_tau, za);
+    case kDrawResidual: return fmax(prob_of(s.a, inv_tau, za) - prob_of(s.c, inv_tau, zc), 0.0);
+    case kDrawFallbackR: {
+      const double pa = prob_of(s.a, inv_tau, za);
+      return s.Wr > 0.0 ? fmax(pa - prob_of(s.c, inv_tau, zc), 0.0) / s.Wr : pa;
+    }
     default: {  // kDrawRestart: fallback_r - fallback_q, with c's probability computed once
-      const double pa = prob(s.a, inv_tau, t), pc = prob(s.c, inv_tau, t);
+      const double pa = prob_of(s.a, inv_tau, za), pc = prob_of(s.c, inv_tau, zc);
       const double r = s.Wr > 0.0 ? fmax(pa - pc, 0.0) / s.Wr : pa;
-      const double q = s.Wm > 0.0 ? fmax(prob(s.m, inv_tau, t) - pc, 0.0) / s.Wm : 0.0;
+      const double q = s.Wm > 0.0 ? fmax(prob_of(s.m, inv_tau, zm) - pc, 0.0) / s.Wm : 0.0;
       return fmax(r - q, 0.0);
     }
   }
+}
+
+__device__ inline double weight(const DrawSpec& s, double inv_tau, int t) {
+  return weight_of(s, inv_tau, s.a.z[t], s.c.z[t], s.m.z[t]);
 }
 
 // First index whose running sum of weights exceeds u * total; the last index
@@ -284,13 +310,47 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_stats_kernel(const Acce
   const int t1 = min(p.V, t0 + p.slice);
   float mv = -INFINITY;
   int mi = 0x7fffffff;
-  for (int t = t0 + threadIdx.x; t < t1; t += kAcceptThreads) better(mv, mi, z[t], t);
-  wg_argmax(mv, mi);
   double s = 0.0;
-  if (!p.greedy && mv > -INFINITY) {
-    const double M = mv;
-    for (int t = t0 + threadIdx.x; t < t1; t += kAcceptThreads) s += exp((double(z[t]) - M) * p.inv_tau);
-    s = wg_sum(s);
+  const bool sum = !p.greedy;
+  if (t1 - t0 <= kHeld * kAcceptThreads) {
+    // the whole slice in registers: one read of the logits serves both passes
+    float zv[kHeld];
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) zv[j] = load_or(z, t0 + threadIdx.x + j * kAcceptThreads, t1, -INFINITY);
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j)
+      if (t0 + int(threadIdx.x) + j * kAcceptThreads < t1) better(mv, mi, zv[j], t0 + threadIdx.x + j * kAcceptThreads);
+    wg_argmax(mv, mi);
+    if (sum && mv > -INFINITY) {
+      const double M = mv;
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j)
+        if (t0 + int(threadIdx.x) + j * kAcceptThreads < t1) s += exp((double(zv[j]) - M) * p.inv_tau);
+      s = wg_sum(s);
+    }
+  } else {
+    // longer slices: kLoadBatch loads in flight per thread, the slice read twice
+    for (int t = t0 + threadIdx.x; t < t1; t += kLoadBatch * kAcceptThreads) {
+      float zv[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) zv[j] = load_or(z, t + j * kAcceptThreads, t1, -INFINITY);
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j)
+        if (t + j * kAcceptThreads < t1) better(mv, mi, zv[j], t + j * kAcceptThreads);
+    }
+    wg_argmax(mv, mi);
+    if (sum && mv > -INFINITY) {
+      const double M = mv;
+      for (int t = t0 + threadIdx.x; t < t1; t += kLoadBatch * kAcceptThreads) {
+        float zv[kLoadBatch];
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j) zv[j] = load_or(z, t + j * kAcceptThreads, t1, 0.f);
+#pragma unroll
+        for (int j = 0; j < kLoadBatch; ++j)
+          if (t + j * kAcceptThreads < t1) s += exp((double(zv[j]) - M) * p.inv_tau);
+      }
+      s = wg_sum(s);
+    }
   }
   if (threadIdx.x == 0) p.part[size_t(br) * p.split + sl] = RowStat{s, mv, mi};
 }
@@ -372,27 +432,40 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_decide_kernel(const Acc
 }
 
 // ---------------------------------------------------------------------------
-// 3. the fallback's residual masses, per slice
+// 3. the fallback's residual masses, per quarter slice
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kAcceptThreads) void accept_fbsum_kernel(const AcceptParams p) {
-  const int sl = blockIdx.x % p.split;
-  const int b = blockIdx.x / p.split;
+  const int n_parts = p.split * kPartsPerSlice;
+  const int part = blockIdx.x % n_parts;
+  const int b = blockIdx.x / n_parts;
   const SeqState ss = p.state[b];
   if (ss.stage != kStageFallback) return;
   const Dist a = dist_of(p, b, ss.ra), c = dist_of(p, b, ss.rc), m = dist_of(p, b, ss.rm);
-  const int t0 = sl * p.slice;
-  const int t1 = min(p.V, t0 + p.slice);
+  const int per_part = (p.slice + kPartsPerSlice - 1) / kPartsPerSlice;
+  const int t0 = part * per_part;
+  const int t1 = min(p.V, t0 + per_part);
   double wr = 0.0, wm = 0.0;
-  for (int t = t0 + threadIdx.x; t < t1; t += kAcceptThreads) {
-    const double pc = prob(c, p.inv_tau, t);
-    wr += fmax(prob(a, p.inv_tau, t) - pc, 0.0);
-    wm += fmax(prob(m, p.inv_tau, t) - pc, 0.0);
+  for (int t = t0 + threadIdx.x; t < t1; t += kLoadBatch * kAcceptThreads) {
+    float za[kLoadBatch], zc[kLoadBatch], zm[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      za[j] = load_or(a.z, t + j * kAcceptThreads, t1, 0.f);
+      zc[j] = load_or(c.z, t + j * kAcceptThreads, t1, 0.f);
+      zm[j] = load_or(m.z, t + j * kAcceptThreads, t1, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j)
+      if (t + j * kAcceptThreads < t1) {
+        const double pc = prob_of(c, p.inv_tau, zc[j]);
+        wr += fmax(prob_of(a, p.inv_tau, za[j]) - pc, 0.0);
+        wm += fmax(prob_of(m, p.inv_tau, zm[j]) - pc, 0.0);
+      }
   }
   wr = wg_sum(wr);
   wm = wg_sum(wm);
   if (threadIdx.x == 0) {
-    p.sums[(size_t(b) * p.split + sl) * 2] = wr;
-    p.sums[(size_t(b) * p.split + sl) * 2 + 1] = wm;
+    p.sums[(size_t(b) * n_parts + part) * 2] = wr;
+    p.sums[(size_t(b) * n_parts + part) * 2 + 1] = wm;
   }
 }
 
@@ -414,15 +487,20 @@ __global__ void accept_fallback_kernel(const AcceptParams p) {
     s_pt[i] = ok ? prob(dist_of(p, b, target_row(k, 1, i)), it, t) : 0.0;
     s_qt[i] = ok ? prob(dist_of(p, b, draft_row(k, 1, i)), it, t) : 0.0;
   }
+  // the residual masses: the parts' sums, lane i taking parts i, i + 64, ...
+  // in order, then a fixed xor tree over the lanes
+  double Wr = 0.0, Wm = 0.0;
+  const int n_parts = p.split * kPartsPerSlice;
+  for (int i = threadIdx.x; i < n_parts; i += 64) {
+    Wr += p.sums[(size_t(b) * n_parts + i) * 2];
+    Wm += p.sums[(size_t(b) * n_parts + i) * 2 + 1];
+  }
+  Wr = wave_sum(Wr);
+  Wm = wave_sum(Wm);
   __syncthreads();
   if (threadIdx.x != 0) return;
   const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
   auto uni = [&](int w) { return double(rw[w]) * (1.0 / 4294967296.0); };
-  double Wr = 0.0, Wm = 0.0;
-  for (int i = 0; i < p.split; ++i) {
-    Wr += p.sums[(size_t(b) * p.split + i) * 2];
-    Wm += p.sums[(size_t(b) * p.split + i) * 2 + 1];
-  }
   ss.Wr = Wr;
   ss.Wm = Wm;
   ss.kind = kDrawRestart;
@@ -449,31 +527,50 @@ __global__ void accept_fallback_kernel(const AcceptParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 5. tile sums of the final draw's weights, per slice
+// 5. tile sums of the final draw's weights, per quarter slice
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const AcceptParams p) {
   __shared__ int s_last;
-  const int sl = blockIdx.x % p.split;
-  const int b = blockIdx.x / p.split;
+  // kPartsPerSlice parts per slice, so that a small batch still fills the chip
+  const int n_parts = p.split * kPartsPerSlice;
+  const int part = blockIdx.x % n_parts;
+  const int b = blockIdx.x / n_parts;
   const SeqState ss = p.state[b];
   if (ss.stage != kStageDraw) return;
   const DrawSpec d = spec_of(p, b, ss);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile0 = sl * (p.slice / kAcceptTile);
-  const int tile1 = min(p.n_tiles, tile0 + p.slice / kAcceptTile);
+  const int per_part = (p.slice / kAcceptTile + kPartsPerSlice - 1) / kPartsPerSlice;  // tiles
+  const int tile0 = part * per_part;
+  const int tile1 = min(p.n_tiles, tile0 + per_part);
   if (threadIdx.x == 0) s_last = -1;
   __syncthreads();
   int last = -1;
-  for (int tile = tile0 + wave; tile < tile1; tile += kAcceptThreads / 64) {
-    const int t = tile * kAcceptTile + lane;
-    const double w = t < p.V ? weight(d, p.inv_tau, t) : 0.0;
-    if (w > 0.0) last = t;
-    const double ts = wave_sum(w);
-    if (lane == 0) p.tiles[size_t(b) * p.n_tiles + tile] = ts;
+  constexpr int kWaves = kAcceptThreads / 64;
+  for (int tw = tile0 + wave; tw < tile1; tw += kLoadBatch * kWaves) {
+    // this wavefront's next kLoadBatch tiles: loads first, then the sums
+    float za[kLoadBatch], zc[kLoadBatch], zm[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      // tiles past tile1 load index V - 1 and are not used
+      const int t = tw + j * kWaves < tile1 ? (tw + j * kWaves) * kAcceptTile + lane : p.V;
+      za[j] = load_or(d.a.z, t, p.V, 0.f);
+      zc[j] = load_or(d.c.z, t, p.V, 0.f);
+      zm[j] = load_or(d.m.z, t, p.V, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int tile = tw + j * kWaves;
+      if (tile >= tile1) break;
+      const int t = tile * kAcceptTile + lane;
+      const double w = t < p.V ? weight_of(d, p.inv_tau, za[j], zc[j], zm[j]) : 0.0;
+      if (w > 0.0) last = t;
+      const double ts = wave_sum(w);
+      if (lane == 0) p.tiles[size_t(b) * p.n_tiles + tile] = ts;
+    }
   }
   atomicMax(&s_last, last);
   __syncthreads();
-  if (threadIdx.x == 0) p.last[size_t(b) * p.split + sl] = s_last;
+  if (threadIdx.x == 0) p.last[size_t(b) * n_parts + part] = s_last;
 }
 
 // ---------------------------------------------------------------------------
@@ -552,8 +649,10 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_pick_kernel(const Accep
     const unsigned long long over = __ballot(t < p.V && incl > target);
     if (over != 0ull) result = hit * kAcceptTile + __ffsll(static_cast<long long>(over)) - 1;
   }
-  if (result < 0)  // rounding left no crossing: the last index with weight > 0
-    for (int i = 0; i < p.split; ++i) result = max(result, p.last[size_t(b) * p.split + i]);
+  if (result < 0) {  // rounding left no crossing: the last index with weight > 0
+    const int n_parts = p.split * kPartsPerSlice;
+    for (int i = 0; i < n_parts; ++i) result = max(result, p.last[size_t(b) * n_parts + i]);
+  }
   if (lane == 0) {
     p.n_accept[b] = ss.n;
     p.branch[b] = ss.branch;
@@ -572,9 +671,9 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   const Launch all[] = {
       {reinterpret_cast<const void*>(&accept_stats_kernel), p.B * rows * p.split, kAcceptThreads},
       {reinterpret_cast<const void*>(&accept_decide_kernel), p.B, kAcceptThreads},
-      {reinterpret_cast<const void*>(&accept_fbsum_kernel), p.B * p.split, kAcceptThreads},
+      {reinterpret_cast<const void*>(&accept_fbsum_kernel), p.B * p.split * kPartsPerSlice, kAcceptThreads},
       {reinterpret_cast<const void*>(&accept_fallback_kernel), p.B, 64},
-      {reinterpret_cast<const void*>(&accept_drawsum_kernel), p.B * p.split, kAcceptThreads},
+      {reinterpret_cast<const void*>(&accept_drawsum_kernel), p.B * p.split * kPartsPerSlice, kAcceptThreads},
       {reinterpret_cast<const void*>(&accept_pick_kernel), p.B, kAcceptThreads}};
   const int n = p.greedy ? 2 : 6;  // greedy decisions are final after the second
   for (int i = 0; i < n; ++i) {
