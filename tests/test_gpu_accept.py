@@ -68,6 +68,19 @@ def test_accept_full_vocab_size():
         compare(inp, temperature, f"V=65536 tau={temperature}")
 
 
+@pytest.mark.parametrize("B,k,V", [(12, 3, 70001), (4, 2, 300007)])
+def test_accept_ragged_and_long_slices(B, k, V):
+    """Vocabulary sizes that slice unevenly: 70001 gives 18 slices of 3904
+    indices and a shorter last one (every per-index sweep has a ragged
+    tail); 300007 hits the 64-slice cap, so slices of 4736 indices are longer
+    than the 4096 the row statistics hold in registers and take the
+    two-pass path."""
+    for temperature in (0.0, 0.9):
+        inp = accept_inputs(4242 + V, B, k, V, temperature, fallback_frac=0.5, draft_noise=1.5)
+        print(f"[case] B={B} k={k} V={V} tau={temperature}", flush=True)
+        compare(inp, temperature, f"B={B} k={k} V={V} tau={temperature}")
+
+
 def test_accept_edge_cases():
     # tokens out of range, masked (-inf) logits, exact ties for greedy, V = 1
     inp = accept_inputs(31, 40, 3, 64, 0.9, fallback_frac=0.6)
