@@ -11,7 +11,7 @@ Sources (the pages are cited by page and passage):
   - a looped LM runs one block R times per token, so its KV cache holds R
     planes per recurrent layer; self-speculative decoding drafts with a few
     loops and verifies with all R, reading every plane;
-  - the deepest plane alone ("one shared plane") is one cache variant;
+  - the deepest plane alone, shared by every depth, is one cache variant;
   - RIPE stores the deepest plane everywhere except a window of recent
     positions that is kept at full depth;
   - a window at least as long as the draft block makes batched verification
