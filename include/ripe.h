@@ -9,7 +9,7 @@
  * paper page, opening sentence).  Three cache layouts are supported:
  *
  *   FULL     every plane at every position; depth r reads plane r;
- *   DEEPEST  only the deepest plane R ("one shared plane"); every depth
+ *   DEEPEST  only the deepest plane R, shared by all depths; every depth
  *            reads plane R;
  *   RIPE     plane R at every position plus planes 1..R-1 for a window of
  *            the W most recent committed positions; depth r reads plane r
