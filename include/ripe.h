@@ -294,7 +294,11 @@ ripe_status_t ripe_commit(const ripe_desc_t* desc, void* cache, int32_t* seq_len
  * cut at page boundaries, so each lies in one page (results equal the
  * unpaged call's where the cut points coincide, e.g. P = t_max).
  * A commit in which two sequences write one (page, slot) is RIPE_EINVAL.
- * The RIPE ring is per sequence and unpaged.
+ * The RIPE ring is per sequence and unpaged.  A launch carries the page
+ * numbers its pieces read in its kernel arguments: at most 512 pages beyond
+ * the first page of each piece, summed over the launch's pieces.  A
+ * sequence needing more on its own (pages shorter than the split length and
+ * a prefix of about 512 * page_len positions or more) is RIPE_EUNSUPPORTED.
  */
 ripe_status_t ripe_verify_attn_paged(const ripe_desc_t* desc, const void* cache, const int32_t* block_table,
                                      const int32_t* seq_len, const ripe_group_t* groups, const int32_t* parents,
