@@ -2,9 +2,10 @@
 
 * Drafting at depth r_d < R is the verify call with one-row groups (RIPE
   abstract: draft with a few loops); checked against the oracle.
-* A sweep of verify calls over (depth, recurrent layer), and an accept call,
-  captured into one HIP graph (torch.cuda.CUDAGraph) and replayed several
-  times with eager work and synchronisations between the replays: every
+* A sweep of verify calls over (depth, recurrent layer), the same sweep
+  over a paged cache, and an accept call, captured into one HIP graph
+  (torch.cuda.CUDAGraph) and replayed several times with eager work and
+  synchronisations between the replays: every
   replay must reproduce the eager results bit for bit.  The library makes no
   allocation, memset or host synchronisation inside a call, so its launches
   can be captured; the captured calls keep the sequence lengths and groups
@@ -93,6 +94,59 @@ def test_verify_sweep_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, ((o, l), (eo, el)) in enumerate(zip(zip(outs, lses), eager)):
             assert torch.equal(o, eo) and torch.equal(l, el), f"replay {rep}, call {i}"
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_paged_sweep_graph_replays_match_eager(P):
+    """The paged verify call under capture.  With a split length of 64,
+    32-position pages take the step-by-step page reads and 128-position pages
+    the pieces cut at page boundaries; the block table travels in the
+    captured kernel arguments."""
+    case = make_case("c3", B=3, T_range=(100, 700), R=4, Hkv=2, Hq=8, t_max=768)
+    oc = oracle_cache(case, "ripe")
+    nb = case.t_max // P
+    N = case.B * nb + 2
+    table = np.random.default_rng(P).permutation(N)[:case.B * nb].reshape(case.B, nb).astype(np.int32)
+    cache = upload(olay.encode_paged(oc, table, P, N))
+    desc = rp.make_desc("ripe", case.dtype, case.R, case.W, case.B, case.t_max, case.Hkv, case.D, case.Hq,
+                        max_rows=case.n_rows, max_groups=case.B, split_len=64, page_len=P, n_pages=N)
+    dev = Device(case)
+    packed = [rp.pack_groups(case.groups_at(r)) for r in range(1, case.R + 1)]
+    outs = [torch.zeros((case.n_rows, case.Hq, case.D), dtype=torch.bfloat16, device=DEV) for _ in packed]
+    lses = [torch.zeros((case.n_rows, case.Hq), dtype=torch.float32, device=DEV) for _ in packed]
+    ws = rp.new_workspace(desc, DEV)
+    stream = torch.cuda.Stream()
+
+    def sweep():
+        for gs, o, l in zip(packed, outs, lses):
+            rp.ripe_verify_attn(desc, cache, case.seq_len, gs, case.n_rows, case.scale, dev.q, dev.kv_new, o, l,
+                                None, ws, None, stream, block_table=table)
+
+    print(f"[case] paged graph P={P}", flush=True)
+    with torch.cuda.stream(stream):
+        sweep()
+    torch.cuda.synchronize()
+    eager = [(o.clone(), l.clone()) for o, l in zip(outs, lses)]
+    # the eager calls themselves agree with the oracle
+    r = case.R
+    ref = ro.verify(oc, case.groups_at(r), case.q, case.kv_new, case.scale, case.Hq)
+    check(case, case.groups_at(r), (eager[r - 1][0], eager[r - 1][1], None), ref, tag=f"paged graph P={P}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        sweep()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o, l in zip(outs, lses):  # cleared outside the graph, by a kernel
+            o.zero_()
+            l.zero_()
+        other = torch.zeros_like(outs[0])  # eager work on the same workspace between replays
+        rp.ripe_verify_attn(desc, cache, case.seq_len, packed[0], case.n_rows, 0.5, dev.q, dev.kv_new, other,
+                            None, None, ws, block_table=table)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((o, l), (eo, el)) in enumerate(zip(zip(outs, lses), eager)):
+            assert torch.equal(o, eo) and torch.equal(l, el), f"P={P} replay {rep}, call {i}"
 
 
 def test_accept_graph_replays_match_eager():
