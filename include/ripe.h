@@ -2,11 +2,12 @@
  * ripe.h -- C ABI of the RIPE self-speculative verification library for
  * AMD Instinct MI355X (gfx950).
  *
- * A looped (depth-recurrent) language model runs one block of layers R times
- * per token, so each recurrent layer's KV cache holds R planes, one per loop;
- * self-speculative decoding drafts with a few loops and verifies a draft
- * block with all R loops, reading every plane (RIPE abstract, zhuanzhiai.com
- * paper page, opening sentence).  Three cache layouts are supported:
+ * In a looped (depth-recurrent) language model every token passes R times
+ * through the same recurrent block, so the KV cache of a recurrent layer
+ * keeps R planes, one per loop.  Self-speculative decoding proposes tokens
+ * from a shallow loop count and checks them with all R loops, and that check
+ * touches every plane (RIPE abstract, zhuanzhiai.com paper page, opening
+ * sentence).  Three cache layouts are supported:
  *
  *   FULL     every plane at every position; depth r reads plane r;
  *   DEEPEST  only the deepest plane R, shared by all depths; every depth
@@ -24,9 +25,14 @@
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory owned by the caller;
  *    pointers marked "host" are read (or, for seq_len in ripe_commit,
- *    updated) before the call returns.  The library allocates nothing and
- *    keeps no state between calls; calls are asynchronous on `stream`
- *    (0 = the null stream) and never synchronise the host.
+ *    updated) before the call returns.  The library allocates no device
+ *    memory.  Calls are asynchronous on `stream` (0 = the null stream) and
+ *    never synchronise the host.
+ *  - State kept between calls: each host thread keeps the work plan of its
+ *    last verify call (host memory).  A verify call on the same thread whose
+ *    descriptor, lengths, groups, parents, scale and block table equal that
+ *    call's reuses the plan with the new buffer pointers.  The plan is a
+ *    pure function of those inputs, so results never depend on the cache.
  *  - Every argument is validated on the host before any HIP call.  On an
  *    error nothing is launched and no output (device or host) is modified.
  *  - Device pointers must be 16-byte aligned (workspace: 256-byte aligned).
@@ -242,8 +248,8 @@ ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cac
                                         size_t workspace_bytes, void* stream);
 
 /*
- * Commit accepted draft rows (RIPE abstract: the window of recent positions
- * is kept at full depth, older positions collapse to the deepest plane;
+ * Commit accepted draft rows (RIPE abstract, sentence introducing RIPE: the
+ * W most recent positions hold every plane, older ones only the last;
  * LoopSpec summary: rejected continuations are dropped and decoding resumes
  * from the confirmed prefix).
  *

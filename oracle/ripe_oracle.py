@@ -8,14 +8,15 @@ nothing from the library.
 Sources (the pages are cited by page and passage):
 
 * RIPE abstract (zhuanzhiai.com paper page, abstract paragraph):
-  - a looped LM runs one block R times per token, so its KV cache holds R
-    planes per recurrent layer; self-speculative decoding drafts with a few
-    loops and verifies with all R, reading every plane;
-  - the deepest plane alone, shared by every depth, is one cache variant;
-  - RIPE stores the deepest plane everywhere except a window of recent
-    positions that is kept at full depth;
-  - a window at least as long as the draft block makes batched verification
-    block-independent.
+  - opening sentence: the looped model repeats its recurrent block R times for
+    every token, so each recurrent layer caches R K/V planes; drafting uses
+    few loops and verification uses all R, so it reads every plane;
+  - sentence on the deepest plane: one plane (the last) can serve every depth;
+  - sentence introducing RIPE: only the last plane is kept for old positions,
+    while the most recent W positions keep all R planes;
+  - sentence on the 64-position window: when W is no shorter than the draft
+    block, a block's verification result cannot depend on the other blocks
+    of its batch.
 * LoopSpec summary (rit.work blog, "pipelined looped transformers"): branches
   at different recurrent depths are processed in one batched call; a rejected
   branch is dropped and decoding rolls back to the confirmed prefix.
@@ -38,7 +39,6 @@ layout invariants, closed-form fixtures in tests/golden/).
 """
 from __future__ import annotations
 
-import math
 from typing import Dict, Iterable, List, Sequence, Tuple
 
 import numpy as np
@@ -250,7 +250,7 @@ def fill_prefix(cache: LogicalCache, b: int, T: int, plane_values) -> None:
 
 
 # ---------------------------------------------------------------------------
-# commit (RIPE abstract: the window of recent positions is kept at full depth;
+# commit (RIPE abstract, sentence introducing RIPE: recent positions hold every plane;
 # LoopSpec summary: rejected continuations are dropped, accepted ones kept)
 # ---------------------------------------------------------------------------
 def commit(cache: LogicalCache, n_accept: Sequence[int], src_row: Sequence[int],
@@ -417,8 +417,3 @@ def memory_positions(layout, R: int, W: int, T: int) -> int:
     if layout == DEEPEST:
         return T
     return T + min(W, T) * (R - 1)
-
-
-def softmax_ln(x: Sequence[float]) -> float:
-    """log(sum(exp(x))) by the textbook formula (used by pins)."""
-    return math.log(sum(math.exp(v) for v in x))

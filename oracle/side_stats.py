@@ -8,8 +8,9 @@ and this module imports nothing from the library.
 Source: RIPE abstract (zhuanzhiai.com paper page, abstract paragraph).
 Whether the deepest plane alone is enough depends on how close the late
 planes already are to it; on one of the two models a small set of positions
-(1%) carries most of the error of storing only the deepest plane, and a window
-of recent positions kept at full depth removes most of those tail positions.
+(1%) carries most of the error of storing only the deepest plane, and keeping
+every plane for a short window of the newest positions removes most of those
+tail positions.
 
 Reading (the pages name the error without defining it): the error that
 storing plane R instead of plane r at prefix position j introduces into the

@@ -35,6 +35,7 @@ using namespace ripe;
 constexpr int64_t kMaxBytes = int64_t(1) << 50;   // sanity bound on any buffer size
 constexpr int64_t kMaxCommitItems = int64_t(1) << 30;  // commit work items per launch
 constexpr int kMaxCQ = 32;                        // query columns per verify work-group
+constexpr int kMaxSplit = 8192;                   // longest piece (positions)
 
 int elem_bytes(int dtype) { return dtype == RIPE_F32 ? 4 : 2; }
 
@@ -51,7 +52,6 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Partials start 256 bytes into the workspace.
 constexpr int64_t kWsHeader = 256;
-
 
 int ring_width(const ripe_desc_t& d) {
   if (d.layout != RIPE_LAYOUT_RIPE) return 0;
@@ -71,7 +71,7 @@ int split_len(const ripe_desc_t& d) {
   int64_t s = std::max<int64_t>(1024, (work + 1023) / 1024);
   s = std::min<int64_t>(s, std::max<int64_t>(256, (work + 447) / 448));
   s = (s + 31) / 32 * 32;
-  return int(std::min<int64_t>(std::max<int64_t>(s, 256), 8192));
+  return int(std::min<int64_t>(std::max<int64_t>(s, 256), kMaxSplit));
 }
 
 // Near-equal pieces of at most S positions (multiples of 32 but the last).
@@ -111,7 +111,11 @@ ripe_status_t check_desc(const ripe_desc_t* d) {
     return RIPE_EINVAL;
   if (d->page_len > 0 && d->n_pages < 1) return RIPE_EINVAL;
   if (d->n_q_heads % d->n_kv_heads != 0) return RIPE_EINVAL;
-  if (d->R > 127 || d->batch > 65535) return RIPE_EUNSUPPORTED;
+  // plan records narrow these to 16 bits (sequence index, KV head) and cut
+  // pieces of at most split_len positions, whose byte extents feed 32-bit
+  // buffer resources
+  if (d->R > 127 || d->batch > 65535 || d->n_kv_heads > 65535 || d->split_len > kMaxSplit)
+    return RIPE_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return RIPE_EUNSUPPORTED;
   if (d->t_max % 32 != 0 || d->split_len % 32 != 0) return RIPE_EUNSUPPORTED;
   if (d->page_len > 0 && (d->page_len % 32 != 0 || d->t_max % d->page_len != 0)) return RIPE_EUNSUPPORTED;
@@ -311,6 +315,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       if (kp < 0) return RIPE_EINVAL;
       if (kp > 0 && (ps < 0 || int64_t(ps) + kp > n_rows)) return RIPE_ERANGE;
       if (kp > 65535) return RIPE_EUNSUPPORTED;
+      // the ring slots a parent hides are tracked in 16-bit fields
+      if (kp > 0 && ring_width(d) > 65535) return RIPE_EUNSUPPORTED;
     }
   const int nblk = d.page_len > 0 ? d.t_max / d.page_len : 0;  // block-table row length
   if (table != nullptr)

@@ -81,6 +81,32 @@ def test_bad_descriptor(field, value, status):
     assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) == status
 
 
+def test_limits_of_the_plan_records():
+    """Values the plan narrows to 16 bits, and pieces whose byte extents feed
+    32-bit buffer resources, are refused rather than wrapped."""
+    d = rp.make_desc("ripe", "bf16", 4, 64, 2, 1024, 65536, 64, 65536)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) == -4
+    d = rp.make_desc("ripe", "bf16", 4, 64, 2, 1024, 65535, 64, 65535)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) > 0
+    d = rp.make_desc("ripe", "bf16", 4, 64, 2, 16384, 8, 128, 32, split_len=8192 + 32)
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) == -4
+    d.split_len = 8192
+    assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 0) > 0
+
+
+def test_inflight_ring_wider_than_16_bits():
+    # a ring of 70016 slots: fine without a parent, refused with one in flight
+    d = rp.make_desc("ripe", "bf16", 2, 70016, 1, 70016, 1, 64, 1, max_rows=8, max_groups=1)
+    sl = np.array([100], np.int32)
+    garr = rp.pack_groups([(0, 1, 4, 4)])
+    par = np.array([[0, 4]], np.int32)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    st = binding.lib.ripe_verify_attn_inflight(
+        ctypes.byref(d), FAKE, sl.ctypes.data_as(I32P), garr.ctypes.data_as(ctypes.POINTER(rp.ripe_group_t)),
+        par.ctypes.data_as(I32P), 1, 8, 1.0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == -4
+
+
 def test_bad_kind():
     d = rp.make_desc("ripe", "bf16", 32, 64, 2, 1024, 8, 128, 32)
     assert binding.lib.ripe_layout_bytes(ctypes.byref(d), 9) == -1

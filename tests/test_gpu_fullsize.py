@@ -163,13 +163,16 @@ def test_c4_full_size_mixed_depths_and_commit():
     run_and_check(case, desc, cache, oc, groups, sample, sl2, "c4 after commit")
 
 
-@pytest.mark.parametrize("layout", ["ripe", "full"])
+@pytest.mark.parametrize("layout", ["ripe", "full", "deepest"])
 def test_c5_full_size_sampled(layout):
+    """The fixed-memory sweep at its full sizes (FULL: B=4, T=8192; RIPE and
+    DEEPEST: B=64, T~U[4096, 8192]), one call over the whole batch, sampled
+    sequences at depths 1, 16 and 32 against the oracle."""
     case = make_case("c5", layout=layout)
     t_max = t_max_of(case)
     desc = bench_desc(case, layout, t_max)
     sample = {0, case.B - 1} | ({int(np.argmax(case.seq_len))} if case.B > 4 else set())
-    depths = (1, 32)
+    depths = (1, 16, 32)
     cache, oc = fill(case, layout, desc, t_max, sample, planes=set(depths) if layout == "full" else None)
     sl = case.seq_len.astype(np.int32)
     for r in depths:

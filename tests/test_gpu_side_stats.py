@@ -63,7 +63,10 @@ def oracle_kappa(oc, groups, case):
     return res
 
 
-def run(case, groups, tag="", check_out=True):
+def run(case, groups, tag="", check_out=True, definition=False):
+    """ripe_position_error against the oracle: its rank-one form, or with
+    ``definition`` the definition itself (one attention per substituted
+    position; small inputs only)."""
     print(f"[case] {tag} {case.dtype} T={list(case.seq_len)[:6]} groups={len(groups)}", flush=True)
     planes = {g.depth for g in groups} | {case.R}
     oc = oracle_cache(case, "full", planes=planes)
@@ -81,7 +84,8 @@ def run(case, groups, tag="", check_out=True):
     torch.cuda.synchronize()
     e = err.cpu().numpy().astype(np.float64)
     kg = cond.cpu().numpy().astype(np.float64)
-    ref = ss.position_error_rank1(oc, groups, case.q, case.kv_new, case.scale, case.Hq)
+    form = ss.position_error if definition else ss.position_error_rank1
+    ref = form(oc, groups, case.q, case.kv_new, case.scale, case.Hq)
     kap = oracle_kappa(oc, groups, case)
     n_ill = n_pos = 0
     for gi, (g, want, kj) in enumerate(zip(groups, ref, kap)):
@@ -114,6 +118,25 @@ def run(case, groups, tag="", check_out=True):
         assert np.abs(o - o_ref[rows]).max() <= O_TOL[case.dtype] * vmax, tag
         assert np.abs(ls - l_ref[rows]).max() <= LSE_TOL, tag
     return e, ref, kap
+
+
+def test_against_the_definition_fp32():
+    """The definition (one full attention per substituted position), not the
+    rank-one identity the kernel evaluates: c1's shape, groups at three
+    depths."""
+    case = make_case("c1", layout="full", k=12)  # fp32, R=4, Hkv=Hq=4, D=64, T=128
+    groups = [Group(0, 1, 0, 4), Group(0, 2, 4, 5), Group(0, 4, 9, 3)]
+    run(case, groups, tag="c1 definition", definition=True)
+
+
+@pytest.mark.parametrize("convention", ["workload", "pages"])
+def test_against_the_definition_c2_shape(convention):
+    """The definition on c2's structure (bf16, R=32, 1% tail positions with 8x
+    plane noise, k=8), reduced to T=200 and 4 heads, at depths 4 and 28."""
+    case = make_case("c2", layout="full", T_range=(200, 200), Hkv=4, Hq=4, convention=convention)
+    for r in (4, 28):
+        _, _, kap = run(case, case.groups_at(r), tag=f"c2 definition {convention} r={r}", definition=True)
+        assert set(np.nonzero(kap[0] > 1.0)[0]) <= set(case.planes.tail[0].tolist())
 
 
 def test_fp32_groups_at_several_depths():

@@ -1,9 +1,9 @@
 """Seeded synthetic workloads shaped like the RIPE pages' looped-model caches.
 
-The pages (RIPE abstract on zhuanzhiai.com, "A looped language model runs one
-block of layers R times per token ...") describe a cache with R K/V planes per
-recurrent layer whose planes approach the deepest one geometrically (0.88 per
-loop on Huginn, 0.81 on Raven).  The five workloads below restate the
+The RIPE abstract (zhuanzhiai.com paper page, opening and second sentences)
+describes a looped model whose KV cache keeps one K/V plane per loop of each
+recurrent layer, R planes in all, and reports that the planes close in on the
+deepest one by a constant factor per loop (0.88 on Huginn, 0.81 on Raven).  The five workloads below restate the
 benchmark configurations c1..c5 of this repository; the values are synthetic:
 
 * deepest plane K_R, V_R ~ N(0, 1);
