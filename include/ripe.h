@@ -220,6 +220,32 @@ ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const
                                size_t workspace_bytes, void* stream);
 
 /*
+ * ripe_verify_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call the allocator,
+ * harnesses that forbid allocation.  Arguments, checks and results are those
+ * of ripe_verify_attn, without the workspace: the split partials live in a
+ * static device array of RIPE_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (about 32.5 MiB), one copy per GPU, held until the process ends.  The
+ * call allocates nothing, with no hipMalloc, hipFree or allocating library
+ * routine.  The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress, with the device current); a failed lookup returns
+ * RIPE_EHIP.  The size covers the largest launch any call makes, so no
+ * valid call is refused for scratch.  If a launch needed more, the call
+ * would return RIPE_EWORKSPACE before launching anything.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's partials; nothing in it needs clearing.  Calls that overlap on one
+ * GPU, e.g. on two streams without ordering, race on the array and give
+ * undefined results.  Order them on one stream, or use ripe_verify_attn
+ * with a workspace each.
+ */
+#define RIPE_NOALLOC_SCRATCH_BYTES 34078976
+ripe_status_t ripe_verify_attn_noalloc(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
+                                       const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
+                                       float softmax_scale, const void* q, const void* kv_new, void* out,
+                                       float* lse, int8_t* plane_sel, void* stream);
+
+/*
  * Verification while each group's parent block is still in flight (LoopSpec
  * summary: the computation of the next position starts from an early draft
  * before the current one is confirmed).  As ripe_verify_attn, with

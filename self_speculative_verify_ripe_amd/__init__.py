@@ -8,4 +8,5 @@ from .binding import (DTYPES, LAYOUTS, RIPE_BF16, RIPE_BYTES_CACHE,  # noqa: F40
                       RIPE_LAYOUT_RIPE, STATUS, RipeError, make_desc, ripe_commit, ripe_desc_t,
                       ripe_group_t, ripe_layout_bytes, ripe_verify_attn, pack_groups, new_workspace,
                       ripe_accept_desc_t, make_accept_desc, ripe_accept_workspace_bytes, ripe_accept,
-                      commit_args, pack_parents, ripe_position_error, RIPE_BYTES_POSERR_WORKSPACE)
+                      commit_args, pack_parents, ripe_position_error, RIPE_BYTES_POSERR_WORKSPACE,
+                      ripe_verify_attn_noalloc)

@@ -63,6 +63,10 @@ def _load():
                                      ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ripe_verify_attn.restype = ctypes.c_int
+    lib.ripe_verify_attn_noalloc.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
+                                             ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, P, P, P, P, P, P]
+    lib.ripe_verify_attn_noalloc.restype = ctypes.c_int
     lib.ripe_verify_attn_inflight.argtypes = [ctypes.POINTER(ripe_desc_t), P, ctypes.POINTER(ctypes.c_int32),
                                               ctypes.POINTER(ripe_group_t), ctypes.POINTER(ctypes.c_int32),
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P, P, P, P, P,
@@ -237,6 +241,22 @@ def ripe_verify_attn(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: I
         what = "ripe_verify_attn_inflight"
     if st != 0:
         raise RipeError(st, what)
+
+
+def ripe_verify_attn_noalloc(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,
+                             n_rows: int, softmax_scale: float, q, kv_new, out, lse=None, plane_sel=None,
+                             stream=None) -> None:
+    """ripe_verify_attn without a workspace: the split partials use the
+    library's static device scratch (asynchronous on ``stream``; calls that
+    overlap on one GPU race on that scratch)."""
+    sl = _i32(seq_len, desc.batch)
+    gptr, ng, _keep = _groups(groups)
+    st = lib.ripe_verify_attn_noalloc(ctypes.byref(desc), _ptr(cache),
+                                      sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), gptr, ng,
+                                      int(n_rows), float(softmax_scale), _ptr(q), _ptr(kv_new), _ptr(out),
+                                      _ptr(lse), _ptr(plane_sel), _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_verify_attn_noalloc")
 
 
 def ripe_position_error(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups: Iterable,

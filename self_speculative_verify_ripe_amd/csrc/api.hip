@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "accept.h"
@@ -52,6 +53,45 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Partials start 256 bytes into the workspace.
 constexpr int64_t kWsHeader = 256;
+
+// ---- the static scratch of ripe_verify_attn_noalloc ----------------------
+// The largest workspace one verify launch uses: the header and kMaxItems
+// partials of 32 query columns x (D + 2) floats at the largest head
+// dimension, D = 128.
+// Calls are cut into launches of at most kMaxItems items, so every verify
+// call fits.  Each GPU the library runs on holds its own copy until the
+// process ends.
+constexpr size_t kStaticWsBytes = size_t(kWsHeader) + size_t(kMaxItems) * 32 * (128 + 2) * 4;
+static_assert(kStaticWsBytes == RIPE_NOALLOC_SCRATCH_BYTES, "ripe.h states the scratch size");
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each device holds its own copy; in host
+// code the array's name is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ripe_status_t static_scratch(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "ripe_verify_attn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return RIPE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t s = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (s != hipSuccess) return hip_status(s, "ripe_verify_attn_noalloc: hipGetSymbolAddress");
+    if (p == nullptr) return RIPE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RIPE_OK;
+}
 
 int ring_width(const ripe_desc_t& d) {
   if (d.layout != RIPE_LAYOUT_RIPE) return 0;
@@ -235,13 +275,15 @@ extern "C" int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind) {
 
 // Every verify entry point.  parents: host [n_groups][2] (row_start, n_rows)
 // of each group's in-flight parent block, or nullptr for none.  table: the
-// block table of a paged cache (nullptr for an unpaged one).
+// block table of a paged cache (nullptr for an unpaged one).  static_ws: use
+// the static scratch instead of the caller's workspace (looked up after every
+// check has passed, right before the first launch).
 static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, const int32_t* table,
                           const int32_t* seq_len,
                           const ripe_group_t* groups, const int32_t* parents, int32_t n_groups, int32_t n_rows,
                           float softmax_scale, const void* q, const void* kv_new, void* out, float* lse,
                           int8_t* plane_sel, void* workspace, size_t workspace_bytes, void* stream,
-                          bool out_f32 = false) {
+                          bool out_f32 = false, bool static_ws = false) {
   ripe_status_t st = check_desc(desc);
   if (st != RIPE_OK) return st;
   const ripe_desc_t& d = *desc;
@@ -254,7 +296,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
   if (cache == nullptr || q == nullptr || kv_new == nullptr || out == nullptr) return RIPE_EINVAL;
   if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(kv_new, 16) || !aligned(out, 16)) return RIPE_EINVAL;
   if ((lse && !aligned(lse, 4)) || (plane_sel && !aligned(plane_sel, 16))) return RIPE_EINVAL;
-  if (workspace && !aligned(workspace, 256)) return RIPE_EINVAL;
+  if (!static_ws && workspace && !aligned(workspace, 256)) return RIPE_EINVAL;
   for (int b = 0; b < d.batch; ++b)
     if (seq_len[b] < 0 || seq_len[b] > d.t_max) return RIPE_ERANGE;
   const int G = d.n_q_heads / d.n_kv_heads;
@@ -274,8 +316,18 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
   };
   auto launch_all = [&](int NB) -> ripe_status_t {
+    if (static_ws) {
+      const ripe_status_t s = static_scratch(&workspace);
+      if (s != RIPE_OK) return s;
+      workspace_bytes = kStaticWsBytes;
+    }
     for (int pi = 0; pi < sc.n_plans; ++pi)
-      if (workspace == nullptr || size_t(sc.plans[pi].part_bytes) > workspace_bytes) return RIPE_EWORKSPACE;
+      if (workspace == nullptr || size_t(sc.plans[pi].part_bytes) > workspace_bytes) {
+        if (static_ws && std::getenv("RIPE_DEBUG") != nullptr)
+          std::fprintf(stderr, "[ripe] ripe_verify_attn_noalloc: a launch needs %lld bytes of scratch, more than %zu\n",
+                       (long long)sc.plans[pi].part_bytes, kStaticWsBytes);
+        return RIPE_EWORKSPACE;
+      }
     for (int pi = 0; pi < sc.n_plans; ++pi) {
       LaunchPlan& lp = sc.plans[pi];
       set_pointers(lp.p);
@@ -597,6 +649,15 @@ extern "C" ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* c
                                           size_t workspace_bytes, void* stream) {
   return verify_impl(desc, cache, nullptr, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q, kv_new,
                      out, lse, plane_sel, workspace, workspace_bytes, stream);
+}
+
+extern "C" ripe_status_t ripe_verify_attn_noalloc(const ripe_desc_t* desc, const void* cache,
+                                                  const int32_t* seq_len, const ripe_group_t* groups,
+                                                  int32_t n_groups, int32_t n_rows, float softmax_scale,
+                                                  const void* q, const void* kv_new, void* out, float* lse,
+                                                  int8_t* plane_sel, void* stream) {
+  return verify_impl(desc, cache, nullptr, seq_len, groups, nullptr, n_groups, n_rows, softmax_scale, q, kv_new,
+                     out, lse, plane_sel, nullptr, 0, stream, false, true);
 }
 
 extern "C" ripe_status_t ripe_verify_attn_inflight(const ripe_desc_t* desc, const void* cache,

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_commit_paged",
                      "ripe_layout_bytes", "ripe_position_error", "ripe_verify_attn", "ripe_verify_attn_inflight",
-                     "ripe_verify_attn_paged"]
+                     "ripe_verify_attn_noalloc", "ripe_verify_attn_paged"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
