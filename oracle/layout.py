@@ -5,17 +5,20 @@ declares, used to build device buffers for parity tests and to compare the
 buffers the commit kernel writes, byte for byte.  It shares no code with the
 library (which computes addresses in C++).
 
-Layout (E = element bytes, T = t_max, a multiple of 32; We = min(W, T);
-BW = min(32, We)); the K region comes first, then the V region:
+Layout (E = element bytes, T = t_max, a multiple of 32; We = min(W, T));
+the K region comes first, then the V region:
 
 * FULL     K [B][R][Hkv][T][D]              V [B][R][Hkv][T/32][D][32]
 * DEEPEST  K [B][Hkv][T][D]                 V [B][Hkv][T/32][D][32]
 * RIPE     K deep [B][Hkv][T][D]            V deep [B][Hkv][T/32][D][32]
-             then ring [B][R-1][Hkv][We][D]   then ring [B][R-1][Hkv][We/BW][D][BW]
+             then ring [B][R-1][Hkv][We][D]   then ring [B][R-1][Hkv][We*D] (below)
 
 V is stored transposed in blocks of 32 positions (each head dimension's 32
-values contiguous).  Plane p is stored at index p - 1 (plane R deepest);
-RIPE keeps position j's planes 1..R-1 in ring slot j mod We.
+values contiguous).  A ring's V of one (sequence, plane, head) holds its We
+slots as floor(We/32) such blocks [D][32] followed, when We is not a
+multiple of 32, by one narrower block [D][We mod 32] (``ring_v_offset``).
+Plane p is stored at index p - 1 (plane R deepest); RIPE keeps position j's
+planes 1..R-1 in ring slot j mod We.
 
 Paged caches (page length P, N pages): the main region becomes a pool,
 K [N][planes][Hkv][P][D] and V [N][planes][Hkv][P/32][D][32] (planes = R for
@@ -41,6 +44,24 @@ def ring_width(W: int, t_max: int) -> int:
     return min(max(W, 0), t_max)
 
 
+def ring_v_offset(slot: int, d: int, We: int, D: int) -> int:
+    """Element offset of V (ring slot, head dimension d) within one
+    (sequence, plane, head) ring of We slots: blocks of 32 slots stored
+    [D][32], the last We mod 32 slots as one block [D][We mod 32]."""
+    if not (0 <= slot < We and 0 <= d < D):
+        raise IndexError((slot, d))
+    full = (We // 32) * 32
+    if slot < full:
+        return (slot // 32) * 32 * D + d * 32 + slot % 32
+    w = We - full
+    return full * D + d * w + (slot - full)
+
+
+def ring_v_offsets(We: int, D: int) -> np.ndarray:
+    """ring_v_offset for every (slot, d): int array [We, D]."""
+    return np.array([[ring_v_offset(s, d, We, D) for d in range(D)] for s in range(We)], dtype=np.int64)
+
+
 def layout_elements(layout, R: int, W: int, B: int, t_max: int, Hkv: int, D: int) -> int:
     """Elements (K and V together) one recurrent layer's cache holds."""
     layout = layout_code(layout)
@@ -60,8 +81,9 @@ def layout_bytes(layout, dtype: str, R: int, W: int, B: int, t_max: int, Hkv: in
 def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, Hkv: int,
                   D: int):
     """Named array views of a flat element buffer: K and V of the main region
-    (FULL planes or the deep plane) and, for RIPE, of the ring.  V views are
-    blocked: [..., n/width, D, width]."""
+    (FULL planes or the deep plane) and, for RIPE, of the ring.  Main V views
+    are blocked [..., n/32, D, 32]; the ring V view is [B, R-1, Hkv, We*D],
+    indexed through ring_v_offsets."""
     layout = layout_code(layout)
     T = t_max
     if layout == FULL:
@@ -71,7 +93,7 @@ def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: 
     We = ring_width(W, T) if layout == RIPE else 0
     parts = [("main", main, 32)]
     if We > 0:
-        parts.append(("ring", (B, R - 1, Hkv, We, D), min(32, We)))
+        parts.append(("ring", (B, R - 1, Hkv, We, D), None))
     views = {}
     off = 0
     for kind in ("K", "V"):
@@ -80,6 +102,8 @@ def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: 
             flat = buf_elems[off:off + n]
             if kind == "K":
                 views[(kind, name)] = flat.reshape(shp)
+            elif w is None:
+                views[(kind, name)] = flat.reshape(*shp[:3], shp[3] * shp[4])
             else:
                 *lead, nn, dd = shp
                 views[(kind, name)] = flat.reshape(*lead, nn // w, dd, w)
@@ -127,7 +151,7 @@ def encode(cache: LogicalCache) -> np.ndarray:
             vd[...] = np.where(hb[None, :, None, :], vblk, vd)
     if cache.layout == RIPE and ("K", "ring") in views:
         We = ring_width(cache.W, T)
-        BW = min(32, We)
+        voff = ring_v_offsets(We, D)
         kring, vring = views[("K", "ring")], views[("V", "ring")]
         filled = np.zeros((B, R - 1, We), dtype=bool)
         for (b, p), store in cache._sparse.items():
@@ -137,7 +161,7 @@ def encode(cache: LogicalCache) -> np.ndarray:
                     raise ValueError("two held positions share a ring slot")
                 filled[b, p - 1, s] = True
                 kring[b, p - 1, :, s] = _bits(k, cache.dtype)
-                vring[b, p - 1, :, s // BW, :, s % BW] = _bits(v, cache.dtype)
+                vring[b, p - 1][:, voff[s]] = _bits(v, cache.dtype)
     return buf.view(np.uint8)
 
 
@@ -170,13 +194,13 @@ def decode(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: i
             cache.put_range(b, p, 0, k, v)
         if layout == RIPE and ("K", "ring") in views:
             We = ring_width(W, T)
-            BW = min(32, We)
+            voff = ring_v_offsets(We, D)
             kring, vring = views[("K", "ring")], views[("V", "ring")]
             for p in range(1, R):
                 for j in range(max(0, Tb - W), Tb):
                     s = j % We
                     cache.put(b, p, j, val(kring[b, p - 1, :, s]),
-                              val(vring[b, p - 1, :, s // BW, :, s % BW]))
+                              val(vring[b, p - 1][:, voff[s]]))
     return cache
 
 
@@ -206,7 +230,7 @@ def _pool_views(elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, H
         if We > 0:
             flat = elems[off:off + n_ring]
             views[(kind, "ring")] = flat.reshape(ring) if kind == "K" else \
-                flat.reshape(B, R - 1, Hkv, We // min(32, We), D, min(32, We))
+                flat.reshape(B, R - 1, Hkv, We * D)
             off += n_ring
     assert off == elems.size
     return views

@@ -139,7 +139,7 @@ def test_verify_after_commit_equals_verify_on_filled_cache():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("W", [0, 8, 16, 64, 96, 500])
+@pytest.mark.parametrize("W", [0, 1, 3, 4, 5, 8, 12, 16, 40, 64, 70, 96, 500])
 def test_encode_size_and_round_trip(layout, dtype, W):
     R, B, t_max, Hkv, D = 3, 2, 96, 2, 8
     planes = PlaneModel(11, R, Hkv, D, 0.88, dtype)
@@ -154,6 +154,44 @@ def test_encode_size_and_round_trip(layout, dtype, W):
     assert buf.size == 2 * B * Hkv * D * per_seq * E
     back = lay.decode(buf, layout, dtype, R, W, B, t_max, Hkv, D, lengths)
     assert back.same_contents(c)
+
+
+@pytest.mark.parametrize("We,slot,d,want", [
+    # D = 4.  Windows that are multiples of 32: blocks [D][32] only.
+    (32, 5, 2, 2 * 32 + 5), (64, 37, 1, 32 * 4 + 1 * 32 + 5),
+    # windows below 32: one block [D][We]
+    (8, 3, 3, 3 * 8 + 3), (12, 7, 3, 3 * 12 + 7), (1, 0, 2, 2), (5, 4, 1, 1 * 5 + 4),
+    # 32-slot blocks, then a narrower block [D][We mod 32] for the last slots
+    (40, 35, 2, 32 * 4 + 2 * 8 + 3), (40, 31, 3, 3 * 32 + 31), (100, 70, 1, 2 * 32 * 4 + 1 * 32 + 6),
+    (100, 99, 3, 96 * 4 + 3 * 4 + 3), (70, 64, 0, 64 * 4),
+])
+def test_ring_v_offsets_hand_computed(We, slot, d, want):
+    """The ring's V offsets written out by hand for the block rule the
+    layout statement gives (blocks of 32 slots, then the remaining slots as
+    one narrower block)."""
+    assert lay.ring_v_offset(slot, d, We, 4) == want
+    offs = lay.ring_v_offsets(We, 4)
+    assert sorted(offs.ravel().tolist()) == list(range(We * 4))  # a permutation of the ring
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [12, 40, 100])
+def test_encoder_ring_offsets_any_window(dtype, W):
+    """A single ring element of a window that is not a multiple of 32 lands
+    where the block rule puts it, in K and V."""
+    R, B, T, H, D = 3, 2, 128, 2, 4
+    c = ro.LogicalCache("ripe", dtype, R, W, B, T, H, D)
+    b, h, d, p, j = 1, 1, 3, 2, 117
+    k = np.zeros((H, D)); v = np.zeros((H, D))
+    k[h, d], v[h, d] = 7.0, 9.0
+    c.put(b, p, j, k, v)
+    buf = lay.encode(c)
+    n_k = lay.layout_elements("ripe", R, W, B, T, H, D) // 2
+    deep = B * H * T * D
+    slot = j % W
+    head = ((b * (R - 1) + (p - 1)) * H + h) * W * D
+    assert _elem(buf, dtype, deep + head + slot * D + d) == 7.0
+    assert _elem(buf, dtype, n_k + deep + head + lay.ring_v_offset(slot, d, W, D)) == 9.0
 
 
 def _elem(buf, dtype, index):

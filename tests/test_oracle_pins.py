@@ -227,26 +227,29 @@ def test_window_positions():
     check_window_count()
 
 
-def test_batched_equals_alone():
+@pytest.mark.parametrize("W", [1, 3, 4, 5, 8, 12, 40, 100])
+def test_batched_equals_alone(W):
     case = small_c3()
     groups = case.groups_at(2)
-    out, lse, sels = verify_case(case, "ripe", case.W, groups)
+    out, lse, sels = verify_case(case, "ripe", W, groups)
     for g, sel in zip(groups, sels):
-        o1, l1, s1 = verify_case(case, "ripe", case.W, [g])
+        o1, l1, s1 = verify_case(case, "ripe", W, [g])
         rows = slice(g.row_start, g.row_start + g.n_rows)
         assert np.array_equal(out[rows], o1[rows]) and np.array_equal(lse[rows], l1[rows])
         assert np.array_equal(sel, s1[0])
 
 
-def test_mixed_depth_branches_are_siblings():
+@pytest.mark.parametrize("W", [4, 64])
+def test_mixed_depth_branches_are_siblings(W):
     """Two branches of one sequence at different depths in one call give what
     each gives alone (LoopSpec: branches at different depths, one batched
-    call)."""
+    call); W = 4 is the branches' own length k."""
     case = make_case("c4", B=3, T_range=(50, 70), R=20, Hkv=2, Hq=4, D=8)
     groups = case.groups()
-    out, lse, _ = verify_case(case, "ripe", case.W, groups)
+    assert all(g.n_rows == 4 for g in groups)
+    out, lse, _ = verify_case(case, "ripe", W, groups)
     for g in groups:
-        o1, l1, _ = verify_case(case, "ripe", case.W, [g])
+        o1, l1, _ = verify_case(case, "ripe", W, [g])
         rows = slice(g.row_start, g.row_start + g.n_rows)
         assert np.array_equal(out[rows], o1[rows]) and np.array_equal(lse[rows], l1[rows])
 
