@@ -84,10 +84,9 @@ typedef enum {
  *  layout      ripe_layout_t
  *  dtype       ripe_dtype_t
  *  R           loops = planes, 1..127
- *  W           RIPE window in positions, >= 0 (ignored by FULL / DEEPEST).
- *              With We = min(W, t_max): We must be 0, 8, 16, 24 or a
- *              multiple of 32.  W = 0 keeps only plane R; W >= t_max keeps
- *              every plane everywhere.
+ *  W           RIPE window in positions, any W >= 0 (ignored by FULL /
+ *              DEEPEST).  W = 0 keeps only plane R; W >= t_max keeps every
+ *              plane everywhere.  The ring holds We = min(W, t_max) slots.
  *  batch       sequences B >= 1
  *  t_max       capacity per sequence, a positive multiple of 32
  *  n_kv_heads  Hkv >= 1
@@ -142,18 +141,23 @@ typedef struct ripe_group {
 
 /*
  * Byte layout of one recurrent layer's cache (E = 4 for F32, 2 for BF16;
- * T = t_max; We = min(W, T); BW = min(32, We)).  The K region comes first,
- * then the V region, with no padding:
+ * T = t_max; We = min(W, T)).  The K region comes first, then the V region,
+ * with no padding:
  *
  *   FULL     K [B][R][Hkv][T][D]            V [B][R][Hkv][T/32][D][32]
  *   DEEPEST  K [B][Hkv][T][D]               V [B][Hkv][T/32][D][32]
  *   RIPE     K deep [B][Hkv][T][D]          V deep [B][Hkv][T/32][D][32]
- *            then K ring [B][R-1][Hkv][We][D], V ring [B][R-1][Hkv][We/BW][D][BW]
+ *            then K ring [B][R-1][Hkv][We][D], V ring [B][R-1][Hkv][We*D]
  *
  * Plane p lives at index p-1.  V is stored transposed in blocks of 32
  * positions so that each head dimension's 32 values are contiguous.  RIPE
  * keeps planes 1..R-1 of position j in ring slot j mod We; the deep region
- * holds plane R of every position.  Hence the cache costs
+ * holds plane R of every position.  The V ring of one (sequence, plane,
+ * head) stores its We slots as floor(We/32) blocks [D][32], followed, when
+ * We is not a multiple of 32, by one block [D][We mod 32] holding the last
+ * slots: V of slot s, head dimension d sits at element
+ *   (s/32)*32*D + d*32 + s%32            for s < F = floor(We/32)*32,
+ *   F*D + d*(We - F) + (s - F)           otherwise.  Hence the cache costs
  *   FULL    2*B*Hkv*D*E * R*T
  *   DEEPEST 2*B*Hkv*D*E * T
  *   RIPE    2*B*Hkv*D*E * (T + We*(R-1))

@@ -160,8 +160,6 @@ ripe_status_t check_desc(const ripe_desc_t* d) {
   if (d->t_max % 32 != 0 || d->split_len % 32 != 0) return RIPE_EUNSUPPORTED;
   if (d->page_len > 0 && (d->page_len % 32 != 0 || d->t_max % d->page_len != 0)) return RIPE_EUNSUPPORTED;
   if (d->n_q_heads / d->n_kv_heads > 65535) return RIPE_EUNSUPPORTED;
-  const int We = ring_width(*d);
-  if (!(We == 0 || (We < 32 && We % 8 == 0) || We % 32 == 0)) return RIPE_EUNSUPPORTED;
   if (region_elems(*d) < 0) return RIPE_EUNSUPPORTED;
   return RIPE_OK;
 }
@@ -413,7 +411,6 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.layout = d.layout;
     p.R = d.R;
     p.We = We;
-    p.BW = We < 32 ? We : 32;
     p.t_max = d.t_max;
     p.H = d.n_kv_heads;
     p.Hq = d.n_q_heads;
@@ -855,7 +852,6 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
     p.layout = d.layout;
     p.R = d.R;
     p.We = We;
-    p.BW = We < 32 ? We : 32;
     p.t_max = d.t_max;
     p.H = d.n_kv_heads;
     p.n_rows = n_rows;

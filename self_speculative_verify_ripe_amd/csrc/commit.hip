@@ -11,7 +11,8 @@
 //
 // One thread copies 8 consecutive head-dim elements of one (row, plane,
 // head): a 16- or 32-byte K row piece, and 8 V elements into the transposed
-// 32-position V blocks.  Paged caches: the host cuts jobs at page boundaries
+// V blocks (32 positions each; a RIPE ring whose width We is not a multiple
+// of 32 ends with one block of We mod 32 slots).  Paged caches: the host cuts jobs at page boundaries
 // and gives each main-region job its page.  Destinations (position, plane, head, element) are
 // distinct across threads, so the writes never race.
 #include <hip/hip_runtime.h>
@@ -51,24 +52,24 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
   const T* ks = kv + (size_t(pl - 1) * p.n_rows + src) * Hd + size_t(h) * D + ch * 8;
   const T* vs = kv + (size_t(p.R + pl - 1) * p.n_rows + src) * Hd + size_t(h) * D + ch * 8;
   size_t off;
-  int slot, bw;
+  int slot;
+  int full = 1 << 30;  // slots held in 32-wide V blocks; the rest form one narrower block
+  int tail = 0;        // its width
   if (p.layout == 2 && pl < p.R) {
     off = p.ring_off + ((size_t(jb.b) * (p.R - 1) + (pl - 1)) * p.H + h) * size_t(p.We) * D;
     slot = j % p.We;
-    bw = p.BW;
+    full = p.We / 32 * 32;
+    tail = p.We - full;
   } else if (p.page_len > 0) {  // paged main region: the job's rows share one page
     off = (((p.layout == 0) ? size_t(jb.page) * p.R + (pl - 1) : size_t(jb.page)) * p.H + h) *
           size_t(p.page_len) * D;
     slot = j % p.page_len;
-    bw = 32;
   } else if (p.layout == 0) {
     off = ((size_t(jb.b) * p.R + (pl - 1)) * p.H + h) * size_t(p.t_max) * D;
     slot = j;
-    bw = 32;
   } else {
     off = (size_t(jb.b) * p.H + h) * size_t(p.t_max) * D;
     slot = j;
-    bw = 32;
   }
   T* kd = static_cast<T*>(p.cache_k) + off + size_t(slot) * D + ch * 8;
   constexpr int NV = 8 * sizeof(T) / 16;  // 16-byte pieces per 8 elements
@@ -79,10 +80,11 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
 #pragma unroll
   for (int v = 0; v < NV; ++v) reinterpret_cast<u32x4*>(vv)[v] = reinterpret_cast<const u32x4*>(vs)[v];
   T* vd = static_cast<T*>(p.cache_v) + off;
-  const int blk = slot / bw;
-  const int sl = slot - blk * bw;
+  // element (slot, d) of a [D][w] block that starts at slot b0: b0 * D + d * w + (slot - b0)
+  const int b0 = slot < full ? slot / 32 * 32 : full;
+  const int w = slot < full ? 32 : tail;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vd[(size_t(blk) * D + ch * 8 + e) * bw + sl] = vv[e];
+  for (int e = 0; e < 8; ++e) vd[size_t(b0) * D + size_t(ch * 8 + e) * w + (slot - b0)] = vv[e];
 }
 
 template <typename T, int D>

@@ -183,7 +183,7 @@ struct VerifyParams {
   int8_t* plane_sel;
   float* ws;             // split partials, [item][16 NB columns][D + 2]
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
-  int32_t layout, R, We, BW, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
+  int32_t layout, R, We, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
   int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
@@ -212,7 +212,7 @@ struct CommitParams {
   void* cache_v;
   const void* kv_new;
   uint64_t ring_off;
-  int32_t layout, R, We, BW, t_max, H, n_rows, n_jobs, n_items;
+  int32_t layout, R, We, t_max, H, n_rows, n_jobs, n_items;
   int32_t page_len;         // paged cache: positions per page (0: unpaged)
   CommitJob job[kMaxJobs];  // a RIPE job with plane_lo < R writes the ring
 };

@@ -80,12 +80,18 @@ struct Op<__bf16> {
     return static_cast<float>(static_cast<const __bf16*>(base)[idx]);
   }
   __device__ static inline void put_elem(u32x4 (&v)[VCH], int e, const void* base, size_t idx) {
-    const uint16_t bits = static_cast<const uint16_t*>(base)[idx];
+    put_bits(v, e, static_cast<const uint16_t*>(base)[idx]);
+  }
+  __device__ static inline void put_bits(u32x4 (&v)[VCH], int e, uint32_t bits) {
     const int w = e >> 1;
     if (e & 1)
-      v[0][w] = (v[0][w] & 0x0000FFFFu) | (uint32_t(bits) << 16);
+      v[0][w] = (v[0][w] & 0x0000FFFFu) | (bits << 16);
     else
-      v[0][w] = (v[0][w] & 0xFFFF0000u) | uint32_t(bits);
+      v[0][w] = (v[0][w] & 0xFFFF0000u) | (bits & 0xFFFFu);
+  }
+  // one element through a buffer resource (0 past its end)
+  __device__ static inline uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
   }
 };
 
@@ -129,6 +135,10 @@ struct Op<float> {
   }
   __device__ static inline void put_elem(u32x4 (&v)[VCH], int e, const void* base, size_t idx) {
     v[e >> 2][e & 3] = static_cast<const uint32_t*>(base)[idx];
+  }
+  __device__ static inline void put_bits(u32x4 (&v)[VCH], int e, uint32_t bits) { v[e >> 2][e & 3] = bits; }
+  __device__ static inline uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
 };
 
@@ -326,7 +336,10 @@ constexpr int verify_lds_bytes() {
 // (read from that page), 2 when pieces may span pages (such a piece is read
 // step by step: each 32-position step lies inside one page); 0 unpaged.  The
 // step-by-step code is compiled only into PG = 2, whose loop it slows.
-template <typename T, int D, int NB, bool INF, int PG = 0>
+// RT: the RIPE ring's last V block (We mod 32 slots) is too narrow for
+// 16-byte loads of 8 slots, so its step is read one element at a time; the
+// code is compiled only into the launches whose window needs it.
+template <typename T, int D, int NB, bool INF, int PG = 0, bool RT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
 void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
@@ -412,7 +425,9 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     // The buffer resources span the piece only: loads past its end return
     // zeros.
     size_t off;
-    int bw = kStep;
+    // slots from the piece's start to the end of the region's V blocks: the
+    // ring's last block is narrower when We is not a multiple of 32
+    int vlim = 1 << 30;
     // a paged prefix-plane piece inside one page is addressed like an
     // unpaged one; one that spans pages is read step by step (below)
     const int P = PG > 0 ? p.page_len : 1;
@@ -431,12 +446,12 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
             size_t(pc.c0) * D;
     } else {
       off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D +
-            size_t(pc.c0) * D;  // c0 is a multiple of 32, and of the ring's block width
-      bw = p.BW;
+            size_t(pc.c0) * D;  // c0 is a multiple of 32: a V block starts there
+      vlim = p.We - pc.c0;
     }
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.cache_k) + off, uint32_t(pc.len) * D * E);
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(static_cast<const T*>(p.cache_v) + off, uint32_t(ceil_div(pc.len, bw)) * bw * D * E);
+        make_rsrc(static_cast<const T*>(p.cache_v) + off, uint32_t(min(ceil_div(pc.len, kStep) * kStep, vlim)) * D * E);
     const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
     const uint32_t koff = (krow * D + lg * VEC) * E;
     // A step past the piece maps to an offset beyond the resource's range:
@@ -460,19 +475,36 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
 #pragma unroll
         for (int c = 0; c < KC; ++c) k[mb][c] = bload16(rs, base + (4 * mb * D + c * 4 * VEC) * E);
     };
+    // The step's V block holds w slots [D][w] (w = 32 but for a ring's last
+    // block); lane group lg takes slots 8 lg .. 8 lg + 7 of head dimension
+    // ln + 16 db.
     auto load_v = [&](int st, bool live, u32x4 (&v)[DB][VCH]) {
       __amdgpu_buffer_rsrc_t rs = vrs;
-      const int slot0 = st * kStep + 8 * lg;
-      const int blk = slot0 / bw;
-      uint32_t base = live ? uint32_t((blk * D + ln) * bw + (slot0 - blk * bw)) * E : kOutOfRange;
-      if (PG == 2 && per_step) {  // bw = 32: the step is one whole V block
+      const int w = min(kStep, vlim - st * kStep);
+      uint32_t base = live ? uint32_t(st * kStep * D + ln * w + 8 * lg) * E : kOutOfRange;
+      if (PG == 2 && per_step) {  // w = 32: the step is one whole V block
         rs = make_rsrc(static_cast<const T*>(p.cache_v) + step_base(st), uint32_t(kStep) * D * E);
         base = live ? uint32_t(ln * kStep + 8 * lg) * E : kOutOfRange;
+      }
+      if (RT && live && (w * E) % 16 != 0) {
+        // a narrow block whose rows are not 16-byte aligned: element loads
+        // (slots past w read as zero and are masked below anyway)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int c = 0; c < VCH; ++c) v[db][c] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t o = (8 * lg + e < w) ? base + uint32_t(16 * db * w + e) * E : kOutOfRange;
+            O::put_bits(v[db], e, O::bload_elem(rs, o));
+          }
+        }
+        return;
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) v[db][c] = bload16_stream(rs, base + (16 * db * bw + c * VEC) * E);
+        for (int c = 0; c < VCH; ++c) v[db][c] = bload16_stream(rs, base + (16 * db * w + c * VEC) * E);
     };
     const bool hole = INF && pc.kind == kSegRing && sr.hole > 0;
     // first step's loads go out before the query setup
@@ -774,14 +806,23 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
   if (p.n_wg <= 0) return hipSuccess;
   const int grid = p.n_blocks;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  const void* const kerns[2][3] = {
-      {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0>),
-       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1>),
-       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2>)},
-      {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0>),
-       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1>),
-       reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2>)}};
-  const void* kern = kerns[p.inflight ? 1 : 0][p.page_mode];
+  const void* const kerns[2][2][3] = {
+      {{reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2>)},
+       {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2>)}},
+      {{reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0, true>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1, true>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2, true>)},
+       {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0, true>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1, true>),
+        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2, true>)}}};
+  // element loads for the ring's last V block only where its rows are not
+  // 16-byte aligned
+  const bool rt = p.layout == 2 && ((p.We % kStep) * int(sizeof(T))) % 16 != 0;
+  const void* kern = kerns[rt ? 1 : 0][p.inflight ? 1 : 0][p.page_mode];
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
   // Merge: 64-wide head-dim slices while they still give one work-group per

@@ -43,7 +43,7 @@ def test_struct_sizes_match_header():
 
 @pytest.mark.parametrize("layout", ["full", "deepest", "ripe"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("W", [0, 8, 16, 24, 32, 64, 96, 4096, 100000])
+@pytest.mark.parametrize("W", [0, 1, 3, 4, 5, 8, 12, 16, 24, 32, 40, 64, 96, 100, 4096, 100000])
 def test_cache_bytes_closed_form(layout, dtype, W):
     R, B, T, H, D = 32, 3, 1024, 8, 128
     d = rp.make_desc(layout, dtype, R, W, B, T, H, D, 32)
@@ -72,7 +72,7 @@ def test_workspace_bound_positive():
 @pytest.mark.parametrize("field,value,status", [
     ("layout", 3, -1), ("dtype", 7, -1), ("R", 0, -1), ("W", -1, -1), ("batch", 0, -1),
     ("t_max", 0, -1), ("n_kv_heads", 0, -1), ("n_q_heads", 12, -1), ("head_dim", 96, -4),
-    ("t_max", 100, -4), ("W", 40, -4), ("R", 200, -4), ("split_len", 48, -4),
+    ("t_max", 100, -4), ("R", 200, -4), ("split_len", 48, -4),
     ("split_len", -32, -1),
 ])
 def test_bad_descriptor(field, value, status):

@@ -33,7 +33,7 @@ def draw(seed):
         Hkv=int(rng.integers(1, 4)),
         G=int(rng.choice([1, 2, 4, 5])),
         R=int(rng.choice([1, 3, 6])),
-        W=int(rng.choice([0, 8, 16, 24, 32, 64, 160])),
+        W=int(rng.choice([0, 3, 8, 12, 16, 24, 32, 40, 64, 100, 160])),
         B=int(rng.integers(1, 7)),
         k=int(rng.integers(2, 13)),
         split_len=int(rng.choice([0, 32, 64, 96])),
