@@ -120,6 +120,9 @@ inline int piece_len(int len, int S) {
   return ((len + n - 1) / n + kStep - 1) / kStep * kStep;
 }
 
+// Rings of at most this many slots join their depth's anchor part (plan.h).
+constexpr int kFold = 4 * kStep;
+
 // Positions of the main region (FULL: per plane; otherwise the deep plane):
 // t_max per sequence, or the page pool of a paged cache.
 long double main_positions(const ripe_desc_t& d) {
@@ -223,14 +226,22 @@ int compute_units() {
   return n;
 }
 
+// One part of a sequence's plan: runs [first, first + n_run) of its run
+// list, the first n_stream of them streamed from the cache.
+struct PartRec {
+  int first, n_stream, n_run, steps;
+};
+
 struct VerifyScratch {
   std::vector<std::pair<int, int>> spans;
-  std::vector<int> count, fill, order;
+  std::vector<int> count, fill, order, seg_last;
+  std::vector<std::vector<Piece>> part_runs;
   std::vector<Seg> segs;
   std::vector<Piece> pieces;
+  std::vector<PartRec> parts;
   std::vector<Item> items;
   std::vector<int> cost, by_size;
-  std::vector<WgCost> long_wg, solo_wg, wgs;
+  std::vector<WgCost> wgs;
   std::vector<LaunchPlan> plans;
   int n_plans = 0;
   // The inputs the plans above were built from (pointers aside).  A call
@@ -454,34 +465,115 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       if (kp == 0) ps = 0;
     }
     const InFlight fl = in_flight(d.layout, We, T, kp);
-    // pieces of this sequence: every segment cut into near-equal runs of at
-    // most S positions.  Paged caches: with pages of at least S positions a
-    // prefix-plane segment is first cut at page boundaries (every piece then
-    // lies in one page); with shorter pages the plan is the unpaged one and
-    // the kernel reads each step of a piece from its page.
+    // Parts of this sequence: every streamed segment (prefix plane, ring) is
+    // cut on its own into near-equal pieces of at most S positions (multiples
+    // of 32 but the last), each piece a part of its own.  Short rings (at
+    // most kFold slots) and the groups' own draft rows are appended to the
+    // anchor part of their depth: the last piece of the first segment that
+    // a group at that depth reads (RIPE: the deep plane, else the ring; FULL:
+    // the plane at that depth; DEEPEST: the plane).  Neither the cuts nor
+    // the anchors depend on the other groups of the sequence, so a group's
+    // runs fall in the same parts alone or with siblings (whose extra runs
+    // are masked for its columns).  An in-flight parent's rows form parts of
+    // their own.  Paged caches: with pages of at least S positions a
+    // prefix-plane piece is first cut at page boundaries (every run then lies
+    // in one page); with shorter pages a run may span pages and the kernel
+    // reads each step from its page.
     const bool cut_at_pages = table != nullptr && d.page_len >= S;
-    sc.pieces.clear();
+    sc.segs.clear();
     enumerate_segments(d.layout, d.R, We, T, grp, 0, gc, kp, [&](const Seg& sg) {
+      sc.segs.push_back(sg);
+      return false;
+    });
+    const int n_seg = int(sc.segs.size());
+    auto stream = [](const Seg& sg) { return sg.kind == kSegPlane || sg.kind == kSegRing; };
+    // the anchor segment of depth r: -1 if none
+    auto anchor_seg = [&](int r) {
+      int ring = -1;
+      for (int i = 0; i < n_seg; ++i) {
+        const Seg& sg = sc.segs[i];
+        if (sg.kind == kSegPlane && (d.layout != RIPE_LAYOUT_FULL || sg.depth == r)) return i;
+        if (sg.kind == kSegRing && sg.depth == r && ring < 0) ring = i;
+      }
+      return ring;
+    };
+    auto folded = [&](int i) {  // a short ring that goes into another segment's anchor part
+      const Seg& sg = sc.segs[i];
+      return sg.kind == kSegRing && sg.len <= kFold && anchor_seg(sg.depth) != i;
+    };
+    sc.part_runs.resize(std::max<size_t>(sc.part_runs.size(), size_t(n_seg) * 64 + 1));
+    int n_part = 0;
+    sc.seg_last.assign(n_seg, -1);
+    for (int i = 0; i < n_seg; ++i) {
+      const Seg& sg = sc.segs[i];
+      if (!stream(sg) || folded(i) || sg.len == 0) continue;
       const bool cut = cut_at_pages && sg.kind == kSegPlane;
       for (int a0 = 0; a0 < sg.len;) {
         const int a1 = cut ? std::min(sg.len, (a0 / d.page_len + 1) * d.page_len) : sg.len;
         const int pl = piece_len(a1 - a0, S);
-        for (int c0 = a0; c0 < a1; c0 += pl)
-          sc.pieces.push_back(Piece{c0, std::min(pl, a1 - c0), uint8_t(sg.kind), uint8_t(sg.depth),
-                                    uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0});
+        for (int c0 = a0; c0 < a1; c0 += pl) {
+          if (size_t(n_part) >= sc.part_runs.size()) sc.part_runs.resize(2 * sc.part_runs.size());
+          sc.part_runs[n_part].clear();
+          sc.part_runs[n_part].push_back(Piece{c0, std::min(pl, a1 - c0), uint8_t(sg.kind), uint8_t(sg.depth), 0, 0});
+          sc.seg_last[i] = n_part++;
+        }
         a0 = a1;
       }
-      return false;
-    });
+    }
+    // the part a short run of depth r joins: its anchor's last piece, or a new part
+    auto home = [&](int r) -> int {
+      const int a = anchor_seg(r);
+      if (a >= 0 && sc.seg_last[a] >= 0) return sc.seg_last[a];
+      if (size_t(n_part) >= sc.part_runs.size()) sc.part_runs.resize(2 * sc.part_runs.size());
+      sc.part_runs[n_part].clear();
+      return n_part++;
+    };
+    for (int i = 0; i < n_seg; ++i)
+      if (folded(i)) {
+        const Seg& sg = sc.segs[i];
+        sc.part_runs[home(sg.depth)].push_back(Piece{0, sg.len, uint8_t(sg.kind), uint8_t(sg.depth), 0, 0});
+      }
+    for (int i = 0; i < n_seg; ++i) {
+      const Seg& sg = sc.segs[i];
+      if (stream(sg) || sg.len == 0) continue;
+      const Piece pc{0, sg.len, uint8_t(sg.kind), uint8_t(sg.depth), uint8_t(sg.gidx < 0 ? 0 : sg.gidx), 0};
+      if (sg.kind == kSegDraft) {
+        sc.part_runs[home(sg.depth)].push_back(pc);
+      } else {  // in-flight parent rows: parts of their own, at most S rows each
+        const int pl = piece_len(sg.len, S);
+        for (int c0 = 0; c0 < sg.len; c0 += pl) {
+          if (size_t(n_part) >= sc.part_runs.size()) sc.part_runs.resize(2 * sc.part_runs.size());
+          sc.part_runs[n_part].clear();
+          sc.part_runs[n_part++].push_back(Piece{c0, std::min(pl, sg.len - c0), pc.kind, pc.depth, 0, 0});
+        }
+      }
+    }
+    // flatten: each part's streamed runs first, then its draft-row runs
+    sc.pieces.clear();
+    sc.parts.clear();
+    for (int k = 0; k < n_part; ++k) {
+      PartRec pr{int(sc.pieces.size()), 0, 0, 0};
+      for (const Piece& pc : sc.part_runs[k])
+        if (pc.kind == kSegPlane || pc.kind == kSegRing) {
+          sc.pieces.push_back(pc);
+          pr.steps += (pc.len + kStep - 1) / kStep;
+        }
+      pr.n_stream = int(sc.pieces.size()) - pr.first;
+      for (const Piece& pc : sc.part_runs[k])
+        if (!(pc.kind == kSegPlane || pc.kind == kSegRing)) sc.pieces.push_back(pc);
+      pr.n_run = int(sc.pieces.size()) - pr.first;
+      if (pr.n_run > 255 || pr.steps > 65535) return RIPE_EUNSUPPORTED;
+      sc.parts.push_back(pr);
+    }
     const int n_piece = int(sc.pieces.size());
-    // page entries past the first that the sequence's prefix-plane pieces
+    // page entries past the first that the sequence's prefix-plane runs
     // need (paged caches)
     int n_refs = 0;
     if (table != nullptr)
       for (const Piece& pc : sc.pieces)
         if (pc.kind == kSegPlane) n_refs += (pc.c0 + pc.len - 1) / d.page_len - pc.c0 / d.page_len;
     if (n_refs > kMaxPageRefs) return RIPE_EUNSUPPORTED;  // one sequence's pages must fit a launch
-    const int n_split = n_piece;
+    const int n_split = n_part;
     const int n_cc = (nq + CQ - 1) / CQ;
     const int64_t per_head = int64_t(n_split) * n_cc;
     if (per_head > kMaxItems || n_piece > kMaxPieces) return RIPE_EUNSUPPORTED;  // one KV head must fit a launch
@@ -533,17 +625,21 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
         }
         cur->t.piece[p.n_pieces++] = pc;
       }
-      // items of unit (h, cc): one per piece; partial slot = part0 + unit *
-      // n_split + piece
+      // items of unit (h, cc): one per part; partial slot = part0 + unit *
+      // n_split + part
       for (int hh = 0; hh < hc; ++hh)
         for (int cc = 0; cc < n_cc; ++cc) {
           const int unit = hh * n_cc + cc;
-          for (int k = 0; k < n_piece; ++k) {
+          for (int k = 0; k < n_split; ++k) {
+            const PartRec& pr = sc.parts[k];
             Item& it = cur->t.item[p.n_wg++];
-            it.piece = uint16_t(pbase + k);
+            it.r0 = uint16_t(pbase + pr.first);
+            it.n_stream = uint8_t(pr.n_stream);
+            it.n_run = uint8_t(pr.n_run);
             it.part = uint16_t(sr.part0 + unit * n_split + k);
             it.h = uint16_t(h + hh);
             it.cc = uint16_t(cc);
+            it.steps = uint16_t(pr.steps);
           }
           Unit& un = cur->u.unit[p.n_units + unit];
           un.part = sr.part0 + unit * n_split;
@@ -559,8 +655,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       h += hc;
     }
   }
-  // Items run longest first (by 32-position steps; a stable counting sort).
-  // Work-groups: one per long item, one per four consecutive short items.
+  // Items run longest first (by 32-position steps; a stable counting sort),
+  // one work-group each.
   // The hardware dispatches work-groups in grid order: the first round puts
   // work-group j on compute unit j mod n_cu, and with two resident per unit,
   // j and j + n_cu share one.  A unit's finishing time follows the total
@@ -577,10 +673,16 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     lp.part_bytes = kWsHeader + int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
     Item* items = lp.t.item;
     const int n = lp.p.n_wg;
+    // an item's cost: its streamed steps and its draft-row steps
+    auto cost_of = [&](const Item& it) {
+      int c = it.steps;
+      for (int r = it.r0 + it.n_stream; r < it.r0 + it.n_run; ++r) c += (lp.t.piece[r].len + kStep - 1) / kStep;
+      return c;
+    };
     int max_steps = 0;
     sc.cost.resize(n);
     for (int i = 0; i < n; ++i) {
-      sc.cost[i] = (lp.t.piece[items[i].piece].len + kStep - 1) / kStep;
+      sc.cost[i] = cost_of(items[i]);
       max_steps = std::max(max_steps, sc.cost[i]);
     }
     sc.by_size.assign(max_steps + 2, 0);  // by_size[max_steps - c + 1]: items with more steps than c
@@ -589,23 +691,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     sc.items.resize(n);
     for (int i = 0; i < n; ++i) sc.items[sc.by_size[max_steps - sc.cost[i]]++] = items[i];
     std::copy(sc.items.begin(), sc.items.end(), items);
-    for (int i = 0; i < n; ++i) sc.cost[i] = (lp.t.piece[items[i].piece].len + kStep - 1) / kStep;
-    int n_big = 0;
-    while (n_big < n && sc.cost[n_big] > kSoloSteps) ++n_big;
-    // work-groups by decreasing work (steps): both runs below are already
-    // decreasing, so one merge orders them
-    sc.long_wg.clear();
-    sc.solo_wg.clear();
-    for (int i = 0; i < n_big; ++i) sc.long_wg.push_back({sc.cost[i], uint16_t(i)});
-    for (int i = n_big; i < n; i += kWaves) {
-      const int cnt = std::min(kWaves, n - i);
-      int w = 0;
-      for (int k = 0; k < cnt; ++k) w += sc.cost[i + k];
-      sc.solo_wg.push_back({w, uint16_t(i | ((cnt - 1) << 11) | kWgSolo)});
-    }
-    sc.wgs.resize(sc.long_wg.size() + sc.solo_wg.size());
-    std::merge(sc.long_wg.begin(), sc.long_wg.end(), sc.solo_wg.begin(), sc.solo_wg.end(), sc.wgs.begin(),
-               [](const WgCost& x, const WgCost& y) { return x.work > y.work; });
+    sc.wgs.resize(n);
+    for (int i = 0; i < n; ++i) sc.wgs[i] = WgCost{cost_of(items[i]), uint16_t(i)};
     const int N = int(sc.wgs.size());
     uint16_t* wg = lp.t.wg;
     if (per_cu == 2 && n_cu > 0 && N > n_cu && N <= 2 * n_cu) {

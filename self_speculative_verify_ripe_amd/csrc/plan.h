@@ -8,11 +8,14 @@
 //   kind 1  a RIPE window ring for each distinct depth r < R, read in ring
 //           slot order (slot s holds the one window position j = s mod We);
 //   kind 2  one group's own draft rows at its depth (causal within the group).
-// Every segment is cut into near-equal pieces of at most S positions (S a
-// multiple of 32, fixed by the descriptor; every piece but a segment's last
-// is a multiple of 32 long).  A work item is one piece for one KV head and one
-// query-column chunk: one work-group streams it and writes one split partial.
-// Partials start 256 bytes into the workspace.
+// The streamed segments of a sequence (prefix planes, then rings) are laid end
+// to end and cut into n near-equal parts (n from the split length S, fixed by
+// the descriptor), each cut falling on a segment boundary or on a multiple of
+// 32 positions inside a segment.  A part is a list of runs (pieces), slices of
+// one segment each; the sequence's draft-row segments (kinds 2-4) are
+// appended to its last part.  A work item is one part for one KV head and one
+// query-column chunk: one work-group reads its runs in order and writes one
+// split partial.  Partials start 256 bytes into the workspace.
 // The plan of a sequence depends only on the descriptor, its committed length
 // and its own groups, so a group's result is bit-identical whether it is
 // verified alone or batched with other sequences, and RIPE with W >= T (or
@@ -39,9 +42,8 @@ constexpr int kMaxSeq = 64;      // sequences per launch
 constexpr int kMaxGroups = 128;  // groups per launch
 constexpr int kMaxJobs = 128;    // commit jobs per launch
 constexpr int kMaxItems = 2048;  // verify work items (and merge units) per launch
-constexpr int kMaxPieces = 512;  // pieces per launch
+constexpr int kMaxPieces = 512;  // runs (pieces) per launch
 constexpr int kMaxPageRefs = 512;   // paged caches: pages after a piece's first, per launch
-constexpr int kSoloSteps = 4;    // a piece of at most this many steps runs on one wavefront
 
 // kinds 3 and 4: the rows of a parent block still in flight, read from the
 // draft tensors at the plane they will be read from once committed: rows
@@ -108,7 +110,7 @@ struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
   uint8_t seq;         // launch-local sequence index
 };
 
-// A run of positions of one segment of one sequence (12 bytes).
+// A run: positions of one segment of one sequence (12 bytes).
 struct Piece {
   int32_t c0;          // first position, segment-local (a multiple of 32)
   int32_t len;         // positions (kind 0), ring slots (kind 1) or rows (kind 2)
@@ -118,25 +120,23 @@ struct Piece {
   uint8_t s;           // launch-local sequence
 };
 
-// One verify work item (8 bytes): piece `piece` for KV head h and
+// One verify work item (12 bytes): runs [r0, r0 + n_stream) streamed from
+// the cache (prefix planes, rings), then runs [r0 + n_stream, r0 + n_run)
+// read from the draft tensors (draft rows, parent rows), for KV head h and
 // query-column chunk cc, written to split partial slot `part`.
 struct Item {
-  uint16_t piece;
+  uint16_t r0;
+  uint8_t n_stream;
+  uint8_t n_run;
   uint16_t part;
   uint16_t h;
   uint16_t cc;
+  uint16_t steps;      // 32-position steps of its stream runs
 };
 
-// Work-group entries (16 bits): bits 0-10 the first item, bits 11-12 the
-// number of items less one, bit 15 set for a work-group of short items.
-constexpr uint16_t kWgSolo = 0x8000;
-static_assert(kMaxItems <= 2048, "work-group entries hold an 11-bit item index");
-
-// Pieces, work items and work-groups of one launch.  Items are ordered
-// longest first.  Items of at most kSoloSteps steps are short: up to four of
-// them share a work-group, one per wavefront; every other item has a
-// work-group of its own.  wg[] maps each work-group of the grid to its items
-// (see the planner for the placement order).
+// Runs, work items and work-groups of one launch.  wg[] maps each
+// work-group of the grid to its item (see the planner for the placement
+// order).
 struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];

@@ -324,19 +324,25 @@ constexpr int verify_lds_bytes() {
   return merge > draft ? merge : draft;
 }
 
-// Work items: one piece of one sequence for one KV head and one query-column
-// chunk (see plan.h).  A work-group runs either one long item, its steps
-// spread over the four wavefronts and merged through LDS, or up to four short
-// items, one per wavefront, each wavefront writing its own partial.  The
-// host's work-group table says which; the hardware dispatches work-groups in
-// grid order.  INF: the launch has in-flight parent blocks (parent segments,
-// ring slots hidden by the parent); launches without them use the kernel
-// compiled without that code, whose step loop it would otherwise slow down.
-// PG, paged caches: 1 when every prefix-plane piece lies inside one page
-// (read from that page), 2 when pieces may span pages (such a piece is read
-// step by step: each 32-position step lies inside one page); 0 unpaged.  The
-// step-by-step code is compiled only into PG = 2, whose loop it slows.
-// RT: the RIPE ring's last V block (We mod 32 slots) is too narrow for
+// Work items: one part of one sequence's runs for one KV head and one
+// query-column chunk (see plan.h).  The four wavefronts take each run's
+// 32-position steps in turn -- wavefront w the run's steps w, w + 4, ...,
+// streamed runs first, then draft-row runs -- and merge their softmax states
+// through LDS into one partial.  Numbering the steps per run keeps a run's
+// steps on the same wavefronts whatever other runs the item holds: runs
+// that another group of the sequence adds are masked for this group's
+// columns and leave its state bit-identical.  A wavefront keeps two run contexts:
+// the run of the step it computes and the run of the step it prefetches, so
+// the loads of a step in the next run go out before the current step is done
+// and a run boundary costs no pipeline bubble.  The hardware dispatches
+// work-groups in grid order.  INF: the launch has in-flight parent blocks
+// (parent segments, ring slots hidden by the parent); launches without them
+// use the kernel compiled without that code, whose step loop it would
+// otherwise slow down.  PG, paged caches: 1 when every prefix-plane run lies
+// inside one page (read from that page), 2 when runs may span pages (such a
+// run is read step by step: each 32-position step lies inside one page); 0
+// unpaged.  The step-by-step code is compiled only into PG = 2, whose loop it
+// slows.  RT: the RIPE ring's last V block (We mod 32 slots) is too narrow for
 // 16-byte loads of 8 slots, so its step is read one element at a time; the
 // code is compiled only into the launches whose window needs it.
 template <typename T, int D, int NB, bool INF, int PG = 0, bool RT = false>
@@ -360,27 +366,20 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
 
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  // A long item: wavefront w runs steps w, w + 4, ...  A short one: the
-  // wavefront runs every step of its own item.
-  const uint32_t wge = tab.wg[blockIdx.x];
-  const bool solo = (wge & kWgSolo) != 0;
-  if (solo && wave > int((wge >> 11) & 3)) return;  // (short items only: no barrier follows)
-  const int idx = int(wge & 0x7ffu) + (solo ? wave : 0);
-  const int st0 = solo ? 0 : wave;
-  const int sstride = solo ? 1 : kWaves;
-  const Item it = tab.item[idx];
-  const Piece pc = tab.piece[it.piece];
+  const Item it = tab.item[tab.wg[blockIdx.x]];
   const int h = it.h;
   const int cc = it.cc;
-  const SeqRec sr = p.seq[pc.s];
+  const int r_draft = it.r0 + it.n_stream;  // first draft-row run
+  const int r_end = it.r0 + it.n_run;
+  const SeqRec sr = p.seq[tab.piece[it.r0].s];
   const int Wb = min(p.We, sr.T);
-  const int nsteps = ceil_div(pc.len, kStep);
 
   // ---- query columns of this lane ---------------------------------------
   // Straight-line on purpose: every lane loads from a valid address and
   // padding columns are zeroed by selects, with no loads under divergent
-  // control flow.  hi[nb]: piece-local end of what the column sees.
-  int hi[NB];
+  // control flow.  The column's group, row and depth are kept to resolve each
+  // run's visibility.
+  int cgi[NB], crow[NB], cdep[NB];
   u32x4 qf[NB][KC];
   auto setup_columns = [&]() {
 #pragma unroll
@@ -396,7 +395,17 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
         const u32x4 v = ld16(qp + c * 4 * VEC + lg * VEC);
         qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
       }
-      const int gd = g.depth;
+      cgi[nb] = gi;
+      crow[nb] = row;
+      cdep[nb] = g.depth;
+    }
+  };
+  // Run-local end of what each column sees in run `pc` (0: nothing).
+  auto run_hi = [&](const Piece& pc, int (&hi)[NB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int gd = cdep[nb];
+      const int gi = cgi[nb];
       int hv;
       if (pc.kind == kSegPlane)
         hv = (p.layout == 0) ? (gd == pc.depth ? sr.T : 0)
@@ -405,12 +414,12 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
       else if (pc.kind == kSegRing)
         hv = (gd == pc.depth) ? Wb : 0;
       else if (!INF || pc.kind == kSegDraft)
-        hv = (gi == pc.gidx) ? row + 1 : 0;
+        hv = (gi == pc.gidx) ? crow[nb] + 1 : 0;
       else if (pc.kind == kSegParentDeep)  // in-flight parent rows: all visible
         hv = pc.c0 + pc.len;
       else
         hv = (gd == pc.depth) ? pc.c0 + pc.len : 0;
-      hi[nb] = valid ? hv - pc.c0 : 0;
+      hi[nb] = gi >= 0 ? hv - pc.c0 : 0;
     }
   };
 
@@ -419,203 +428,240 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   const float sl2 = p.scale_log2;
   u32x4 kf[2][KC], vf[DB][VCH];
 
-  // Wavefront w runs steps w, w + 4, ... of the piece.
-  if (INF ? (pc.kind == kSegPlane || pc.kind == kSegRing) : pc.kind != kSegDraft) {
-    // ---- prefix plane or window ring: raw buffer loads ------------------
-    // The buffer resources span the piece only: loads past its end return
-    // zeros.
-    size_t off;
-    // slots from the piece's start to the end of the region's V blocks: the
+  // ---- streamed runs (prefix planes, rings): raw buffer loads ------------
+  // A run context: the buffer resources of one run (they span the run only:
+  // loads past its end return zeros), its ns steps, and its visibility (set
+  // once the columns are known).
+  struct Ctx {
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    int r, ns, len, c0, vlim, depth;
+    bool ring, per_step;
+    int hi[NB];
+  };
+  const int P = PG > 0 ? p.page_len : 1;
+  // element offset of position pos of run pc's pages (paged caches)
+  auto page_base = [&](int r, const Piece& pc, int pos) -> size_t {
+    const int k = pos / P - pc.c0 / P;  // page of the run
+    const size_t pg = size_t(k == 0 ? tab.pages[r] : tab.pages[kMaxPieces + tab.pref[r] + k - 1]);
+    return (((p.layout == 0) ? pg * p.R + (pc.depth - 1) : pg) * p.H + h) * size_t(P) * D + size_t(pos % P) * D;
+  };
+  auto make_ctx = [&](int r, Ctx& c) {
+    const Piece pc = tab.piece[r];
+    c.r = r;
+    c.ns = ceil_div(pc.len, kStep);
+    c.len = pc.len;
+    c.c0 = pc.c0;
+    c.depth = pc.depth;
+    c.ring = pc.kind == kSegRing;
+    // slots from the run's start to the end of the region's V blocks: the
     // ring's last block is narrower when We is not a multiple of 32
-    int vlim = 1 << 30;
-    // a paged prefix-plane piece inside one page is addressed like an
-    // unpaged one; one that spans pages is read step by step (below)
-    const int P = PG > 0 ? p.page_len : 1;
-    const bool plane_paged = PG > 0 && pc.kind == kSegPlane;
-    const bool per_step = PG == 2 && plane_paged && (pc.c0 + pc.len - 1) / P != pc.c0 / P;
-    auto page_base = [&](int pos) -> size_t {  // element offset of position pos of the piece's pages
-      const int k = pos / P - pc.c0 / P;      // page of the piece
-      const size_t pg = size_t(k == 0 ? tab.pages[it.piece] : tab.pages[kMaxPieces + tab.pref[it.piece] + k - 1]);
-      return (((p.layout == 0) ? pg * p.R + (pc.depth - 1) : pg) * p.H + h) * size_t(P) * D + size_t(pos % P) * D;
-    };
+    c.vlim = c.ring ? p.We - pc.c0 : (1 << 30);
+    const bool plane_paged = PG > 0 && !c.ring;
+    c.per_step = PG == 2 && plane_paged && (pc.c0 + pc.len - 1) / P != pc.c0 / P;
+    size_t off;
     if (plane_paged) {
-      off = page_base(pc.c0);
-    } else if (pc.kind == kSegPlane) {
+      off = page_base(r, pc, pc.c0);
+    } else if (!c.ring) {
       off = (((p.layout == 0) ? size_t(sr.b) * p.R + (pc.depth - 1) : size_t(sr.b)) * p.H + h) *
                 size_t(p.t_max) * D +
             size_t(pc.c0) * D;
     } else {
       off = p.ring_off + ((size_t(sr.b) * (p.R - 1) + (pc.depth - 1)) * p.H + h) * size_t(p.We) * D +
             size_t(pc.c0) * D;  // c0 is a multiple of 32: a V block starts there
-      vlim = p.We - pc.c0;
     }
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const T*>(p.cache_k) + off, uint32_t(pc.len) * D * E);
-    const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(static_cast<const T*>(p.cache_v) + off, uint32_t(min(ceil_div(pc.len, kStep) * kStep, vlim)) * D * E);
-    const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
-    const uint32_t koff = (krow * D + lg * VEC) * E;
-    // A step past the piece maps to an offset beyond the resource's range:
-    // those loads return zeros without touching memory, so the prefetch
-    // below is unconditional and the wait counts stay exact.
-    constexpr uint32_t kOutOfRange = 0x80000000u;
-    // A piece spanning pages: the step's K rows are one 32-row run of its
-    // page and its V values one [D][32] block, so each step gets resources of
-    // its own (a step past the piece reads the piece's last page, out of range).
-    auto step_base = [&](int st) -> size_t { return page_base(pc.c0 + min(st, nsteps - 1) * kStep); };
-    auto load_k = [&](int st, bool live, u32x4 (&k)[2][KC]) {
-      __amdgpu_buffer_rsrc_t rs = krs;
-      uint32_t base = live ? uint32_t(st * kStep) * D * E + koff : kOutOfRange;
-      if (PG == 2 && per_step) {
-        rs = make_rsrc(static_cast<const T*>(p.cache_k) + step_base(st),
-                       uint32_t(min(kStep, pc.len - min(st, nsteps - 1) * kStep)) * D * E);
-        base = live ? koff : kOutOfRange;
-      }
+    c.krs = make_rsrc(static_cast<const T*>(p.cache_k) + off, uint32_t(pc.len) * D * E);
+    c.vrs = make_rsrc(static_cast<const T*>(p.cache_v) + off,
+                      uint32_t(min(c.ns * kStep, c.vlim)) * D * E);
+  };
+  // move (c, st) on to this wavefront's next step: st + 4 in the same run,
+  // else step `wave` of the next run that has one; returns false past the
+  // item's last streamed run
+  auto advance = [&](Ctx& c, int& st) -> bool {
+    while (st >= c.ns) {
+      if (c.r + 1 >= r_draft) return false;
+      make_ctx(c.r + 1, c);
+      st = wave;
+    }
+    return true;
+  };
+  const uint32_t krow = uint32_t(8 * (ln >> 2) + (ln & 3));
+  const uint32_t koff = (krow * D + lg * VEC) * E;
+  // A step past the item maps to an offset beyond the resource's range:
+  // those loads return zeros without touching memory, so the prefetch below
+  // is unconditional and the wait counts stay exact.
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  // A run spanning pages: the step's K rows are one 32-row run of its page
+  // and its V values one [D][32] block, so each step gets resources of its
+  // own.
+  auto step_base = [&](const Ctx& c, int st) -> size_t {
+    const Piece pc = tab.piece[c.r];
+    return page_base(c.r, pc, pc.c0 + min(st, c.ns - 1) * kStep);
+  };
+  auto load_k = [&](const Ctx& c, int st, bool live, u32x4 (&k)[2][KC]) {
+    __amdgpu_buffer_rsrc_t rs = c.krs;
+    uint32_t base = live ? uint32_t(st * kStep) * D * E + koff : kOutOfRange;
+    if (PG == 2 && c.per_step) {
+      rs = make_rsrc(static_cast<const T*>(p.cache_k) + step_base(c, st),
+                     uint32_t(min(kStep, c.len - min(st, c.ns - 1) * kStep)) * D * E);
+      base = live ? koff : kOutOfRange;
+    }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int c = 0; c < KC; ++c) k[mb][c] = bload16(rs, base + (4 * mb * D + c * 4 * VEC) * E);
-    };
-    // The step's V block holds w slots [D][w] (w = 32 but for a ring's last
-    // block); lane group lg takes slots 8 lg .. 8 lg + 7 of head dimension
-    // ln + 16 db.
-    auto load_v = [&](int st, bool live, u32x4 (&v)[DB][VCH]) {
-      __amdgpu_buffer_rsrc_t rs = vrs;
-      const int w = min(kStep, vlim - st * kStep);
-      uint32_t base = live ? uint32_t(st * kStep * D + ln * w + 8 * lg) * E : kOutOfRange;
-      if (PG == 2 && per_step) {  // w = 32: the step is one whole V block
-        rs = make_rsrc(static_cast<const T*>(p.cache_v) + step_base(st), uint32_t(kStep) * D * E);
-        base = live ? uint32_t(ln * kStep + 8 * lg) * E : kOutOfRange;
-      }
-      if (RT && live && (w * E) % 16 != 0) {
-        // a narrow block whose rows are not 16-byte aligned: element loads
-        // (slots past w read as zero and are masked below anyway)
+      for (int cch = 0; cch < KC; ++cch) k[mb][cch] = bload16(rs, base + (4 * mb * D + cch * 4 * VEC) * E);
+  };
+  // The step's V block holds w slots [D][w] (w = 32 but for a ring's last
+  // block); lane group lg takes slots 8 lg .. 8 lg + 7 of head dimension
+  // ln + 16 db.
+  auto load_v = [&](const Ctx& c, int st, bool live, u32x4 (&v)[DB][VCH]) {
+    __amdgpu_buffer_rsrc_t rs = c.vrs;
+    const int w = min(kStep, c.vlim - st * kStep);
+    uint32_t base = live ? uint32_t(st * kStep * D + ln * w + 8 * lg) * E : kOutOfRange;
+    if (PG == 2 && c.per_step) {  // w = 32: the step is one whole V block
+      rs = make_rsrc(static_cast<const T*>(p.cache_v) + step_base(c, st), uint32_t(kStep) * D * E);
+      base = live ? uint32_t(ln * kStep + 8 * lg) * E : kOutOfRange;
+    }
+    if (RT && live && (w * E) % 16 != 0) {
+      // a narrow block whose rows are not 16-byte aligned: element loads
+      // (slots past w read as zero and are masked below anyway)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-          for (int c = 0; c < VCH; ++c) v[db][c] = u32x4{0u, 0u, 0u, 0u};
+        for (int cch = 0; cch < VCH; ++cch) v[db][cch] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t o = (8 * lg + e < w) ? base + uint32_t(16 * db * w + e) * E : kOutOfRange;
-            O::put_bits(v[db], e, O::bload_elem(rs, o));
-          }
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t o = (8 * lg + e < w) ? base + uint32_t(16 * db * w + e) * E : kOutOfRange;
+          O::put_bits(v[db], e, O::bload_elem(rs, o));
         }
-        return;
       }
+      return;
+    }
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) v[db][c] = bload16_stream(rs, base + (16 * db * w + c * VEC) * E);
-    };
-    const bool hole = INF && pc.kind == kSegRing && sr.hole > 0;
-    // first step's loads go out before the query setup
-    load_k(st0, st0 < nsteps, kf);
-    load_v(st0, st0 < nsteps, vf);
+      for (int cch = 0; cch < VCH; ++cch) v[db][cch] = bload16_stream(rs, base + (16 * db * w + cch * VEC) * E);
+  };
+
+  Ctx cur;
+  int st = wave;
+  bool have = it.n_stream > 0;
+  if (have) {
+    make_ctx(it.r0, cur);
+    have = advance(cur, st);
+  }
+  if (!have) setup_columns();
+  if (have) {
+    // the first step's loads go out before the query setup
+    load_k(cur, st, true, kf);
+    load_v(cur, st, true, vf);
     setup_columns();
-    for (int st = st0; st < nsteps; st += sstride) {
-      const bool more = st + sstride < nsteps;
+    run_hi(tab.piece[cur.r], cur.hi);
+    for (;;) {
       floatx4 sacc[2][NB];
       qk<T, D, NB>(kf, qf, sacc);
-      load_k(st + sstride, more, kf);
+      Ctx nxt = cur;
+      int sn = st + kWaves;
+      const bool more = advance(nxt, sn);
+      if (more && nxt.r != cur.r) run_hi(tab.piece[nxt.r], nxt.hi);
+      load_k(nxt, sn, more, kf);
       int lim[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - st * kStep;
-      // a ring whose oldest slots now lie before the window (a parent block
-      // in flight) does not read those slots
+      for (int nb = 0; nb < NB; ++nb) lim[nb] = cur.hi[nb] - st * kStep;
       typename O::P pf[NB];
-      if constexpr (INF)
-        sm.update(sacc, lim, sl2, pf, hole, pc.c0 + st * kStep, sr.ring_base, sr.hole, p.We);
-      else
+      if constexpr (INF) {
+        // a ring whose oldest slots now lie before the window (a parent block
+        // in flight) does not read those slots
+        const bool hole = cur.ring && sr.hole > 0;
+        sm.update(sacc, lim, sl2, pf, hole, cur.c0 + st * kStep, sr.ring_base, sr.hole, p.We);
+      } else {
         sm.update(sacc, lim, sl2, pf);
-      // a step reaching past the piece's end: zero the V values of the
-      // missing positions (they may hold anything, even NaN)
-      if ((st + 1) * kStep > pc.len) {
-        const int nval = pc.len - (st * kStep + 8 * lg);
+      }
+      // a step reaching past the run's end: zero the V values of the missing
+      // positions (they may hold anything, even NaN)
+      if ((st + 1) * kStep > cur.len) {
+        const int nval = cur.len - (st * kStep + 8 * lg);
 #pragma unroll
         for (int db = 0; db < DB; ++db) O::zero_tail(vf[db], nval);
       }
       sm.pv(vf, pf);
-      load_v(st + sstride, more, vf);
+      load_v(nxt, sn, more, vf);
+      if (!more) break;
+      cur = nxt;
+      st = sn;
     }
-  } else {
-    // ---- a group's own draft rows (kv_new, row-major): K rows are loaded
-    // in MFMA order directly; V rows are staged in this wavefront's LDS slice
-    // with 16-byte loads and read back transposed.
-    setup_columns();
-    // the piece's first row: the group's own rows, or the in-flight parent's
-    // (the rows before its window first, then the window's)
+  }
+
+  // ---- draft-row runs (kv_new, row-major): the group's own rows or the
+  // in-flight parent's.  K rows are loaded in MFMA order directly; V rows are
+  // staged in this wavefront's LDS slice with 16-byte loads and read back
+  // transposed.
+  if (r_draft < r_end) {
     const int Hd = p.H * D;
-    const size_t row0 = (!INF || pc.kind == kSegDraft
-                             ? size_t(p.grp[pc.gidx].row_start)
-                             : size_t(sr.parent_row0) + (pc.kind == kSegParentWin ? sr.nd : 0)) +
-                        size_t(pc.c0);
-    const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
-    const T* vb = static_cast<const T*>(p.kv_new) + (size_t(p.R + pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
     T* stage = reinterpret_cast<T*>(lds_raw) + size_t(wave) * kStep * D;  // [32 rows][D]
     constexpr int CPR = D / VEC;  // 16-byte pieces per row
-    const int len = pc.len;
-    for (int st = st0; st < nsteps; st += sstride) {
-      const int base = st * kStep;
+    for (int r = r_draft; r < r_end; ++r) {
+      const Piece pc = tab.piece[r];
+      const int ns = ceil_div(pc.len, kStep);
+      int st = wave;
+      if (st < ns) {
+        int hi[NB];
+        run_hi(pc, hi);
+        // the run's first row: the group's own rows, or the in-flight
+        // parent's (the rows before its window first, then the window's)
+        const size_t row0 = (!INF || pc.kind == kSegDraft
+                                 ? size_t(p.grp[pc.gidx].row_start)
+                                 : size_t(sr.parent_row0) + (pc.kind == kSegParentWin ? sr.nd : 0)) +
+                            size_t(pc.c0);
+        const T* kb = static_cast<const T*>(p.kv_new) + (size_t(pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
+        const T* vb = static_cast<const T*>(p.kv_new) + (size_t(p.R + pc.depth - 1) * p.n_rows + row0) * Hd + size_t(h) * D;
+        const int len = pc.len;
+        for (; st < ns; st += kWaves) {
+          const int base = st * kStep;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int pos = base + 8 * (ln >> 2) + 4 * mb + (ln & 3);
-        const bool ok = pos < len;
-        const T* rp = kb + size_t(ok ? pos : 0) * Hd + lg * VEC;
+          for (int mb = 0; mb < 2; ++mb) {
+            const int pos = base + 8 * (ln >> 2) + 4 * mb + (ln & 3);
+            const bool ok = pos < len;
+            const T* rp = kb + size_t(ok ? pos : 0) * Hd + lg * VEC;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const u32x4 v = ld16(rp + c * 4 * VEC);
-          kf[mb][c] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+            for (int cch = 0; cch < KC; ++cch) {
+              const u32x4 v = ld16(rp + cch * 4 * VEC);
+              kf[mb][cch] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+            }
+          }
+          // stage V rows [base, base + 32) of this head: piece i = (row, 16 B)
+#pragma unroll
+          for (int i = lane; i < kStep * CPR; i += 64) {
+            const int rr = i / CPR;
+            const int cch = i - rr * CPR;
+            const bool ok = base + rr < len;
+            const u32x4 v = ld16(vb + size_t(ok ? base + rr : 0) * Hd + cch * VEC);
+            *reinterpret_cast<u32x4*>(stage + rr * D + cch * VEC) = ok ? v : u32x4{0u, 0u, 0u, 0u};
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged rows are in LDS
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int v = 0; v < VCH; ++v) vf[db][v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) O::put_elem(vf[db], e, stage, size_t(8 * lg + e) * D + 16 * db + ln);
+          }
+          __builtin_amdgcn_wave_barrier();
+          floatx4 sacc[2][NB];
+          qk<T, D, NB>(kf, qf, sacc);
+          int lim[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - base;
+          typename O::P pf[NB];
+          sm.update(sacc, lim, sl2, pf);
+          sm.pv(vf, pf);
         }
       }
-      // stage V rows [base, base + 32) of this head: piece i = (row, 16 B)
-#pragma unroll
-      for (int i = lane; i < kStep * CPR; i += 64) {
-        const int r = i / CPR;
-        const int c = i - r * CPR;
-        const bool ok = base + r < len;
-        const u32x4 v = ld16(vb + size_t(ok ? base + r : 0) * Hd + c * VEC);
-        *reinterpret_cast<u32x4*>(stage + r * D + c * VEC) = ok ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staged rows are in LDS
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int v = 0; v < VCH; ++v) vf[db][v] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O::put_elem(vf[db], e, stage, size_t(8 * lg + e) * D + 16 * db + ln);
-      }
-      __builtin_amdgcn_wave_barrier();
-      floatx4 sacc[2][NB];
-      qk<T, D, NB>(kf, qf, sacc);
-      int lim[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) lim[nb] = hi[nb] - base;
-      typename O::P pf[NB];
-      sm.update(sacc, lim, sl2, pf);
-      sm.pv(vf, pf);
     }
   }
 
   const size_t stride = size_t(CQ) * (D + 2);
   float* const part = p.ws + size_t(it.part) * stride;
-  if (solo) {
-    // ---- a short item's partial, straight from this wavefront's registers
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float lt = wave_sum_lanegroups(sm.l[nb]);
-      const int col = ln + 16 * nb;
-      if (cc * CQ + col < sr.nq) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<floatx4*>(part + size_t(col) * D + 16 * db + 4 * lg) = sm.acc[db][nb];
-        if (lg == 0) {
-          part[size_t(CQ) * D + col] = sm.m[nb];
-          part[size_t(CQ) * D + CQ + col] = lt;
-        }
-      }
-    }
-    return;
-  }
 
   // ---- merge the four wavefronts through LDS, write one partial ----------
   __syncthreads();  // the draft path's staging slices are reused below
