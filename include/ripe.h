@@ -211,12 +211,18 @@ int64_t ripe_layout_bytes(const ripe_desc_t* desc, int32_t kind);
  *  plane_sel     device int8 [n_groups][t_max]: plane (1..R) read by group
  *                g at prefix position j, written for j < T_seq; may be NULL
  *  workspace     device scratch of workspace_bytes bytes (256-byte aligned;
- *                ripe_layout_bytes(desc, RIPE_BYTES_WORKSPACE) suffices);
- *                its contents need no initialisation and are clobbered
+ *                ripe_layout_bytes(desc, RIPE_BYTES_WORKSPACE) suffices).
+ *                Its first RIPE_WORKSPACE_ZERO_BYTES bytes must be zero
+ *                before the first call that uses it (e.g. allocated with a
+ *                zero fill); every call leaves them zero, so a workspace is
+ *                zeroed once.  They hold the arrival counters through which
+ *                the split-K work items of one launch find the last of them,
+ *                which merges the partials.  The rest is clobbered.
  *  stream        hipStream_t (as void*) the kernels are launched on
  *
  * Calls that share a workspace must be ordered on one stream.
  */
+#define RIPE_WORKSPACE_ZERO_BYTES 16640
 ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
                                const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
                                float softmax_scale, const void* q, const void* kv_new, void* out,
@@ -243,7 +249,7 @@ ripe_status_t ripe_verify_attn(const ripe_desc_t* desc, const void* cache, const
  * undefined results.  Order them on one stream, or use ripe_verify_attn
  * with a workspace each.
  */
-#define RIPE_NOALLOC_SCRATCH_BYTES 34078976
+#define RIPE_NOALLOC_SCRATCH_BYTES 34095360
 ripe_status_t ripe_verify_attn_noalloc(const ripe_desc_t* desc, const void* cache, const int32_t* seq_len,
                                        const ripe_group_t* groups, int32_t n_groups, int32_t n_rows,
                                        float softmax_scale, const void* q, const void* kv_new, void* out,
@@ -470,7 +476,9 @@ ripe_status_t ripe_accept(const ripe_accept_desc_t* desc, const float* target_lo
  *  workspace  device, 256-byte aligned; at least
  *             ripe_layout_bytes(desc, RIPE_BYTES_POSERR_WORKSPACE) bytes
  *             (RIPE_EWORKSPACE if smaller than the call needs).  Scratch
- *             only; owned by the caller.
+ *             owned by the caller; zero-filled before its first use (it
+ *             holds a verify workspace, whose counters must start at zero),
+ *             and every call leaves those counters zero.
  *
  * Validation and errors as for ripe_verify_attn; err, cond and lse must be
  * 4-byte aligned, out_f32 16-byte aligned.  Asynchronous on stream; launches kernels only.

@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("RIPE_LIB", os.path.join(_PKG, "libripe.so"))
 RIPE_LAYOUT_FULL, RIPE_LAYOUT_DEEPEST, RIPE_LAYOUT_RIPE = 0, 1, 2
 RIPE_F32, RIPE_BF16 = 0, 1
 RIPE_BYTES_CACHE, RIPE_BYTES_WORKSPACE, RIPE_BYTES_POSERR_WORKSPACE = 0, 1, 2
+RIPE_WORKSPACE_ZERO_BYTES = 16640  # leading workspace bytes that must be zero before its first use
 STATUS = {0: "RIPE_OK", -1: "RIPE_EINVAL", -2: "RIPE_ERANGE", -3: "RIPE_ECAPACITY",
           -4: "RIPE_EUNSUPPORTED", -5: "RIPE_EWORKSPACE", -6: "RIPE_EHIP"}
 LAYOUTS = {"full": RIPE_LAYOUT_FULL, "deepest": RIPE_LAYOUT_DEEPEST, "ripe": RIPE_LAYOUT_RIPE}
@@ -171,7 +172,7 @@ def ripe_layout_bytes(desc: ripe_desc_t, kind: int = RIPE_BYTES_CACHE) -> int:
 
 def new_workspace(desc: ripe_desc_t, device="cuda"):
     """A workspace big enough for any verify call within the descriptor's
-    bounds (zero-filled; the kernels need no particular contents)."""
+    bounds, zero-filled (its leading counters must start at zero)."""
     import torch
     return torch.zeros(ripe_layout_bytes(desc, RIPE_BYTES_WORKSPACE), dtype=torch.uint8,
                        device=device)

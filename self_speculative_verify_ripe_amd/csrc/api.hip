@@ -51,18 +51,17 @@ ripe_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Partials start 256 bytes into the workspace.
-constexpr int64_t kWsHeader = 256;
-
 // ---- the static scratch of ripe_verify_attn_noalloc ----------------------
-// The largest workspace one verify launch uses: the header and kMaxItems
-// partials of 32 query columns x (D + 2) floats at the largest head
-// dimension, D = 128.
+// The largest workspace one verify launch uses: the header (with the merge
+// units' arrival words, zero before and after every call; a static array
+// starts zeroed) and kMaxItems partials of 32 query columns x (D + 2) floats
+// at the largest head dimension, D = 128.
 // Calls are cut into launches of at most kMaxItems items, so every verify
 // call fits.  Each GPU the library runs on holds its own copy until the
 // process ends.
 constexpr size_t kStaticWsBytes = size_t(kWsHeader) + size_t(kMaxItems) * 32 * (128 + 2) * 4;
 static_assert(kStaticWsBytes == RIPE_NOALLOC_SCRATCH_BYTES, "ripe.h states the scratch size");
+static_assert(kWsHeader == RIPE_WORKSPACE_ZERO_BYTES, "ripe.h states the zeroed workspace header");
 }  // namespace
 
 static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
@@ -122,6 +121,9 @@ inline int piece_len(int len, int S) {
 
 // Rings of at most this many slots join their depth's anchor part (plan.h).
 constexpr int kFold = 4 * kStep;
+// Launches whose units have at most this many items merge them in the verify
+// kernel (the last item of each unit); others run the merge kernel.
+constexpr int kFuseSplits = 8;
 
 // Positions of the main region (FULL: per plane; otherwise the deep plane):
 // t_max per sequence, or the page pool of a paged cache.
@@ -185,7 +187,7 @@ int64_t workspace_bound(const ripe_desc_t& d) {
   per_seq += (1 + std::min<int64_t>(groups, d.R)) * ((rows + S - 1) / S);  // an in-flight parent's rows
   const int64_t col_chunks = (rows * G + 15) / 16 + nseq;
   const long double slots = (long double)d.n_kv_heads * col_chunks * per_seq;
-  const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4 + 256;
+  const long double bytes = slots * kMaxCQ * (d.head_dim + 2) * 4 + kWsHeader;
   if (bytes > (long double)kMaxBytes) return -1;
   return int64_t(bytes);
 }
@@ -242,6 +244,9 @@ struct VerifyScratch {
   std::vector<Item> items;
   std::vector<int> cost, by_size;
   std::vector<WgCost> wgs;
+  std::vector<int64_t> unit_cost;
+  std::vector<int> item_unit, unit_order, unit_xcd;
+  std::vector<uint16_t> xcd_items[kXcds];
   std::vector<LaunchPlan> plans;
   int n_plans = 0;
   // The inputs the plans above were built from (pointers aside).  A call
@@ -323,6 +328,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.lse = lse;
     p.plane_sel = plane_sel;
     p.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
+    p.arrive = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + kWsArrive);
   };
   auto launch_all = [&](int NB) -> ripe_status_t {
     if (static_ws) {
@@ -693,20 +699,81 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     std::copy(sc.items.begin(), sc.items.end(), items);
     sc.wgs.resize(n);
     for (int i = 0; i < n; ++i) sc.wgs[i] = WgCost{cost_of(items[i]), uint16_t(i)};
-    const int N = int(sc.wgs.size());
+    // Fused merge: the items of a unit go on grid positions equal mod 8 (one
+    // XCD); units are spread over the XCDs by their total work, largest
+    // first, and each XCD's items are placed on its compute units as below.
+    // One work-group reads the partials of a unit at the rate of one
+    // work-group, so launches with units of more than kFuseSplits items
+    // (whose merge is better spread over several work-groups), or a grid past
+    // the work-group table, keep the separate merge kernel.
+    const int cus_x = n_cu / kXcds;
+    bool fused = n_cu > 0 && n_cu % kXcds == 0 && per_cu == 2;
+    for (int s = 0; s < lp.p.n_seq && fused; ++s) fused = lp.p.seq[s].n_split <= kFuseSplits;
     uint16_t* wg = lp.t.wg;
-    if (per_cu == 2 && n_cu > 0 && N > n_cu && N <= 2 * n_cu) {
-      const int P = N - n_cu;  // compute units running two work-groups
-      const int S = n_cu - P;  // ... and one
-      for (int j = 0; j < P; ++j) {
-        wg[j] = sc.wgs[S + j].entry;
-        wg[n_cu + j] = sc.wgs[N - 1 - j].entry;
+    if (fused) {
+      const int nu = lp.p.n_units;
+      sc.unit_cost.assign(nu, 0);
+      sc.item_unit.resize(n);
+      for (int i = 0; i < n; ++i) {
+        const SeqRec& sr = lp.p.seq[lp.t.piece[items[i].r0].s];
+        const int u = sr.unit0 + (items[i].h - sr.h0) * sr.n_cc + items[i].cc;
+        sc.item_unit[i] = u;
+        sc.unit_cost[u] += sc.wgs[i].work;
       }
-      for (int j = 0; j < S; ++j) wg[P + j] = sc.wgs[j].entry;
-    } else {
-      for (int j = 0; j < N; ++j) wg[j] = sc.wgs[j].entry;
+      sc.unit_order.resize(nu);
+      for (int u = 0; u < nu; ++u) sc.unit_order[u] = u;
+      std::stable_sort(sc.unit_order.begin(), sc.unit_order.end(),
+                       [&](int a, int b) { return sc.unit_cost[a] > sc.unit_cost[b]; });
+      sc.unit_xcd.assign(nu, 0);
+      int64_t load[kXcds] = {};
+      for (int u : sc.unit_order) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+          if (load[x] < load[best]) best = x;
+        sc.unit_xcd[u] = best;
+        load[best] += sc.unit_cost[u];
+      }
+      for (int x = 0; x < kXcds; ++x) sc.xcd_items[x].clear();
+      for (int i = 0; i < n; ++i) sc.xcd_items[sc.unit_xcd[sc.item_unit[i]]].push_back(sc.wgs[i].entry);  // decreasing work
+      int rows = 0;
+      for (int x = 0; x < kXcds; ++x) rows = std::max(rows, int(sc.xcd_items[x].size()));
+      if (int64_t(rows) * kXcds > int64_t(kMaxItems) + 512) fused = false;
+      if (fused) {
+        for (int j = 0; j < rows * kXcds; ++j) wg[j] = kWgEmpty;
+        for (int x = 0; x < kXcds; ++x) {
+          const std::vector<uint16_t>& v = sc.xcd_items[x];
+          const int nx = int(v.size());
+          auto put = [&](int k, uint16_t e) { wg[x + kXcds * k] = e; };
+          if (nx > cus_x && nx <= 2 * cus_x) {
+            const int P = nx - cus_x, S = cus_x - P;
+            for (int k = 0; k < P; ++k) {
+              put(k, v[S + k]);
+              put(cus_x + k, v[nx - 1 - k]);
+            }
+            for (int k = 0; k < S; ++k) put(P + k, v[k]);
+          } else {
+            for (int k = 0; k < nx; ++k) put(k, v[k]);
+          }
+        }
+        lp.p.n_blocks = rows * kXcds;
+      }
     }
-    lp.p.n_blocks = N;
+    lp.p.fused = fused ? 1 : 0;
+    if (!fused) {
+      const int N = n;
+      if (per_cu == 2 && n_cu > 0 && N > n_cu && N <= 2 * n_cu) {
+        const int P = N - n_cu;  // compute units running two work-groups
+        const int S = n_cu - P;  // ... and one
+        for (int j = 0; j < P; ++j) {
+          wg[j] = sc.wgs[S + j].entry;
+          wg[n_cu + j] = sc.wgs[N - 1 - j].entry;
+        }
+        for (int j = 0; j < S; ++j) wg[P + j] = sc.wgs[j].entry;
+      } else {
+        for (int j = 0; j < N; ++j) wg[j] = sc.wgs[j].entry;
+      }
+      lp.p.n_blocks = N;
+    }
   }
   sc.key_desc = d;
   sc.key_rows = n_rows;

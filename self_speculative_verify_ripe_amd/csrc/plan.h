@@ -15,7 +15,10 @@
 // one segment each; the sequence's draft-row segments (kinds 2-4) are
 // appended to its last part.  A work item is one part for one KV head and one
 // query-column chunk: one work-group reads its runs in order and writes one
-// split partial.  Partials start 256 bytes into the workspace.
+// split partial.
+//
+// Workspace: a 256-byte header, one 64-bit arrival word per merge unit
+// (kMaxItems of them; zero between calls), then the partials.
 // The plan of a sequence depends only on the descriptor, its committed length
 // and its own groups, so a group's result is bit-identical whether it is
 // verified alone or batched with other sequences, and RIPE with W >= T (or
@@ -44,6 +47,9 @@ constexpr int kMaxJobs = 128;    // commit jobs per launch
 constexpr int kMaxItems = 2048;  // verify work items (and merge units) per launch
 constexpr int kMaxPieces = 512;  // runs (pieces) per launch
 constexpr int kMaxPageRefs = 512;   // paged caches: pages after a piece's first, per launch
+constexpr int kXcds = 8;         // work-group i of a grid runs on XCD i mod 8 (checked as it runs)
+constexpr int64_t kWsArrive = 256;                          // arrival words
+constexpr int64_t kWsHeader = kWsArrive + 8 * int64_t(kMaxItems);  // partials
 
 // kinds 3 and 4: the rows of a parent block still in flight, read from the
 // draft tensors at the plane they will be read from once committed: rows
@@ -135,12 +141,14 @@ struct Item {
 };
 
 // Runs, work items and work-groups of one launch.  wg[] maps each
-// work-group of the grid to its item (see the planner for the placement
-// order).
+// work-group of the grid to its item, or to none (kWgEmpty); see the
+// planner for the placement order.
+constexpr uint16_t kWgEmpty = 0xFFFF;
+
 struct ItemTable {
   Piece piece[kMaxPieces];
   Item item[kMaxItems];
-  uint16_t wg[kMaxItems];
+  uint16_t wg[kMaxItems + 512];
   // paged caches: prefix-plane piece i starts in page pages[i] (read with the
   // piece itself); a piece spanning pages continues in pages[kMaxPieces +
   // pref[i]], pages[kMaxPieces + pref[i] + 1], ...
@@ -182,6 +190,7 @@ struct VerifyParams {
   float* lse;
   int8_t* plane_sel;
   float* ws;             // split partials, [item][16 NB columns][D + 2]
+  unsigned long long* arrive;  // one arrival word per merge unit (fused merge)
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
   int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
@@ -194,6 +203,7 @@ struct VerifyParams {
   int32_t page_len;      // paged cache: positions per page (0: unpaged)
   int32_t page_mode;     // 0 unpaged, 1 every prefix-plane piece in one page, 2 pieces may span pages
   int32_t n_refs;        // paged cache: entries of ItemTable::pages used past kMaxPieces
+  int32_t fused;         // the last item of each unit merges it (else a merge kernel follows)
 };
 
 struct CommitJob {     // rows of one sequence written to one region (24 bytes)

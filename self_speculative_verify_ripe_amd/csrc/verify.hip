@@ -307,6 +307,30 @@ __device__ inline void qk(const u32x4 (&kf)[2][D / (4 * Op<T>::VEC)],
     }
 }
 
+// plane_sel rows of a sequence's groups (positions j < T), written by one
+// work-group of nthreads threads: the plane each group's depth reads at j.
+__device__ inline void write_plane_sel(const VerifyParams& p, const SeqRec& sr, int tid, int nthreads) {
+  if (p.plane_sel == nullptr) return;
+  for (int gi = sr.g_begin; gi < sr.g_begin + sr.g_count; ++gi) {
+    const int r = p.grp[gi].depth;
+    int8_t* rowp = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
+    for (int j0 = tid * 16; j0 < sr.T; j0 += nthreads * 16) {
+      int8_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
+        const int pl = (p.layout == 0) ? r : (p.layout == 1) ? p.R : ((j >= sr.tw) ? r : p.R);
+        v[e] = int8_t(pl);
+      }
+      if (j0 + 16 <= sr.T) {
+        *reinterpret_cast<u32x4*>(rowp + j0) = *reinterpret_cast<const u32x4*>(v);
+      } else {
+        for (int e = 0; j0 + e < sr.T; ++e) rowp[j0 + e] = v[e];
+      }
+    }
+  }
+}
+
 // Wavefronts per SIMD the register allocation targets: two work-groups per
 // CU, each wavefront with one K/V step in flight ahead of the one it computes.
 template <typename T, int D, int NB>
@@ -366,7 +390,9 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
 
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  const Item it = tab.item[tab.wg[blockIdx.x]];
+  const uint32_t wge = tab.wg[blockIdx.x];
+  if (wge == kWgEmpty) return;  // a grid position with no item (XCD placement)
+  const Item it = tab.item[wge];
   const int h = it.h;
   const int cc = it.cc;
   const int r_draft = it.r0 + it.n_stream;  // first draft-row run
@@ -663,7 +689,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   const size_t stride = size_t(CQ) * (D + 2);
   float* const part = p.ws + size_t(it.part) * stride;
 
-  // ---- merge the four wavefronts through LDS, write one partial ----------
+  // ---- merge the four wavefronts through LDS ------------------------------
   __syncthreads();  // the draft path's staging slices are reused below
   typedef float OSlice[CQ][D + 4];
   OSlice* lds_o = reinterpret_cast<OSlice*>(lds_raw);
@@ -684,12 +710,13 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __syncthreads();
   const int col = threadIdx.x / TPC;
   const int d0 = (threadIdx.x % TPC) * DPT;
-  if (cc * CQ + col < sr.nq) {
-    float M = -INFINITY;
+  const bool col_ok = cc * CQ + col < sr.nq;
+  float M = -INFINITY, L = 0.f;
+  float o[DPT];
+  if (col_ok) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][col]);
     float f[kWaves];
-    float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = lds_m[w][col];
@@ -698,16 +725,153 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     }
 #pragma unroll
     for (int d = 0; d < DPT; d += 4) {
-      floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+      floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += f[w] * *reinterpret_cast<const floatx4*>(&lds_o[w][col][d0 + d]);
-      *reinterpret_cast<floatx4*>(part + size_t(col) * D + d0 + d) = o;
+      for (int w = 0; w < kWaves; ++w) a += f[w] * *reinterpret_cast<const floatx4*>(&lds_o[w][col][d0 + d]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[d + e] = a[e];
     }
+  }
+  // the (sequence, KV head, column chunk) unit this item belongs to
+  const int unit_local = (h - sr.h0) * sr.n_cc + cc;
+  const int n_split = sr.n_split;
+  // outputs of a column from its merged (M, L, O) (log2 domain)
+  auto write_out = [&](float Mx, float Lx, const float (&ox)[DPT], bool poison) {
+    int row = 0, hh = 0;
+    const int gi = column_group(p, sr, cc * CQ + col, row, hh);
+    if (gi < 0) return;
+    const GroupRec& g = p.grp[gi];
+    const size_t orow = size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh;
+    float res[DPT];
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) res[d] = poison ? __builtin_nanf("") : ox[d] / Lx;
+    if (p.out_f32)
+      Op<float>::store(static_cast<float*>(p.out) + orow * D + d0, res, DPT);
+    else
+      O::store(static_cast<T*>(p.out) + orow * D + d0, res, DPT);
+    if (p.lse != nullptr && d0 == 0)
+      p.lse[orow] = poison ? __builtin_nanf("") : (Mx + log2f(Lx)) * 0.69314718055994530942f;
+  };
+  if (n_split == 1) {
+    // the unit is this one item: its outputs, no partial
+    if (col_ok) write_out(M, L, o, false);
+    if (h == 0 && cc == 0) write_plane_sel(p, sr, threadIdx.x, kThreads);
+    return;
+  }
+  if (col_ok) {
+#pragma unroll
+    for (int d = 0; d < DPT; d += 4)
+      *reinterpret_cast<floatx4*>(part + size_t(col) * D + d0 + d) = floatx4{o[d], o[d + 1], o[d + 2], o[d + 3]};
     if (d0 == 0) {
       part[size_t(CQ) * D + col] = M;
       part[size_t(CQ) * D + CQ + col] = L;
     }
   }
+  if (!p.fused) return;  // verify_merge_kernel merges the units
+
+  // ---- fused merge: the unit's last item merges it ------------------------
+  // Every item of a unit runs on one XCD (the planner places them on grid
+  // positions equal mod 8), whose L2 all its compute units share.  Each item
+  // waits until its partial stores are acknowledged by that L2, then counts
+  // itself in the unit's arrival word: one byte per XCD, so the last arrival
+  // also sees whether every item ran on its own XCD.  The last one resets
+  // the word for the next call and reads the partials back past its L1; if
+  // the items were not all on one XCD its L2 cannot be trusted, and it writes
+  // NaN rather than a result.
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores have reached the L2
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  int* const lds_flag = reinterpret_cast<int*>(lds_raw);
+  if (threadIdx.x == 0) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcds - 1);  // HW_REG_XCC_ID
+    unsigned long long* const word = p.arrive + (sr.unit0 + unit_local);
+    const unsigned long long add = 1ull << (8 * xcc);
+    const unsigned long long now =
+        __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+    unsigned total = 0;
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x) total += unsigned(now >> (8 * x)) & 0xFFu;
+    int flag = 0;
+    if (total == unsigned(n_split)) {
+      flag = 1;
+      if (now != (static_cast<unsigned long long>(n_split) << (8 * xcc))) flag |= 2;  // items on several XCDs
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *lds_flag = flag;
+  }
+  __syncthreads();
+  const int flag = *lds_flag;
+  if (!(flag & 1)) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (col_ok) {
+    // The unit's partials in split order, read past the L1 (sc0).  The loads
+    // of a batch of splits all go out before any is used (a read past the
+    // resource, for splits beyond the unit's, returns 0 and is not used):
+    // first every split's maximum, 16 at a time, then the weighted sums, 4
+    // splits at a time.  The arithmetic is the merge kernel's, in split order.
+    const float* const p0 = p.ws + size_t(sr.part0 + unit_local * n_split) * stride;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(p0, uint32_t(n_split) * uint32_t(stride) * 4u);
+    auto ld1 = [&](int s, size_t idx) -> float {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           prs, s < n_split ? uint32_t((size_t(s) * stride + idx) * 4) : 0x80000000u, 0, 1));
+    };
+    constexpr int U = 4;  // splits whose loads go out together
+    float Mx = -INFINITY;
+    float Lx = 0.f;
+    float ox[DPT];
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) ox[d] = 0.f;
+    float ms[U], ls[U];
+    floatx4 ov[U][DPT / 4];
+    auto load_splits = [&](int s0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        ms[u] = ld1(s, size_t(CQ) * D + col);
+        ls[u] = ld1(s, size_t(CQ) * D + CQ + col);
+#pragma unroll
+        for (int d = 0; d < DPT; d += 4)
+          ov[u][d / 4] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                             prs, s < n_split ? uint32_t((size_t(s) * stride + size_t(col) * D + d0 + d) * 4) : 0x80000000u,
+                             0, 1));
+      }
+    };
+    auto add_splits = [&](int s0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u >= n_split) break;
+        const float fs = (ms[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[u] - Mx);
+        Lx += fs * ls[u];
+#pragma unroll
+        for (int d = 0; d < DPT; d += 4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ox[d + e] += fs * ov[u][d / 4][e];
+      }
+    };
+    if (n_split <= U) {
+      // one round trip: every split's (m, l, O), then the maximum, then the sums
+      load_splits(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u < n_split) Mx = fmaxf(Mx, ms[u]);
+      add_splits(0);
+    } else {
+      for (int s0 = 0; s0 < n_split; s0 += 16) {
+        float mm[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) mm[u] = ld1(s0 + u, size_t(CQ) * D + col);
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (s0 + u < n_split) Mx = fmaxf(Mx, mm[u]);
+      }
+      for (int s0 = 0; s0 < n_split; s0 += U) {
+        load_splits(s0);
+        add_splits(s0);
+      }
+    }
+    write_out(Mx, Lx, ox, (flag & 2) != 0);
+  }
+  if (h == 0 && cc == 0) write_plane_sel(p, sr, threadIdx.x, kThreads);
 }
 
 // Merge: one work-group per (sequence, KV head, query-column chunk) and
@@ -733,6 +897,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
   typedef typename FloatN<DPT>::type VecT;
   const int slice = blockIdx.x % NS;
   const Unit un = ut.unit[blockIdx.x / NS];
+  if (un.n_split == 1) return;  // the unit's one item wrote its outputs
   const int cc = un.cc;
   const int h = un.h;
   const size_t stride = size_t(CQ) * (D + 2);
@@ -821,26 +986,7 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
   }
   const SeqRec sr = p.seq[un.s];
   // plane_sel of the sequence's groups: written once, by unit (h 0, chunk 0), slice 0
-  if (p.plane_sel != nullptr && h == 0 && cc == 0 && slice == 0) {
-    for (int gi = sr.g_begin; gi < sr.g_begin + sr.g_count; ++gi) {
-      const int r = p.grp[gi].depth;
-      int8_t* rowp = p.plane_sel + size_t(p.gorig[gi]) * p.t_max;
-      for (int j0 = threadIdx.x * 16; j0 < sr.T; j0 += kMergeThreads * 16) {
-        int8_t v[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = j0 + e;
-          const int pl = (p.layout == 0) ? r : (p.layout == 1) ? p.R : ((j >= sr.tw) ? r : p.R);
-          v[e] = int8_t(pl);
-        }
-        if (j0 + 16 <= sr.T) {
-          *reinterpret_cast<u32x4*>(rowp + j0) = *reinterpret_cast<const u32x4*>(v);
-        } else {
-          for (int e = 0; j0 + e < sr.T; ++e) rowp[j0 + e] = v[e];
-        }
-      }
-    }
-  }
+  if (h == 0 && cc == 0 && slice == 0) write_plane_sel(p, sr, threadIdx.x, kMergeThreads);
 }
 
 // ---------------------------------------------------------------------------
@@ -870,7 +1016,7 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
   const bool rt = p.layout == 2 && ((p.We % kStep) * int(sizeof(T))) % 16 != 0;
   const void* kern = kerns[rt ? 1 : 0][p.inflight ? 1 : 0][p.page_mode];
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.fused) return e;
   // Merge: 64-wide head-dim slices while they still give one work-group per
   // compute unit, else 32-wide ones (more work-groups for few units).
   // Measured against 32-wide slices up to 1024 work-groups and whole rows

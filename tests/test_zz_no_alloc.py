@@ -47,7 +47,10 @@ def call_both(case, desc, cache, groups, seq_len):
     assert st == 0, rp.STATUS.get(st, st)
     torch.cuda.synchronize()
     b = outputs(case, len(groups))
+    # a workspace whose counters start at zero (as required) and whose
+    # partial area holds garbage
     ws = torch.full((rp.ripe_layout_bytes(desc, rp.RIPE_BYTES_WORKSPACE),), 0xFF, dtype=torch.uint8, device=DEV)
+    ws[:binding.RIPE_WORKSPACE_ZERO_BYTES] = 0
     st = binding.lib.ripe_verify_attn(ctypes.byref(desc), cache.data_ptr(), sl.ctypes.data_as(I32P), gptr, len(garr),
                                       case.n_rows, case.scale, dev.q.data_ptr(), dev.kv_new.data_ptr(),
                                       b[0].data_ptr(), b[1].data_ptr(), b[2].data_ptr(), ws.data_ptr(), ws.numel(),
