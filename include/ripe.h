@@ -144,19 +144,21 @@ typedef struct ripe_group {
  * T = t_max; We = min(W, T)).  The K region comes first, then the V region,
  * with no padding:
  *
- *   FULL     K [B][R][Hkv][T][D]            V [B][R][Hkv][T/32][D][32]
- *   DEEPEST  K [B][Hkv][T][D]               V [B][Hkv][T/32][D][32]
- *   RIPE     K deep [B][Hkv][T][D]          V deep [B][Hkv][T/32][D][32]
+ *   FULL     K [B][R][Hkv][T][D]            V [B][R][Hkv][T/8][D][8]
+ *   DEEPEST  K [B][Hkv][T][D]               V [B][Hkv][T/8][D][8]
+ *   RIPE     K deep [B][Hkv][T][D]          V deep [B][Hkv][T/8][D][8]
  *            then K ring [B][R-1][Hkv][We][D], V ring [B][R-1][Hkv][We*D]
  *
- * Plane p lives at index p-1.  V is stored transposed in blocks of 32
- * positions so that each head dimension's 32 values are contiguous.  RIPE
- * keeps planes 1..R-1 of position j in ring slot j mod We; the deep region
- * holds plane R of every position.  The V ring of one (sequence, plane,
- * head) stores its We slots as floor(We/32) blocks [D][32], followed, when
- * We is not a multiple of 32, by one block [D][We mod 32] holding the last
- * slots: V of slot s, head dimension d sits at element
- *   (s/32)*32*D + d*32 + s%32            for s < F = floor(We/32)*32,
+ * Plane p lives at index p-1.  V is stored transposed in blocks of 8
+ * positions so that each head dimension's 8 values are contiguous (one
+ * 16-byte MFMA operand load for BF16; a commit of a few positions rewrites
+ * one or two small blocks).  RIPE keeps planes 1..R-1 of position j in ring
+ * slot j mod We; the deep region holds plane R of every position.  The V
+ * ring of one (sequence, plane, head) stores its We slots as floor(We/8)
+ * blocks [D][8], followed, when We is not a multiple of 8, by one block
+ * [D][We mod 8] holding the last slots: V of slot s, head dimension d sits
+ * at element
+ *   (s/8)*8*D + d*8 + s%8                for s < F = floor(We/8)*8,
  *   F*D + d*(We - F) + (s - F)           otherwise.  Hence the cache costs
  *   FULL    2*B*Hkv*D*E * R*T
  *   DEEPEST 2*B*Hkv*D*E * T
@@ -169,9 +171,9 @@ typedef struct ripe_group {
  * region (FULL: every plane; DEEPEST and RIPE: the deep plane) becomes a pool
  * of N = n_pages pages, with the same order inside a page:
  *
- *   FULL     K [N][R][Hkv][P][D]            V [N][R][Hkv][P/32][D][32]
- *   DEEPEST  K [N][Hkv][P][D]               V [N][Hkv][P/32][D][32]
- *   RIPE     K pool [N][Hkv][P][D]          V pool [N][Hkv][P/32][D][32]
+ *   FULL     K [N][R][Hkv][P][D]            V [N][R][Hkv][P/8][D][8]
+ *   DEEPEST  K [N][Hkv][P][D]               V [N][Hkv][P/8][D][8]
+ *   RIPE     K pool [N][Hkv][P][D]          V pool [N][Hkv][P/8][D][8]
  *            then the ring exactly as above, one per sequence
  *
  * (K pool, K ring, V pool, V ring), costing 2*Hkv*D*E*(N*P*planes +

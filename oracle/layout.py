@@ -8,20 +8,20 @@ library (which computes addresses in C++).
 Layout (E = element bytes, T = t_max, a multiple of 32; We = min(W, T));
 the K region comes first, then the V region:
 
-* FULL     K [B][R][Hkv][T][D]              V [B][R][Hkv][T/32][D][32]
-* DEEPEST  K [B][Hkv][T][D]                 V [B][Hkv][T/32][D][32]
-* RIPE     K deep [B][Hkv][T][D]            V deep [B][Hkv][T/32][D][32]
+* FULL     K [B][R][Hkv][T][D]              V [B][R][Hkv][T/8][D][8]
+* DEEPEST  K [B][Hkv][T][D]                 V [B][Hkv][T/8][D][8]
+* RIPE     K deep [B][Hkv][T][D]            V deep [B][Hkv][T/8][D][8]
              then ring [B][R-1][Hkv][We][D]   then ring [B][R-1][Hkv][We*D] (below)
 
-V is stored transposed in blocks of 32 positions (each head dimension's 32
-values contiguous).  A ring's V of one (sequence, plane, head) holds its We
-slots as floor(We/32) such blocks [D][32] followed, when We is not a
-multiple of 32, by one narrower block [D][We mod 32] (``ring_v_offset``).
+V is stored transposed in blocks of V_BLOCK = 8 positions (each head
+dimension's 8 values contiguous).  A ring's V of one (sequence, plane, head)
+holds its We slots as floor(We/8) such blocks [D][8] followed, when We is
+not a multiple of 8, by one narrower block [D][We mod 8] (``ring_v_offset``).
 Plane p is stored at index p - 1 (plane R deepest); RIPE keeps position j's
 planes 1..R-1 in ring slot j mod We.
 
 Paged caches (page length P, N pages): the main region becomes a pool,
-K [N][planes][Hkv][P][D] and V [N][planes][Hkv][P/32][D][32] (planes = R for
+K [N][planes][Hkv][P][D] and V [N][planes][Hkv][P/8][D][8] (planes = R for
 FULL, the plane index dropped otherwise), and block k of sequence b
 (positions [kP, kP + P)) lives in page table[b][k]; the RIPE ring stays one
 per sequence.  encode_paged builds it by moving each block of the unpaged
@@ -38,6 +38,7 @@ import numpy as np
 from .ripe_oracle import DEEPEST, FULL, RIPE, LogicalCache, layout_code
 
 ELEM_BYTES = {"f32": 4, "bf16": 2}
+V_BLOCK = 8  # positions per transposed V block
 
 
 def ring_width(W: int, t_max: int) -> int:
@@ -46,13 +47,15 @@ def ring_width(W: int, t_max: int) -> int:
 
 def ring_v_offset(slot: int, d: int, We: int, D: int) -> int:
     """Element offset of V (ring slot, head dimension d) within one
-    (sequence, plane, head) ring of We slots: blocks of 32 slots stored
-    [D][32], the last We mod 32 slots as one block [D][We mod 32]."""
+    (sequence, plane, head) ring of We slots: blocks of V_BLOCK slots stored
+    [D][V_BLOCK], the last We mod V_BLOCK slots as one block
+    [D][We mod V_BLOCK]."""
     if not (0 <= slot < We and 0 <= d < D):
         raise IndexError((slot, d))
-    full = (We // 32) * 32
+    n = V_BLOCK
+    full = (We // n) * n
     if slot < full:
-        return (slot // 32) * 32 * D + d * 32 + slot % 32
+        return (slot // n) * n * D + d * n + slot % n
     w = We - full
     return full * D + d * w + (slot - full)
 
@@ -82,7 +85,7 @@ def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: 
                   D: int):
     """Named array views of a flat element buffer: K and V of the main region
     (FULL planes or the deep plane) and, for RIPE, of the ring.  Main V views
-    are blocked [..., n/32, D, 32]; the ring V view is [B, R-1, Hkv, We*D],
+    are blocked [..., n/V_BLOCK, D, V_BLOCK]; the ring V view is [B, R-1, Hkv, We*D],
     indexed through ring_v_offsets."""
     layout = layout_code(layout)
     T = t_max
@@ -91,7 +94,7 @@ def _region_views(buf_elems: np.ndarray, layout, R: int, W: int, B: int, t_max: 
     else:
         main = (B, Hkv, T, D)
     We = ring_width(W, T) if layout == RIPE else 0
-    parts = [("main", main, 32)]
+    parts = [("main", main, V_BLOCK)]
     if We > 0:
         parts.append(("ring", (B, R - 1, Hkv, We, D), None))
     views = {}
@@ -146,8 +149,8 @@ def encode(cache: LogicalCache) -> np.ndarray:
             kd = kmain[b, p - 1] if cache.layout == FULL else kmain[b]
             vd = vmain[b, p - 1] if cache.layout == FULL else vmain[b]
             kd[:, held] = _bits(kt[:, held], cache.dtype)
-            vblk = _bits(np.swapaxes(vt.reshape(H, T // 32, 32, D), -1, -2), cache.dtype)
-            hb = held.reshape(T // 32, 32)
+            vblk = _bits(np.swapaxes(vt.reshape(H, T // V_BLOCK, V_BLOCK, D), -1, -2), cache.dtype)
+            hb = held.reshape(T // V_BLOCK, V_BLOCK)
             vd[...] = np.where(hb[None, :, None, :], vblk, vd)
     if cache.layout == RIPE and ("K", "ring") in views:
         We = ring_width(cache.W, T)
@@ -188,7 +191,7 @@ def decode(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_max: i
         planes = range(1, R + 1) if layout == FULL else [R]
         for p in planes:
             kd = kmain[b, p - 1] if layout == FULL else kmain[b]          # [H, T, D]
-            vd = vmain[b, p - 1] if layout == FULL else vmain[b]          # [H, T/32, D, 32]
+            vd = vmain[b, p - 1] if layout == FULL else vmain[b]          # [H, T/8, D, 8]
             k = np.moveaxis(val(kd[:, :Tb]), 0, 1)
             v = np.moveaxis(np.swapaxes(val(vd), -1, -2).reshape(Hkv, T, D)[:, :Tb], 0, 1)
             cache.put_range(b, p, 0, k, v)
@@ -215,7 +218,7 @@ def paged_layout_elements(layout, R: int, W: int, B: int, t_max: int, Hkv: int, 
 
 def _pool_views(elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, Hkv: int, D: int, P: int, N: int):
     """K/V views of a paged buffer: pools [N, planes, H, P, D] and
-    [N, planes, H, P/32, D, 32] (planes = 1 unless FULL), rings as unpaged."""
+    [N, planes, H, P/8, D, 8] (planes = 1 unless FULL), rings as unpaged."""
     layout = layout_code(layout)
     planes = R if layout == FULL else 1
     We = ring_width(W, t_max) if layout == RIPE else 0
@@ -225,7 +228,7 @@ def _pool_views(elems: np.ndarray, layout, R: int, W: int, B: int, t_max: int, H
     views, off = {}, 0
     for kind in ("K", "V"):
         views[(kind, "pool")] = elems[off:off + n_pool].reshape(pool) if kind == "K" else \
-            elems[off:off + n_pool].reshape(N, planes, Hkv, P // 32, D, 32)
+            elems[off:off + n_pool].reshape(N, planes, Hkv, P // V_BLOCK, D, V_BLOCK)
         off += n_pool
         if We > 0:
             flat = elems[off:off + n_ring]
@@ -268,12 +271,12 @@ def encode_paged(cache: LogicalCache, table, page_len: int, n_pages: int) -> np.
                 ks = src[("K", "main")][b, p - 1] if cache.layout == FULL else src[("K", "main")][b]
                 vs = src[("V", "main")][b, p - 1] if cache.layout == FULL else src[("V", "main")][b]
                 kblk = ks[:, k * P:(k + 1) * P]                        # [H, P, D]
-                vblk = vs[:, k * P // 32:(k + 1) * P // 32]            # [H, P/32, D, 32]
+                vblk = vs[:, k * P // V_BLOCK:(k + 1) * P // V_BLOCK]  # [H, P/8, D, 8]
                 kd, vd = dst[("K", "pool")][pg, pi], dst[("V", "pool")][pg, pi]
                 both = held & written[pg, pi]
-                vmask = held.reshape(P // 32, 32)
+                vmask = held.reshape(P // V_BLOCK, V_BLOCK)
                 if both.any():
-                    bv = both.reshape(P // 32, 32)
+                    bv = both.reshape(P // V_BLOCK, V_BLOCK)
                     if not (np.array_equal(kd[:, both], kblk[:, both]) and
                             np.array_equal(np.where(bv[None, :, None, :], vd, 0),
                                            np.where(bv[None, :, None, :], vblk, 0))):
@@ -308,7 +311,7 @@ def decode_paged(buf: np.ndarray, layout, dtype: str, R: int, W: int, B: int, t_
                 kd = dst[("K", "main")][b, pi] if full else dst[("K", "main")][b]
                 vd = dst[("V", "main")][b, pi] if full else dst[("V", "main")][b]
                 kd[:, k * P:(k + 1) * P] = src[("K", "pool")][pg, pi]
-                vd[:, k * P // 32:(k + 1) * P // 32] = src[("V", "pool")][pg, pi]
+                vd[:, k * P // V_BLOCK:(k + 1) * P // V_BLOCK] = src[("V", "pool")][pg, pi]
     if ("K", "ring") in src:
         dst[("K", "ring")][...] = src[("K", "ring")]
         dst[("V", "ring")][...] = src[("V", "ring")]

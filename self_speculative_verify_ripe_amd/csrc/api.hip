@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <unordered_set>
 #include <vector>
 
 #include "accept.h"
@@ -993,6 +994,43 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
       }
     }
   }
+  // V blocks a job rewrites.  Two tasks of one launch never touch the same
+  // block (a job's own ranges are disjoint; a job whose blocks meet those of
+  // an earlier job of the launch, such as a sequence sharing a page, starts
+  // a new launch), so the read-modify-write of a block never races.
+  struct Blocks {
+    int s0, ring, blk0, nblk0, blk1, nblk1;
+  };
+  auto blocks_of = [&](const Job& jb) {
+    Blocks k{};
+    const bool ring = d.layout == RIPE_LAYOUT_RIPE && jb.plane_lo < d.R;
+    k.ring = ring ? We : 0;
+    k.s0 = ring ? jb.j0 % We : (table != nullptr ? jb.j0 % P : jb.j0);
+    const int e = k.s0 + jb.n;  // one past the last slot, before a ring's wrap
+    if (!ring || e <= We) {
+      k.blk0 = k.s0 / kVBlock;
+      k.nblk0 = (e - 1) / kVBlock - k.blk0 + 1;
+    } else {  // slots [s0, We) then [0, e - We)
+      const int last = (We - 1) / kVBlock, wrap_last = (e - We - 1) / kVBlock;
+      if (wrap_last >= k.s0 / kVBlock) {
+        k.blk0 = 0;
+        k.nblk0 = last + 1;
+      } else {
+        k.blk0 = k.s0 / kVBlock;
+        k.nblk0 = last - k.blk0 + 1;
+        k.blk1 = 0;
+        k.nblk1 = wrap_last + 1;
+      }
+    }
+    return k;
+  };
+  // a launch's blocks: (region, block) with region = page, or sequence and
+  // main / ring
+  std::unordered_set<int64_t> taken;
+  auto key = [&](const Job& jb, const Blocks& k, int blk) {
+    const int64_t region = k.ring ? 2 * int64_t(jb.b) + 1 : (table != nullptr ? 2 * (int64_t(d.batch) + jb.page) : 2 * int64_t(jb.b));
+    return region * (int64_t(d.t_max) / kVBlock + 1) + blk;
+  };
   std::vector<CommitParams> launches;
   size_t i = 0;
   while (i < jobs.size()) {
@@ -1009,25 +1047,43 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
     p.t_max = d.t_max;
     p.H = d.n_kv_heads;
     p.n_rows = n_rows;
-    int64_t items = 0;
+    int64_t items = 0, vtasks = 0;
     int nj = 0;
+    taken.clear();
     for (; i < jobs.size() && nj < kMaxJobs; ++i) {
       const Job& jb = jobs[i];
+      const Blocks k = blocks_of(jb);
       const int64_t cnt = int64_t(jb.n) * jb.n_planes * per_row_plane;
-      if (nj > 0 && items + cnt > kMaxCommitItems) break;
+      const int64_t vt = int64_t(jb.n_planes) * d.n_kv_heads * (k.nblk0 + k.nblk1);
+      if (nj > 0 && (items + cnt > kMaxCommitItems || vtasks + vt > kMaxCommitItems)) break;
+      bool clash = false;
+      for (int r = 0; r < 2 && !clash; ++r)
+        for (int q = 0; q < (r ? k.nblk1 : k.nblk0) && !clash; ++q)
+          clash = taken.count(key(jb, k, (r ? k.blk1 : k.blk0) + q)) != 0;
+      if (clash) break;  // (never for a launch's first job: its blocks are still free)
+      for (int r = 0; r < 2; ++r)
+        for (int q = 0; q < (r ? k.nblk1 : k.nblk0); ++q) taken.insert(key(jb, k, (r ? k.blk1 : k.blk0) + q));
       CommitJob& cj = p.job[nj++];
       cj.item0 = int32_t(items);
-      cj.j0 = jb.j0;
+      cj.vtask0 = int32_t(vtasks);
+      cj.s0 = k.s0;
       cj.src0 = jb.src0;
       cj.n_rows = jb.n;
+      cj.page = jb.page;
+      cj.ring = k.ring;
       cj.b = uint16_t(jb.b);
       cj.plane_lo = uint8_t(jb.plane_lo);
       cj.n_planes = uint8_t(jb.n_planes);
-      cj.page = jb.page;
+      cj.blk0 = k.blk0;
+      cj.nblk0 = k.nblk0;
+      cj.blk1 = k.blk1;
+      cj.nblk1 = k.nblk1;
       items += cnt;
+      vtasks += vt;
     }
     p.n_jobs = nj;
     p.n_items = int32_t(items);
+    p.n_vtasks = int32_t(vtasks);
     launches.push_back(p);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -1,20 +1,29 @@
 // commit.hip -- scatter accepted draft rows into one recurrent layer's cache.
 //
-// RIPE abstract (zhuanzhiai.com paper page): RIPE keeps the deepest plane at
-// every position and full depth only for a window of recent positions.  A
-// commit therefore writes plane R of every accepted row to the deep region
-// and planes 1..R-1 of the rows that end up inside the window to ring slot
-// j mod We; a position leaving the window needs no copy because its plane R
-// is already in the deep region and the position W later reuses its slot.
-// FULL writes planes 1..R, DEEPEST plane R.  LoopSpec summary (rit.work):
-// rejected rows are simply not committed.
+// RIPE abstract (zhuanzhiai.com paper page, sentence introducing RIPE): RIPE
+// keeps the deepest plane at every position and the other planes only for a
+// window of recent positions.  A commit therefore writes plane R of every
+// accepted row to the deep region and planes 1..R-1 of the rows that end up
+// inside the window to ring slot j mod We; a position leaving the window
+// needs no copy because its plane R is already in the deep region and the
+// position W later reuses its slot.  FULL writes planes 1..R, DEEPEST plane
+// R.  LoopSpec summary (rit.work): rejected rows are simply not committed.
 //
-// One thread copies 8 consecutive head-dim elements of one (row, plane,
-// head): a 16- or 32-byte K row piece, and 8 V elements into the transposed
-// V blocks (32 positions each; a RIPE ring whose width We is not a multiple
-// of 32 ends with one block of We mod 32 slots).  Paged caches: the host cuts jobs at page boundaries
-// and gives each main-region job its page.  Destinations (position, plane, head, element) are
-// distinct across threads, so the writes never race.
+// K rows are contiguous per (position, head): one thread copies 8
+// consecutive head-dim elements (16 or 32 bytes).  V is stored transposed in
+// blocks of 8 slots ([D][8]: each head dimension's 8 values one 16- or
+// 32-byte run, a block 2 or 4 KB at D = 128), so a commit of a few
+// positions touches one or two blocks per (plane, head).  One wavefront per
+// (plane, head, block) rewrites the block's runs whole -- it reads a run
+// unless every slot of it is new, puts the new values in and writes the run
+// back; the other slots keep their bytes -- so the stores cover whole cache
+// lines.  (The cache lines a commit dirties, not the bytes it writes, set
+// what the write-back costs the verify calls that stream the cache next;
+// 32-slot blocks would make a commit of 4 positions dirty 4 times the lines.)
+// Jobs and blocks are planned so that no two tasks of a launch touch one
+// block.
+// Paged caches: the host cuts jobs at page boundaries and gives each
+// main-region job its page.
 #include <hip/hip_runtime.h>
 
 #include "plan.h"
@@ -23,73 +32,112 @@ namespace ripe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item >= p.n_items) return;
+// element offset of the (plane pl, head h) region of a job: K row of slot s
+// at off + s * D; V of slot s, dimension d in its block (see the layout)
+__device__ inline size_t region_off(const CommitParams& p, const CommitJob& jb, int pl, int h, int D) {
+  if (jb.ring > 0) return p.ring_off + ((size_t(jb.b) * (p.R - 1) + (pl - 1)) * p.H + h) * size_t(p.We) * D;
+  if (p.page_len > 0)
+    return (((p.layout == 0) ? size_t(jb.page) * p.R + (pl - 1) : size_t(jb.page)) * p.H + h) * size_t(p.page_len) * D;
+  if (p.layout == 0) return ((size_t(jb.b) * p.R + (pl - 1)) * p.H + h) * size_t(p.t_max) * D;
+  return (size_t(jb.b) * p.H + h) * size_t(p.t_max) * D;
+}
+
+__device__ inline int find_job(const CommitParams& p, int x, bool vtask) {
   int lo = 0, hi = p.n_jobs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.job[mid].item0 <= item)
+    if ((vtask ? p.job[mid].vtask0 : p.job[mid].item0) <= x)
       lo = mid;
     else
       hi = mid - 1;
   }
-  const CommitJob& jb = p.job[lo];
-  constexpr int CH = D / 8;
-  int local = item - jb.item0;
-  const int ch = local % CH;
-  local /= CH;
-  const int h = local % p.H;
-  local /= p.H;
-  const int pi = local % jb.n_planes;
-  const int ri = local / jb.n_planes;
-  const int pl = jb.plane_lo + pi;  // 1-based plane
-  const int j = jb.j0 + ri;
-  const int src = jb.src0 + ri;
-  const size_t Hd = size_t(p.H) * D;
+  return lo;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
+  const int kblocks = (p.n_items + 255) / 256;
   const T* kv = static_cast<const T*>(p.kv_new);
-  const T* ks = kv + (size_t(pl - 1) * p.n_rows + src) * Hd + size_t(h) * D + ch * 8;
-  const T* vs = kv + (size_t(p.R + pl - 1) * p.n_rows + src) * Hd + size_t(h) * D + ch * 8;
-  size_t off;
-  int slot;
-  int full = 1 << 30;  // slots held in 32-wide V blocks; the rest form one narrower block
-  int tail = 0;        // its width
-  if (p.layout == 2 && pl < p.R) {
-    off = p.ring_off + ((size_t(jb.b) * (p.R - 1) + (pl - 1)) * p.H + h) * size_t(p.We) * D;
-    slot = j % p.We;
-    full = p.We / 32 * 32;
-    tail = p.We - full;
-  } else if (p.page_len > 0) {  // paged main region: the job's rows share one page
-    off = (((p.layout == 0) ? size_t(jb.page) * p.R + (pl - 1) : size_t(jb.page)) * p.H + h) *
-          size_t(p.page_len) * D;
-    slot = j % p.page_len;
-  } else if (p.layout == 0) {
-    off = ((size_t(jb.b) * p.R + (pl - 1)) * p.H + h) * size_t(p.t_max) * D;
-    slot = j;
-  } else {
-    off = (size_t(jb.b) * p.H + h) * size_t(p.t_max) * D;
-    slot = j;
+  const size_t Hd = size_t(p.H) * D;
+  if (int(blockIdx.x) < kblocks) {
+    // ---- K: one thread per (row, plane, head, 8-element chunk)
+    const int item = blockIdx.x * 256 + threadIdx.x;
+    if (item >= p.n_items) return;
+    const CommitJob& jb = p.job[find_job(p, item, false)];
+    constexpr int CH = D / 8;
+    int local = item - jb.item0;
+    const int ch = local % CH;
+    local /= CH;
+    const int h = local % p.H;
+    local /= p.H;
+    const int pl = jb.plane_lo + local % jb.n_planes;  // 1-based plane
+    const int ri = local / jb.n_planes;
+    const int slot = jb.ring > 0 ? (jb.s0 + ri) % jb.ring : jb.s0 + ri;
+    const T* ks = kv + (size_t(pl - 1) * p.n_rows + jb.src0 + ri) * Hd + size_t(h) * D + ch * 8;
+    T* kd = static_cast<T*>(p.cache_k) + region_off(p, jb, pl, h, D) + size_t(slot) * D + ch * 8;
+    constexpr int NV = 8 * sizeof(T) / 16;  // 16-byte pieces per 8 elements
+#pragma unroll
+    for (int v = 0; v < NV; ++v) reinterpret_cast<u32x4*>(kd)[v] = reinterpret_cast<const u32x4*>(ks)[v];
+    return;
   }
-  T* kd = static_cast<T*>(p.cache_k) + off + size_t(slot) * D + ch * 8;
-  constexpr int NV = 8 * sizeof(T) / 16;  // 16-byte pieces per 8 elements
+  // ---- V: one wavefront per (plane, head, block); lane l rewrites the runs
+  // of head dimensions l, l + 64, ...
+  const int task = (int(blockIdx.x) - kblocks) * 4 + int(threadIdx.x >> 6);
+  if (task >= p.n_vtasks) return;
+  const int lane = threadIdx.x & 63;
+  const CommitJob& jb = p.job[find_job(p, task, true)];
+  int local = task - jb.vtask0;
+  const int nb = jb.nblk0 + jb.nblk1;
+  const int bi = local % nb;
+  local /= nb;
+  const int blk = bi < jb.nblk0 ? jb.blk0 + bi : jb.blk1 + (bi - jb.nblk0);
+  const int h = local % p.H;
+  const int pl = jb.plane_lo + local / p.H;
+  const int bs = blk * kVBlock;                                     // first slot of the block
+  const int w = jb.ring > 0 ? min(kVBlock, jb.ring - bs) : kVBlock;  // its slots
+  // row of slot s (or -1): main regions s0 + i, rings (s0 + i) mod We
+  auto row_of = [&](int s) -> int {
+    int i = s - jb.s0;
+    if (jb.ring > 0 && i < 0) i += jb.ring;
+    return (i >= 0 && i < jb.n_rows) ? i : -1;
+  };
+  T* vb = static_cast<T*>(p.cache_v) + region_off(p, jb, pl, h, D) + size_t(bs) * D;
+  const T* vsrc = kv + (size_t(p.R + pl - 1) * p.n_rows + jb.src0) * Hd + size_t(h) * D;
+  if (w == kVBlock) {
+    int n_new = 0;
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
-    reinterpret_cast<u32x4*>(kd)[v] = reinterpret_cast<const u32x4*>(ks)[v];
-  T vv[8];
+    for (int s = 0; s < kVBlock; ++s) n_new += row_of(bs + s) >= 0;
+    constexpr int NQ = kVBlock * sizeof(T) / 16;  // 16-byte pieces per run
 #pragma unroll
-  for (int v = 0; v < NV; ++v) reinterpret_cast<u32x4*>(vv)[v] = reinterpret_cast<const u32x4*>(vs)[v];
-  T* vd = static_cast<T*>(p.cache_v) + off;
-  // element (slot, d) of a [D][w] block that starts at slot b0: b0 * D + d * w + (slot - b0)
-  const int b0 = slot < full ? slot / 32 * 32 : full;
-  const int w = slot < full ? 32 : tail;
+    for (int d = lane; d < D; d += 64) {
+      u32x4* run = reinterpret_cast<u32x4*>(vb + size_t(d) * kVBlock);
+      T vals[kVBlock];
+      if (n_new < kVBlock) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vd[size_t(b0) * D + size_t(ch * 8 + e) * w + (slot - b0)] = vv[e];
+        for (int q = 0; q < NQ; ++q) reinterpret_cast<u32x4*>(vals)[q] = run[q];
+      }
+#pragma unroll
+      for (int s = 0; s < kVBlock; ++s) {
+        const int i = row_of(bs + s);
+        if (i >= 0) vals[s] = vsrc[size_t(i) * Hd + d];
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) run[q] = reinterpret_cast<const u32x4*>(vals)[q];
+    }
+  } else {
+    // a ring's narrower last block: element by element (its runs need not
+    // be 16-byte aligned)
+    for (int d = lane; d < D; d += 64)
+      for (int s = 0; s < w; ++s) {
+        const int i = row_of(bs + s);
+        if (i >= 0) vb[size_t(d) * w + s] = vsrc[size_t(i) * Hd + d];
+      }
+  }
 }
 
 template <typename T, int D>
 static hipError_t launch_commit_t(const CommitParams& p, hipStream_t stream) {
-  const int blocks = (p.n_items + 255) / 256;
+  const int blocks = (p.n_items + 255) / 256 + (p.n_vtasks + 3) / 4;
   if (blocks == 0) return hipSuccess;
   void* args[] = {const_cast<CommitParams*>(&p)};
   return hipLaunchKernel(reinterpret_cast<const void*>(&commit_rows<T, D>), dim3(blocks), dim3(256),

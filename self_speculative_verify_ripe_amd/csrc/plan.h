@@ -206,15 +206,26 @@ struct VerifyParams {
   int32_t fused;         // the last item of each unit merges it (else a merge kernel follows)
 };
 
-struct CommitJob {     // rows of one sequence written to one region (24 bytes)
-  int32_t item0;       // first work item
-  int32_t j0;          // destination position of the job's first row
+constexpr int kVBlock = 8;  // positions per transposed V block [D][8]
+
+// Rows of one sequence written to one region (48 bytes).  Row i goes to slot
+// s0 + i of the region (a position, a page slot), or for a RIPE ring to slot
+// (s0 + i) mod We.  Its V blocks (kVBlock slots each; a ring's last may be
+// narrower) are rewritten whole, one wavefront per (plane, head, block):
+// the blocks touched form one or two ranges [blk0, blk0 + nblk0) and
+// [blk1, blk1 + nblk1) that share no block.
+struct CommitJob {
+  int32_t item0;       // first K work item
+  int32_t vtask0;      // first V block task
+  int32_t s0;          // slot of the job's first row
   int32_t src0;        // kv_new row of the job's first row
   int32_t n_rows;
+  int32_t page;        // paged cache, main region: the page holding all the job's rows
+  int32_t ring;        // We for a RIPE ring job, 0 for the main region
   uint16_t b;
   uint8_t plane_lo;    // first plane written (1-based)
   uint8_t n_planes;
-  int32_t page;        // paged cache, main region: the page holding all the job's rows
+  int32_t blk0, nblk0, blk1, nblk1;
 };
 
 struct CommitParams {
@@ -223,6 +234,7 @@ struct CommitParams {
   const void* kv_new;
   uint64_t ring_off;
   int32_t layout, R, We, t_max, H, n_rows, n_jobs, n_items;
+  int32_t n_vtasks;         // V block tasks (after the K items)
   int32_t page_len;         // paged cache: positions per page (0: unpaged)
   CommitJob job[kMaxJobs];  // a RIPE job with plane_lo < R writes the ring
 };

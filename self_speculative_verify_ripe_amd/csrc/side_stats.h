@@ -20,7 +20,7 @@ struct PeGroup {       // one group (16 bytes)
 
 struct PosErrParams {
   const void* cache_k;  // FULL K region [B][R][Hkv][t_max][D]
-  const void* cache_v;  // FULL V region [B][R][Hkv][t_max/32][D][32]
+  const void* cache_v;  // FULL V region [B][R][Hkv][t_max/8][D][8]
   const void* q;        // [n_rows][Hq][D], storage dtype
   const float* o;       // FULL output at the group's depth, [n_rows][Hq][D] fp32
   const float* lse;     // its natural-log LSE, [n_rows][Hq]

@@ -20,8 +20,8 @@
 // can be told apart.
 //
 // How: one work-group per (group, KV head, 32 prefix positions).  The tile's
-// K and V rows of planes r and R (four contiguous 32-position blocks of the
-// FULL layout) are staged through LDS -- V transposed to position-major --
+// K and V rows of planes r and R (32 contiguous positions of the FULL
+// layout: K rows, V four [D][8] blocks) are staged through LDS -- V transposed to position-major --
 // and each thread keeps a 1/8 slice of one position's four rows in
 // registers.  The group's query columns and their FULL outputs are staged
 // 16 at a time and read back by broadcast; the two dot products per column
@@ -96,7 +96,6 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
   const int tid = threadIdx.x;
   constexpr int NC = D * E / 128;  // 16-byte chunks per thread per array (32 x D elements)
   constexpr int CR = D / VE;       // K: chunks per row
-  constexpr int CD = 32 / VE;      // V: chunks per head dimension
   u32x4 buf[4][NC];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -108,9 +107,9 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
       if (a < 2) {  // K [t][D]: row-major
         const T* src = static_cast<const T*>(p.cache_k) + (head * p.t_max + j0) * D;
         buf[a][c] = *reinterpret_cast<const u32x4*>(src + size_t(idx / CR) * D + (idx % CR) * VE);
-      } else {      // V [D][32] per block
-        const T* src = static_cast<const T*>(p.cache_v) + (head * (p.t_max / 32) + j0 / 32) * size_t(D) * 32;
-        buf[a][c] = *reinterpret_cast<const u32x4*>(src + size_t(idx / CD) * 32 + (idx % CD) * VE);
+      } else {      // V: the tile is four contiguous blocks [D][8]
+        const T* src = static_cast<const T*>(p.cache_v) + (head * p.t_max + j0) * D;
+        buf[a][c] = *reinterpret_cast<const u32x4*>(src + size_t(idx) * VE);
       }
     }
   }
@@ -155,9 +154,10 @@ __global__ __launch_bounds__(kPeThreads) void position_error_kernel(const PosErr
       const int idx = tid + c * kPeThreads;
       if (a < 2) {
         *reinterpret_cast<u32x4*>(&sk[a][idx / CR][(idx % CR) * VE]) = buf[a][c];
-      } else {  // transposed into [t][D]
+      } else {  // transposed into [t][D]: chunk idx holds slots t0 .. t0 + VE - 1 of dimension d
         const T* e = reinterpret_cast<const T*>(&buf[a][c]);
-        const int d = idx / CD, t0 = (idx % CD) * VE;
+        const int el = idx * VE;
+        const int d = (el % (8 * D)) / 8, t0 = el / (8 * D) * 8 + el % 8;
 #pragma unroll
         for (int x = 0; x < VE; ++x) sv[a - 2][t0 + x][d] = e[x];
       }

@@ -14,18 +14,19 @@
 //   chunk, chunk of <= S key positions of one segment).  Each wavefront
 //   streams 32-position steps straight from HBM into VGPRs in MFMA operand
 //   order: K rows (row-major [pos][D]) feed the A operand of S^T = K Q^T, and
-//   the V blocks (stored transposed, [D][32] per 32 positions) feed the A
-//   operand of O^T += V^T P^T, so no LDS staging or shuffles are needed on
-//   the hot loop.  The next step's K (V) loads are issued as soon as the
-//   current step's K (V) registers are consumed.  Online softmax in the log2
-//   domain with one max reduction per step.  The four wavefronts' (m, l, O)
-//   are merged through LDS into one fp32 partial per work item.  A second
-//   kernel, one work-group per (sequence, KV head, column chunk), merges the
-//   partials in split order, normalises, and writes out (storage dtype,
-//   round-to-nearest-even), the natural-log LSE and plane_sel.  (The merge
-//   is not folded into the first kernel: cross-work-group hand-off on this
-//   multi-die part needs a device-scope fence per work-group, i.e. an L2
-//   writeback and invalidate each, which costs far more than the launch.)
+//   the V blocks (stored transposed, [D][8] per 8 positions, so each lane's
+//   8 slots of one head dimension are one 16-byte load) feed the A operand
+//   of O^T += V^T P^T, so no LDS staging or shuffles are needed on the hot
+//   loop.  The next step's K (V) loads are issued as soon as the current
+//   step's K (V) registers are consumed.  Online softmax in the log2 domain
+//   with one max reduction per step.  The four wavefronts' (m, l, O) are
+//   merged through LDS into one fp32 partial per work item.  The partials
+//   of a (sequence, KV head, column chunk) unit are merged in split order,
+//   normalised and written out (storage dtype, round-to-nearest-even) with
+//   the natural-log LSE and plane_sel: by the unit's last work item to
+//   finish when all of the unit's items run on one XCD (the planner places
+//   them so when a unit has at most 8 items; the hand-off then stays inside
+//   one L2), else by a second kernel, one work-group per unit.
 //
 // MFMA shapes: bf16 v_mfma_f32_16x16x32_bf16 (8 bf16 per lane per operand);
 // fp32 v_mfma_f32_16x16x4_f32 (no reduced-precision path).  For the
@@ -89,10 +90,6 @@ struct Op<__bf16> {
     else
       v[0][w] = (v[0][w] & 0xFFFF0000u) | (bits & 0xFFFFu);
   }
-  // one element through a buffer resource (0 past its end)
-  __device__ static inline uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-  }
 };
 
 // fp32: one 16-byte chunk = 4 elements = four 16x16x4 MFMAs.
@@ -135,10 +132,6 @@ struct Op<float> {
   }
   __device__ static inline void put_elem(u32x4 (&v)[VCH], int e, const void* base, size_t idx) {
     v[e >> 2][e & 3] = static_cast<const uint32_t*>(base)[idx];
-  }
-  __device__ static inline void put_bits(u32x4 (&v)[VCH], int e, uint32_t bits) { v[e >> 2][e & 3] = bits; }
-  __device__ static inline uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
 };
 
@@ -366,9 +359,11 @@ constexpr int verify_lds_bytes() {
 // inside one page (read from that page), 2 when runs may span pages (such a
 // run is read step by step: each 32-position step lies inside one page); 0
 // unpaged.  The step-by-step code is compiled only into PG = 2, whose loop it
-// slows.  RT: the RIPE ring's last V block (We mod 32 slots) is too narrow for
-// 16-byte loads of 8 slots, so its step is read one element at a time; the
-// code is compiled only into the launches whose window needs it.
+// slows.  RT: a BF16 ring of odd width We ends with a V block of odd width
+// (We mod 8 slots) whose runs need not start on a dword, so that block is
+// read with a shift; the code is compiled only into the launches whose
+// window needs it (fp32 runs and even widths start on a dword, which is all
+// a 16-byte buffer load needs).
 template <typename T, int D, int NB, bool INF, int PG = 0, bool RT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
@@ -480,7 +475,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     c.depth = pc.depth;
     c.ring = pc.kind == kSegRing;
     // slots from the run's start to the end of the region's V blocks: the
-    // ring's last block is narrower when We is not a multiple of 32
+    // ring's last block is narrower when We is not a multiple of 8
     c.vlim = c.ring ? p.We - pc.c0 : (1 << 30);
     const bool plane_paged = PG > 0 && !c.ring;
     c.per_step = PG == 2 && plane_paged && (pc.c0 + pc.len - 1) / P != pc.c0 / P;
@@ -517,7 +512,7 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   // is unconditional and the wait counts stay exact.
   constexpr uint32_t kOutOfRange = 0x80000000u;
   // A run spanning pages: the step's K rows are one 32-row run of its page
-  // and its V values one [D][32] block, so each step gets resources of its
+  // and its V values four [D][8] blocks, so each step gets resources of its
   // own.
   auto step_base = [&](const Ctx& c, int st) -> size_t {
     const Piece pc = tab.piece[c.r];
@@ -536,29 +531,36 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
 #pragma unroll
       for (int cch = 0; cch < KC; ++cch) k[mb][cch] = bload16(rs, base + (4 * mb * D + cch * 4 * VEC) * E);
   };
-  // The step's V block holds w slots [D][w] (w = 32 but for a ring's last
-  // block); lane group lg takes slots 8 lg .. 8 lg + 7 of head dimension
-  // ln + 16 db.
+  // V is stored in blocks of 8 slots [D][8] (a ring's last block holds
+  // We mod 8 slots [D][w]): lane group lg takes the block of the step's slots
+  // 8 lg .. 8 lg + 7, head dimension ln + 16 db.  A lane group past the
+  // ring's end loads nothing (its values are masked anyway).
   auto load_v = [&](const Ctx& c, int st, bool live, u32x4 (&v)[DB][VCH]) {
     __amdgpu_buffer_rsrc_t rs = c.vrs;
-    const int w = min(kStep, c.vlim - st * kStep);
-    uint32_t base = live ? uint32_t(st * kStep * D + ln * w + 8 * lg) * E : kOutOfRange;
-    if (PG == 2 && c.per_step) {  // w = 32: the step is one whole V block
+    const int s0 = st * kStep + 8 * lg;
+    const int w = min(8, c.vlim - s0);  // differs between lane groups only in a ring's last step
+    uint32_t base = live && w > 0 ? uint32_t(s0 * D + ln * w) * E : kOutOfRange;
+    if (PG == 2 && c.per_step) {  // w = 8: the step is four whole V blocks
       rs = make_rsrc(static_cast<const T*>(p.cache_v) + step_base(c, st), uint32_t(kStep) * D * E);
-      base = live ? uint32_t(ln * kStep + 8 * lg) * E : kOutOfRange;
+      base = live ? uint32_t(8 * lg * D + ln * 8) * E : kOutOfRange;
     }
-    if (RT && live && (w * E) % 16 != 0) {
-      // a narrow block whose rows are not 16-byte aligned: element loads
-      // (slots past w read as zero and are masked below anyway)
+    if constexpr (RT && sizeof(T) == 2) {
+      // A BF16 ring of odd width ends with a narrow block of odd width, whose
+      // runs start 2 bytes into a dword for every other head dimension, and
+      // a 16-byte buffer load ignores the low two address bits.  So every V
+      // load of this variant is taken from the dword boundary below and
+      // moved down by (off & 2) bytes (no move for aligned runs); slots past
+      // w hold other runs' values and are masked below.  The move is done on
+      // every load, without a branch: the same code under a branch taken
+      // only for the ring's last step made the kernel compute wrong values
+      // in steps that never took it (measured; the cause was not found).
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int cch = 0; cch < VCH; ++cch) v[db][cch] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t o = (8 * lg + e < w) ? base + uint32_t(16 * db * w + e) * E : kOutOfRange;
-          O::put_bits(v[db], e, O::bload_elem(rs, o));
-        }
+        const uint32_t off = w > 0 ? base + uint32_t(16 * db * w) * E : kOutOfRange;
+        const u32x4 x = bload16_stream(rs, off & ~3u);
+        const uint32_t s = (off & 2u) * 8u;
+        v[db][0] = u32x4{__builtin_amdgcn_alignbit(x[1], x[0], s), __builtin_amdgcn_alignbit(x[2], x[1], s),
+                         __builtin_amdgcn_alignbit(x[3], x[2], s), __builtin_amdgcn_alignbit(0u, x[3], s)};
       }
       return;
     }
@@ -1011,9 +1013,9 @@ static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, con
        {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0, true>),
         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1, true>),
         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2, true>)}}};
-  // element loads for the ring's last V block only where its rows are not
-  // 16-byte aligned
-  const bool rt = p.layout == 2 && ((p.We % kStep) * int(sizeof(T))) % 16 != 0;
+  // BF16 rings of odd width: their last V block has runs that start 2 bytes
+  // into a dword
+  const bool rt = sizeof(T) == 2 && p.layout == 2 && p.We % 2 != 0;
   const void* kern = kerns[rt ? 1 : 0][p.inflight ? 1 : 0][p.page_mode];
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess || p.fused) return e;

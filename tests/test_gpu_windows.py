@@ -1,10 +1,11 @@
 """RIPE windows of any width W >= 0 on the GPU, against the float64 oracle.
 
-The ring of We = min(W, t_max) slots keeps its V in 32-slot blocks plus one
-narrower block for the last We mod 32 slots (include/ripe.h).  Widths below
-cover: narrow blocks whose rows are not 16-byte aligned (bf16: We mod 8 != 0;
-fp32: We mod 4 != 0), which the kernel reads element by element, aligned
-narrow blocks, and rings wider than a 32-position step.  Checks: outputs
+The ring of We = min(W, t_max) slots keeps its V in 8-slot blocks plus one
+narrower block for the last We mod 8 slots (include/ripe.h).  Widths below
+cover: BF16 narrow blocks of odd width, whose runs may start 2 bytes into a
+dword (the kernel shifts them into place), narrow blocks whose runs start on
+a dword but not on 16 bytes (We mod 8 in {2, 4, 6}; fp32 at any width), and
+rings wider than a 32-position step.  Checks: outputs
 within tolerance and plane_sel exact; the RIPE identities bit-exact at any W
 (W >= T equals FULL); a window as long as the draft block (W = k) verifying
 each block identically alone and batched; committed bytes bit-exact,
@@ -23,7 +24,7 @@ from gpu_util import DEV, Device, check, gpu_verify, make_desc, oracle_cache, up
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = [1, 3, 4, 5, 12, 40, 100]
+WIDTHS = [1, 3, 4, 5, 6, 12, 40, 50, 100]
 
 
 def run_case(case, groups, W, split_len=0, tag=""):

@@ -157,17 +157,19 @@ def test_encode_size_and_round_trip(layout, dtype, W):
 
 
 @pytest.mark.parametrize("We,slot,d,want", [
-    # D = 4.  Windows that are multiples of 32: blocks [D][32] only.
-    (32, 5, 2, 2 * 32 + 5), (64, 37, 1, 32 * 4 + 1 * 32 + 5),
-    # windows below 32: one block [D][We]
-    (8, 3, 3, 3 * 8 + 3), (12, 7, 3, 3 * 12 + 7), (1, 0, 2, 2), (5, 4, 1, 1 * 5 + 4),
-    # 32-slot blocks, then a narrower block [D][We mod 32] for the last slots
-    (40, 35, 2, 32 * 4 + 2 * 8 + 3), (40, 31, 3, 3 * 32 + 31), (100, 70, 1, 2 * 32 * 4 + 1 * 32 + 6),
-    (100, 99, 3, 96 * 4 + 3 * 4 + 3), (70, 64, 0, 64 * 4),
+    # D = 4, so a full block [D][8] holds 32 elements.  Windows that are
+    # multiples of 8: full blocks only (slot s: block s // 8, then d * 8 + s % 8)
+    (32, 5, 2, 2 * 8 + 5), (64, 37, 1, 4 * 32 + 1 * 8 + 5), (8, 3, 3, 3 * 8 + 3),
+    (40, 35, 2, 4 * 32 + 2 * 8 + 3), (40, 31, 3, 3 * 32 + 3 * 8 + 7),
+    # windows below 8: one block [D][We]
+    (1, 0, 2, 2), (5, 4, 1, 1 * 5 + 4), (3, 2, 3, 3 * 3 + 2),
+    # 8-slot blocks, then a narrower block [D][We mod 8] for the last slots
+    (12, 7, 3, 3 * 8 + 7), (12, 10, 3, 8 * 4 + 3 * 4 + 2), (100, 70, 1, 8 * 32 + 1 * 8 + 6),
+    (100, 99, 3, 96 * 4 + 3 * 4 + 3), (70, 64, 0, 64 * 4), (70, 69, 3, 64 * 4 + 3 * 6 + 5),
 ])
 def test_ring_v_offsets_hand_computed(We, slot, d, want):
     """The ring's V offsets written out by hand for the block rule the
-    layout statement gives (blocks of 32 slots, then the remaining slots as
+    layout statement gives (blocks of 8 slots, then the remaining slots as
     one narrower block)."""
     assert lay.ring_v_offset(slot, d, We, 4) == want
     offs = lay.ring_v_offsets(We, 4)
@@ -177,7 +179,7 @@ def test_ring_v_offsets_hand_computed(We, slot, d, want):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("W", [12, 40, 100])
 def test_encoder_ring_offsets_any_window(dtype, W):
-    """A single ring element of a window that is not a multiple of 32 lands
+    """A single ring element of a window that is not a multiple of 8 lands
     where the block rule puts it, in K and V."""
     R, B, T, H, D = 3, 2, 128, 2, 4
     c = ro.LogicalCache("ripe", dtype, R, W, B, T, H, D)
@@ -223,13 +225,13 @@ def test_encoder_offsets_match_layout_statement(dtype):
         for p, (kv, vv) in marks.items():
             if layout == "full":
                 ko = (((b * R + (p - 1)) * H + h) * T + j) * D + d
-                vo = n_k + ((((b * R + (p - 1)) * H + h) * (T // 32) + j // 32) * D + d) * 32 + j % 32
+                vo = n_k + ((((b * R + (p - 1)) * H + h) * (T // 8) + j // 8) * D + d) * 8 + j % 8
             elif layout == "deepest" or p == R:
                 ko = ((b * H + h) * T + j) * D + d
-                vo = n_k + (((b * H + h) * (T // 32) + j // 32) * D + d) * 32 + j % 32
+                vo = n_k + (((b * H + h) * (T // 8) + j // 8) * D + d) * 8 + j % 8
             else:
                 deep = B * H * T * D
-                We, BW = W, min(32, W)
+                We, BW = W, min(8, W)
                 slot = j % We
                 ko = deep + (((b * (R - 1) + (p - 1)) * H + h) * We + slot) * D + d
                 vo = n_k + deep + ((((b * (R - 1) + (p - 1)) * H + h) * (We // BW) + slot // BW)

@@ -64,7 +64,7 @@ def test_round_trip_and_block_placement(layout, P):
                 ku = u[("K", "main")][b, pi] if full else u[("K", "main")][b]
                 vu = u[("V", "main")][b, pi] if full else u[("V", "main")][b]
                 assert np.array_equal(pv[("K", "pool")][table[b, k], pi], ku[:, k * P:(k + 1) * P])
-                assert np.array_equal(pv[("V", "pool")][table[b, k], pi], vu[:, k * P // 32:(k + 1) * P // 32])
+                assert np.array_equal(pv[("V", "pool")][table[b, k], pi], vu[:, k * P // 8:(k + 1) * P // 8])
     unused = np.setdiff1d(np.arange(N), table.ravel())
     assert np.all(pv[("K", "pool")][unused] == 0x7FC00000)
 
