@@ -441,6 +441,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     p.n_pieces = 0;
     p.n_refs = 0;
     p.inflight = 0;
+    p.k_stream = 0;
     p.scale_log2 = float(double(softmax_scale) * 1.4426950408889634);
     return lp;
   };
@@ -450,6 +451,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     const int g0 = sc.count[b], gc = sc.count[b + 1] - sc.count[b];
     if (gc == 0) continue;
     int nq = 0;
+    bool mixed = false;  // groups at several depths
     for (int k = 0; k < gc; ++k) {
       const ripe_group_t& g = groups[sc.order[g0 + k]];
       grp[k].row_start = g.row_start;
@@ -457,6 +459,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       grp[k].depth = uint8_t(g.depth);
       grp[k].seq = 0;
       nq += g.n_rows * G;
+      mixed = mixed || g.depth != groups[sc.order[g0]].depth;
     }
     const int T = seq_len[b];
     // the sequence's in-flight parent block: the same for all its groups
@@ -611,6 +614,9 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       sr.hole = uint16_t(fl.hole);
       sr.ring_base = uint16_t(fl.ring_base);
       if (kp > 0) p.inflight = 1;
+      // a launch verifying several depths of one sequence streams its K rows
+      // (the one-call-per-step pattern; see the verify kernel's load policy)
+      if (mixed) p.k_stream = 1;
       for (int k = 0; k < gc; ++k) {
         p.grp[p.n_grp] = grp[k];
         p.grp[p.n_grp].seq = uint8_t(p.n_seq);

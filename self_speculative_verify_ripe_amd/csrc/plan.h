@@ -204,6 +204,7 @@ struct VerifyParams {
   int32_t page_mode;     // 0 unpaged, 1 every prefix-plane piece in one page, 2 pieces may span pages
   int32_t n_refs;        // paged cache: entries of ItemTable::pages used past kMaxPieces
   int32_t fused;         // the last item of each unit merges it (else a merge kernel follows)
+  int32_t k_stream;      // K rows non-temporal: some sequence has groups at several depths
 };
 
 constexpr int kVBlock = 8;  // positions per transposed V block [D][8]

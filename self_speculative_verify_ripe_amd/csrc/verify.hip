@@ -184,12 +184,20 @@ __device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 // The same load with the non-temporal (evict-first) cache policy, sc0 | nt,
 // for the V blocks, which are read once.  Measured per call against the
-// default policy: c3 -4%, c5 FULL -4%, c5 RIPE -8%, c4 -2%; giving the K rows
-// the same hint as well helps c4 (-15%) but costs c3 and c5, and K alone helps
-// none.
+// default policy: c3 -4%, c5 FULL -4%, c5 RIPE -8%, c4 -2%.  The K rows take
+// it only in launches that verify several depths of one sequence (the policy
+// bit kPolKStream): in that pattern -- one call per layer and step, each
+// right after a commit -- K rows loaded with the default policy evict the
+// commit's dirty lines from the caches, and their write-back slows the call
+// (c4: 60.6 -> 54.2 us, the same as without a commit); where each call
+// verifies one depth it costs c2 (+6%, whose steps reuse the last-level
+// cache) and c5 (+3%) and gains c3 2%.
 __device__ inline u32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 3));
 }
+
+constexpr int kPolOddRing = 1;
+constexpr int kPolKStream = 2;
 
 // Running softmax state of one wavefront for its NB 16-column blocks.  The
 // reference maximum m only moves when a step's maximum exceeds it by more than
@@ -359,12 +367,13 @@ constexpr int verify_lds_bytes() {
 // inside one page (read from that page), 2 when runs may span pages (such a
 // run is read step by step: each 32-position step lies inside one page); 0
 // unpaged.  The step-by-step code is compiled only into PG = 2, whose loop it
-// slows.  RT: a BF16 ring of odd width We ends with a V block of odd width
-// (We mod 8 slots) whose runs need not start on a dword, so that block is
-// read with a shift; the code is compiled only into the launches whose
-// window needs it (fp32 runs and even widths start on a dword, which is all
-// a 16-byte buffer load needs).
-template <typename T, int D, int NB, bool INF, int PG = 0, bool RT = false>
+// slows.  POL, BF16 only: load-policy bits.  kPolOddRing: a ring of odd width
+// We ends with a V block of odd width (We mod 8 slots) whose runs need not
+// start on a dword, so V is read with a shift; the code is compiled only
+// into the launches whose window needs it (fp32 runs and even widths start
+// on a dword, which is all a 16-byte buffer load needs).  kPolKStream: K rows
+// are loaded non-temporally (see bload16_stream).
+template <typename T, int D, int NB, bool INF, int PG = 0, int POL = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(waves_per_simd<T, D, NB>())))
 void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
@@ -375,6 +384,8 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   constexpr int DB = D / 16;         // 16-wide head-dim blocks of the output
   constexpr int CQ = 16 * NB;        // query columns per work-group
   constexpr int E = sizeof(T);
+  constexpr bool RT = (POL & kPolOddRing) != 0;
+  constexpr bool KNT = (POL & kPolKStream) != 0;
   constexpr int TPC = kThreads / CQ;  // epilogue threads per column
   constexpr int DPT = D / TPC;        // head-dim values per epilogue thread
   const int lane = threadIdx.x & 63;
@@ -529,7 +540,13 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int cch = 0; cch < KC; ++cch) k[mb][cch] = bload16(rs, base + (4 * mb * D + cch * 4 * VEC) * E);
+      for (int cch = 0; cch < KC; ++cch) {
+        const uint32_t o = base + (4 * mb * D + cch * 4 * VEC) * E;
+        if constexpr (KNT)
+          k[mb][cch] = bload16_stream(rs, o);
+        else
+          k[mb][cch] = bload16(rs, o);
+      }
   };
   // V is stored in blocks of 8 slots [D][8] (a ring's last block holds
   // We mod 8 slots [D][w]): lane group lg takes the block of the step's slots
@@ -994,29 +1011,42 @@ __global__ __launch_bounds__(kMergeThreads) void verify_merge_kernel(const Verif
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// The verify kernel for a launch's in-flight and paging modes and load
+// policy bits.  Only BF16 instantiates policies other than 0.
+template <typename T, int D, int NB, int POL>
+static const void* pick_verify(bool inf, int page_mode) {
+  if constexpr (POL != 0 && sizeof(T) != 2) {
+    return nullptr;
+  } else {
+    static const void* const k[2][3] = {
+        {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0, POL>),
+         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1, POL>),
+         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2, POL>)},
+        {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0, POL>),
+         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1, POL>),
+         reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2, POL>)}};
+    return k[inf ? 1 : 0][page_mode];
+  }
+}
+
 template <typename T, int D, int NB>
 static hipError_t launch_verify_t(const VerifyParams& p, const ItemTable& t, const UnitTable& u,
                                   hipStream_t stream) {
   if (p.n_wg <= 0) return hipSuccess;
   const int grid = p.n_blocks;
   void* args[] = {const_cast<VerifyParams*>(&p), const_cast<ItemTable*>(&t)};
-  const void* const kerns[2][2][3] = {
-      {{reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2>)},
-       {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2>)}},
-      {{reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 0, true>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 1, true>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, false, 2, true>)},
-       {reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 0, true>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 1, true>),
-        reinterpret_cast<const void*>(&verify_attn_kernel<T, D, NB, true, 2, true>)}}};
-  // BF16 rings of odd width: their last V block has runs that start 2 bytes
-  // into a dword
-  const bool rt = sizeof(T) == 2 && p.layout == 2 && p.We % 2 != 0;
-  const void* kern = kerns[rt ? 1 : 0][p.inflight ? 1 : 0][p.page_mode];
+  int pol = 0;
+  if constexpr (sizeof(T) == 2) {
+    // BF16 rings of odd width: their last V block has runs that start 2
+    // bytes into a dword
+    if (p.layout == 2 && p.We % 2 != 0) pol |= kPolOddRing;
+    if (p.k_stream) pol |= kPolKStream;
+  }
+  const bool inf = p.inflight != 0;
+  const void* kern = pol == 0                 ? pick_verify<T, D, NB, 0>(inf, p.page_mode)
+                     : pol == kPolOddRing     ? pick_verify<T, D, NB, kPolOddRing>(inf, p.page_mode)
+                     : pol == kPolKStream     ? pick_verify<T, D, NB, kPolKStream>(inf, p.page_mode)
+                                              : pick_verify<T, D, NB, kPolOddRing | kPolKStream>(inf, p.page_mode);
   hipError_t e = hipLaunchKernel(kern, dim3(grid), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess || p.fused) return e;
   // Merge: 64-wide head-dim slices while they still give one work-group per

@@ -86,6 +86,32 @@ def test_window_of_the_draft_length_batched_equals_alone():
         assert torch.equal(ps[gi], p1[0])
 
 
+@pytest.mark.parametrize("W", [3, 5, 6, 64])
+def test_two_depths_per_sequence_any_window(W):
+    """Each sequence's rows split into two groups at different depths in one
+    call -- the launches that stream their K rows non-temporally -- with
+    rings of odd width (whose V is also read with a shift) and even width,
+    against the oracle; every group alone equals the batched call bit for
+    bit."""
+    case = make_case("c3", B=4, T_range=(3, 150), R=6, k=8, Hkv=2, Hq=8, W=W)
+    groups = []
+    for b in range(case.B):
+        s, n = case.blocks[b]
+        groups += [Group(b, (1, 2, 3, 5)[b], s, n // 2), Group(b, 4 + b % 2, s + n // 2, n - n // 2)]
+    print(f"[case] two depths W={W} T={list(case.seq_len)}", flush=True)
+    oc = oracle_cache(case, "ripe", W=W)
+    cache = upload(olay.encode(oc))
+    dev = Device(case)
+    desc = make_desc(case, "ripe", W=W, split_len=32)
+    out, lse, ps = gpu_verify(desc, cache, case, dev, groups)
+    check(case, groups, (out, lse, ps), ro.verify(oc, groups, case.q, case.kv_new, case.scale, case.Hq),
+          tag=f"two depths W={W}")
+    for gi, g in enumerate(groups):
+        o1, l1, _ = gpu_verify(desc, cache, case, dev, [g])
+        rows = slice(g.row_start, g.row_start + g.n_rows)
+        assert torch.equal(out[rows], o1[rows]) and torch.equal(lse[rows], l1[rows]), f"group {gi}"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("W", [3, 12, 40, 100])
 def test_commit_any_window_bytes(dtype, W):
