@@ -653,7 +653,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "ripe_verify_attn call = verify_attn_kernel + verify_merge_kernel",
+                     "kernel": "ripe_verify_attn call = verify_attn_kernel (units merged in the kernel; verify_merge_kernel follows only launches whose units have more than 8 split items)",
                      "avg_call_us": round(r["avg_call_us"], 2),
                      "alg_bytes_per_call": r["alg_bytes_per_call"]},
         "wall_s": round(r["wall"], 3),
