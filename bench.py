@@ -526,7 +526,6 @@ def run_side_stats(reps: int = 20, warmup: int = 3, depths=(4, 16, 28)):
     squared error of rounding that output to bf16."""
     import torch
     import self_speculative_verify_ripe_amd as rp
-    from self_speculative_verify_ripe_amd.side_stats import tail_statistics
     from workloads import make_case
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -580,7 +579,12 @@ def run_side_stats(reps: int = 20, warmup: int = 3, depths=(4, 16, 28)):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
-            st = tail_statistics(err[0].cpu().numpy(), T, case.W, cond=cond[0].cpu().numpy())
+            stats = torch.empty((1, rp.RIPE_TAIL_STATS), dtype=torch.float64, device=dev)
+            rp.ripe_position_error_tail(err, [T], case.W, stats, cond=cond, stream=stream)
+            torch.cuda.synchronize()
+            st = {k: (None if v != v else v) for k, v in zip(rp.TAIL_FIELDS, stats[0].cpu().tolist())}
+            for k in ("tail_positions", "ill_conditioned", "positions"):
+                st[k] = None if st[k] is None else int(st[k])
             exact = {}
             for lay in ("deepest", "ripe"):
                 d, c, wsv = caches[lay]
@@ -594,8 +598,8 @@ def run_side_stats(reps: int = 20, warmup: int = 3, depths=(4, 16, 28)):
             per_depth[f"r={r}"] = {
                 "call_us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                 "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                **{k: rnd(v) for k, v in st.items() if k != "positions"},
-                "first_order_sq_err": float(err[0, :T].sum()),
+                **{k: rnd(v) for k, v in st.items() if k not in ("positions", "total")},
+                "first_order_sq_err": st["total"],
                 "deepest_sq_err": exact["deepest"], "ripe_sq_err": exact["ripe"],
                 "bf16_rounding_sq_err": floor}
         res[conv] = per_depth

@@ -491,6 +491,44 @@ ripe_status_t ripe_position_error(const ripe_desc_t* desc, const void* cache, co
                                   float* cond, float* out_f32, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * ripe_position_error_tail -- the two tail figures of the error rows that
+ * ripe_position_error writes, per row.
+ *
+ * Source: RIPE abstract (zhuanzhiai.com paper page), the sentences on the
+ * error's tail: a small share of positions (1%) carries most of the error of
+ * the deepest-only cache, and a window of recent positions at full depth
+ * removes most of those tail positions.  Read per row (one group) as: the
+ * tail is the n = max(1, floor(tail_frac * T)) largest e_j (n = 0 when
+ * T = 0), ties going to the lower position; its share of sum_j e_j; the
+ * fraction of its positions among the last W; and the share of sum_j e_j
+ * that the last W positions carry.
+ *
+ *  err        device float [n_rows][row_stride]: e_j >= 0 (finite), entries
+ *             at j >= T[i] ignored; e.g. ripe_position_error's err with
+ *             row_stride = t_max.
+ *  cond       optional device float [n_rows][row_stride] (its cond): counts
+ *             the positions with cond > 1 (ill-conditioned e_j) and their
+ *             share; NULL: those outputs are NaN.
+ *  T          host int32 [n_rows]: prefix length of each row, 0..row_stride
+ *             (RIPE_ERANGE otherwise).
+ *  window     W >= 0.
+ *  tail_frac  in (0, 1] (0.01 for the pages' 1%).
+ *  stats      device double [n_rows][RIPE_TAIL_STATS], 8-byte aligned:
+ *             [0] n, [1] tail share, [2] fraction of the tail positions in
+ *             the last W, [3] share of the last W positions, [4] positions
+ *             with cond > 1, [5] their share, [6] sum_j e_j, [7] T.  Shares
+ *             are NaN when sum_j e_j = 0, [2] when n = 0.
+ *
+ * Sums are in double over the float inputs.  RIPE_EINVAL for null or
+ * misaligned pointers, n_rows < 0, row_stride < 0, W < 0 or tail_frac
+ * outside (0, 1].  Asynchronous on stream; launches kernels only.
+ */
+#define RIPE_TAIL_STATS 8
+ripe_status_t ripe_position_error_tail(const float* err, const float* cond, const int32_t* T, int32_t n_rows,
+                                       int32_t row_stride, int32_t window, double tail_frac, double* stats,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

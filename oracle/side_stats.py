@@ -27,10 +27,17 @@ attention per substituted position); ``position_error_rank1`` is the same
 quantity from the softmax identity for a single changed term, in float64,
 fast enough for full-size inputs.  The two are pinned against each other
 and against closed forms in tests/test_oracle_side_stats.py.
+
+``tail_statistics`` reads the abstract's two tail figures off one group's
+error row (reading: the tail is the floor(1% T) largest e_j, ties to the
+lower position; its share of sum_j e_j, and the fraction of its positions in
+the last W), written out with a stable sort; it is pinned by hand-worked
+rows in tests/test_oracle_tail_stats.py.
 """
 from __future__ import annotations
 
-from typing import Iterable, List
+import math
+from typing import Dict, Iterable, List, Optional
 
 import numpy as np
 
@@ -108,4 +115,43 @@ def position_error_rank1(cache: ro.LogicalCache, groups: Iterable, q: np.ndarray
             delta = num / (1.0 + c - a)[:, :, None]
             e += (delta ** 2).sum(axis=(0, 2))
         res.append(e)
+    return res
+
+
+def tail_statistics(err, T: int, W: int, cond=None, tail_frac: float = 0.01) -> Dict[str, Optional[float]]:
+    """One group's row: err (and cond) host arrays of at least T entries, T
+    its prefix length, W a RIPE window.
+
+    * tail_positions: floor(tail_frac * T), at least 1 (0 when T = 0);
+    * tail_share: the share of sum_j e_j carried by the tail_positions
+      largest e_j (among equal values the lower positions first);
+    * tail_in_window: the fraction of those positions among the last W;
+    * window_share: the share of sum_j e_j carried by the last W positions;
+    * ill_conditioned: positions with cond > 1, and ill_conditioned_share
+      their share of sum_j e_j (None without cond).
+    Shares are None when sum_j e_j is 0, tail_in_window when there is no
+    tail position."""
+    e = np.asarray(err, dtype=np.float64)[:T]
+    n_tail = 0 if T == 0 else max(1, int(math.floor(tail_frac * T)))
+    order = np.argsort(-e, kind="stable")  # largest first; equal values keep position order
+    top = order[:n_tail]
+    total = float(e.sum())
+    w0 = max(0, T - W)
+
+    def share(x):
+        return float(x) / total if total > 0 else None
+
+    res = {
+        "positions": int(T),
+        "tail_positions": n_tail,
+        "tail_share": share(e[top].sum()),
+        "tail_in_window": float(np.mean(top >= w0)) if n_tail else None,
+        "window_share": share(e[w0:].sum()),
+        "ill_conditioned": None,
+        "ill_conditioned_share": None,
+    }
+    if cond is not None:
+        ill = np.asarray(cond, dtype=np.float64)[:T] > 1.0
+        res["ill_conditioned"] = int(ill.sum())
+        res["ill_conditioned_share"] = share(e[ill].sum())
     return res

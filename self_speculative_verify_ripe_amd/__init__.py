@@ -9,4 +9,5 @@ from .binding import (DTYPES, LAYOUTS, RIPE_BF16, RIPE_BYTES_CACHE,  # noqa: F40
                       ripe_group_t, ripe_layout_bytes, ripe_verify_attn, pack_groups, new_workspace,
                       ripe_accept_desc_t, make_accept_desc, ripe_accept_workspace_bytes, ripe_accept,
                       commit_args, pack_parents, ripe_position_error, RIPE_BYTES_POSERR_WORKSPACE,
-                      ripe_verify_attn_noalloc)
+                      ripe_verify_attn_noalloc, ripe_position_error_tail, RIPE_TAIL_STATS,
+                      TAIL_FIELDS)

@@ -85,6 +85,9 @@ def _load():
                                         ctypes.POINTER(ripe_group_t), ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ripe_position_error.restype = ctypes.c_int
+    lib.ripe_position_error_tail.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P]
+    lib.ripe_position_error_tail.restype = ctypes.c_int
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.ripe_verify_attn_paged.argtypes = [ctypes.POINTER(ripe_desc_t), P, I32P, I32P,
                                            ctypes.POINTER(ripe_group_t), I32P, ctypes.c_int32, ctypes.c_int32,
@@ -278,6 +281,27 @@ def ripe_position_error(desc: ripe_desc_t, cache, seq_len: Sequence[int], groups
                                  _stream(stream))
     if st != 0:
         raise RipeError(st, "ripe_position_error")
+
+
+RIPE_TAIL_STATS = 8
+TAIL_FIELDS = ("tail_positions", "tail_share", "tail_in_window", "window_share", "ill_conditioned",
+               "ill_conditioned_share", "total", "positions")
+
+
+def ripe_position_error_tail(err, T: Sequence[int], window: int, stats, cond=None, tail_frac: float = 0.01,
+                             row_stride: Optional[int] = None, stream=None) -> None:
+    """Tail figures of error rows (asynchronous on ``stream``): err (and
+    cond) [n_rows, row_stride] float32 on the device, T one prefix length per
+    row, stats [n_rows, RIPE_TAIL_STATS] float64 on the device (fields in
+    TAIL_FIELDS order)."""
+    t = np.ascontiguousarray(np.asarray(T, dtype=np.int32).reshape(-1))
+    if row_stride is None:
+        row_stride = int(err.shape[-1])
+    st = lib.ripe_position_error_tail(_ptr(err), _ptr(cond), t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      int(t.size), int(row_stride), int(window), float(tail_frac), _ptr(stats),
+                                      _stream(stream))
+    if st != 0:
+        raise RipeError(st, "ripe_position_error_tail")
 
 
 def ripe_commit(desc: ripe_desc_t, cache, seq_len, n_accept: Sequence[int],

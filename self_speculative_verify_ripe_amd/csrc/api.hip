@@ -1112,6 +1112,36 @@ extern "C" ripe_status_t ripe_commit_paged(const ripe_desc_t* desc, void* cache,
   return commit_impl(desc, cache, block_table, seq_len, n_accept, src_row, kv_new, n_rows, stream);
 }
 
+extern "C" ripe_status_t ripe_position_error_tail(const float* err, const float* cond, const int32_t* T,
+                                                  int32_t n_rows, int32_t row_stride, int32_t window,
+                                                  double tail_frac, double* stats, void* stream) {
+  if (n_rows < 0 || row_stride < 0 || window < 0 || !(tail_frac > 0.0 && tail_frac <= 1.0)) return RIPE_EINVAL;
+  if (n_rows == 0) return RIPE_OK;
+  if (T == nullptr || err == nullptr || stats == nullptr || !aligned(err, 4) || (cond && !aligned(cond, 4)) ||
+      !aligned(stats, 8))
+    return RIPE_EINVAL;
+  for (int i = 0; i < n_rows; ++i)
+    if (T[i] < 0 || T[i] > row_stride) return RIPE_ERANGE;
+  TailParams p;
+  p.err = err;
+  p.cond = cond;
+  p.stats = stats;
+  p.stride = row_stride;
+  p.window = window;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (int g0 = 0; g0 < n_rows; g0 += kTailRows) {
+    p.g0 = g0;
+    p.n_rows = std::min(kTailRows, n_rows - g0);
+    for (int k = 0; k < p.n_rows; ++k) {
+      const int t = T[g0 + k];
+      p.T[k] = t;
+      p.n_tail[k] = t == 0 ? 0 : std::max(1, int(std::floor(tail_frac * double(t))));
+    }
+    if (hip_status(launch_position_error_tail(p, hs), "ripe_position_error_tail") != RIPE_OK) return RIPE_EHIP;
+  }
+  return RIPE_OK;
+}
+
 extern "C" int64_t ripe_accept_workspace_bytes(const ripe_accept_desc_t* desc) {
   if (desc == nullptr) return RIPE_EINVAL;
   const ripe_accept_desc_t& d = *desc;

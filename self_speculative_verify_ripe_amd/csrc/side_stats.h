@@ -37,4 +37,22 @@ struct PosErrParams {
 
 hipError_t launch_position_error(const PosErrParams& p, int dtype, int D, hipStream_t stream);
 
+// Tail summary of error rows: one work-group per row.
+constexpr int kTailRows = 512;   // rows per launch
+constexpr int kTailStats = 8;    // doubles per row
+
+struct TailParams {
+  const float* err;     // [rows][stride]
+  const float* cond;    // [rows][stride] or null
+  double* stats;        // [rows][kTailStats]
+  int32_t stride;
+  int32_t window;       // W: the last W positions of each row's prefix
+  int32_t g0;           // index of the launch's first row among the call's rows
+  int32_t n_rows;       // rows in this launch
+  int32_t T[kTailRows];       // prefix length of each row
+  int32_t n_tail[kTailRows];  // tail positions of each row
+};
+
+hipError_t launch_position_error_tail(const TailParams& p, hipStream_t stream);
+
 }  // namespace ripe

@@ -262,7 +262,109 @@ hipError_t launch_t(const PosErrParams& p, hipStream_t stream) {
                          dim3((p.t_max + kSumPos - 1) / kSumPos, p.n_grp), dim3(256), args, 0, stream);
 }
 
+// ---- tail summary ---------------------------------------------------------
+// Per row: the share of sum_j e_j carried by its n largest e_j (ties to the
+// lower position), the fraction of those positions in the last W, the share
+// of the last W positions, and the positions with cond > 1 and their share.
+// The n-th largest value is found by bisection on the float's bits (e >= 0,
+// so the bits order like the values), 32 counting passes over the row; the
+// tail is every position above it plus the lowest-numbered positions equal
+// to it.  Sums are in double, each thread over its positions j = t, t + 256,
+// ... in order, then across threads in a fixed order.
+constexpr int kTailThreads = 256;
+
+__device__ inline uint32_t tail_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? 0u : b;  // -0 orders as 0
+}
+
+template <typename V>
+__device__ inline V block_sum(V x, V* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  const V r = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kTailThreads) void position_error_tail_kernel(const TailParams p) {
+  __shared__ double rd[4];
+  __shared__ int ri[4];
+  const int gl = blockIdx.x;
+  const int T = p.T[gl], n = p.n_tail[gl];
+  const float* e = p.err + size_t(p.g0 + gl) * p.stride;
+  const float* c = p.cond ? p.cond + size_t(p.g0 + gl) * p.stride : nullptr;
+  const int w0 = max(0, T - p.window);
+  const int t = threadIdx.x;
+  double tot = 0.0, win = 0.0, ills = 0.0;
+  int illc = 0;
+  for (int j = t; j < T; j += kTailThreads) {
+    const double x = e[j];
+    tot += x;
+    if (j >= w0) win += x;
+    if (c != nullptr && c[j] > 1.0f) {
+      ++illc;
+      ills += x;
+    }
+  }
+  tot = block_sum(tot, rd);
+  win = block_sum(win, rd);
+  ills = block_sum(ills, rd);
+  illc = block_sum(illc, ri);
+  // the n-th largest key: the largest k with count(key >= k) >= n
+  uint32_t tau = 0;
+  if (n > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+      for (int j = t; j < T; j += kTailThreads) cnt += tail_key(e[j]) >= cand;
+      if (block_sum(cnt, ri) >= n) tau = cand;
+    }
+  }
+  int gt = 0, gt_win = 0, tie_low = 0;
+  double s_gt = 0.0;
+  for (int j = t; j < T && n > 0; j += kTailThreads) {
+    const uint32_t k = tail_key(e[j]);
+    if (k > tau) {
+      ++gt;
+      s_gt += e[j];
+      if (j >= w0) ++gt_win;
+    } else if (k == tau && j < w0) {
+      ++tie_low;
+    }
+  }
+  gt = block_sum(gt, ri);
+  gt_win = block_sum(gt_win, ri);
+  tie_low = block_sum(tie_low, ri);
+  s_gt = block_sum(s_gt, rd);
+  if (t == 0) {
+    const int m = n - gt;                        // positions equal to the n-th largest, lowest first
+    const int m_win = m - min(m, tie_low);       // ... of which in the window
+    const double tail = s_gt + double(m) * double(__uint_as_float(tau));
+    const double nan = __builtin_nan("");
+    double* o = p.stats + size_t(p.g0 + gl) * kTailStats;
+    o[0] = n;
+    o[1] = tot > 0.0 ? tail / tot : nan;
+    o[2] = n > 0 ? double(gt_win + m_win) / double(n) : nan;
+    o[3] = tot > 0.0 ? win / tot : nan;
+    o[4] = c != nullptr ? double(illc) : nan;
+    o[5] = c != nullptr && tot > 0.0 ? ills / tot : nan;
+    o[6] = tot;
+    o[7] = T;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_position_error_tail(const TailParams& p, hipStream_t stream) {
+  if (p.n_rows <= 0) return hipSuccess;
+  void* args[] = {const_cast<TailParams*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&position_error_tail_kernel), dim3(p.n_rows),
+                         dim3(kTailThreads), args, 0, stream);
+}
 
 hipError_t launch_position_error(const PosErrParams& p, int dtype, int D, hipStream_t stream) {
   if (p.n_grp <= 0) return hipSuccess;

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert names == ["ripe_accept", "ripe_accept_workspace_bytes", "ripe_commit", "ripe_commit_paged",
-                     "ripe_layout_bytes", "ripe_position_error", "ripe_verify_attn", "ripe_verify_attn_inflight",
+                     "ripe_layout_bytes", "ripe_position_error", "ripe_position_error_tail", "ripe_verify_attn",
+                     "ripe_verify_attn_inflight",
                      "ripe_verify_attn_noalloc", "ripe_verify_attn_paged"]
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
@@ -333,6 +334,36 @@ def test_position_error_rejects(case, status):
 
 def test_position_error_no_groups_is_noop():
     assert call_poserr(groups=()) == 0
+
+
+def call_tail(err=None, cond=None, T=(10, 20), n_rows=None, stride=64, window=8, frac=0.01, stats=None):
+    t = np.asarray(T, dtype=np.int32)
+    return binding.lib.ripe_position_error_tail(
+        FAKE if err is None else err, cond, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        len(t) if n_rows is None else n_rows, stride, window, frac, FAKE if stats is None else stats, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(n_rows=-1), -1),
+    (dict(stride=-1), -1),
+    (dict(window=-1), -1),
+    (dict(frac=0.0), -1),
+    (dict(frac=1.5), -1),
+    (dict(frac=float("nan")), -1),
+    (dict(err=0), -1),
+    (dict(err=FAKE + 2), -1),
+    (dict(cond=FAKE + 2), -1),
+    (dict(stats=0), -1),
+    (dict(stats=FAKE + 4), -1),          # doubles: 8-byte aligned
+    (dict(T=(10, 65)), -2),              # longer than the row stride
+    (dict(T=(10, -1)), -2),
+])
+def test_position_error_tail_rejects(case, status):
+    assert call_tail(**case) == status
+
+
+def test_position_error_tail_no_rows_is_noop():
+    assert call_tail(T=(), n_rows=0) == 0
 
 
 # ---------------------------------------------------------------------------

@@ -188,3 +188,80 @@ def test_full_size_c2():
         top_o = np.argsort(-ref[0], kind="stable")[:n]
         share = lambda x, idx: x[idx].sum() / x.sum()
         assert abs(share(e[0, :T], top_g) - share(ref[0], top_o)) < 1e-3
+
+
+def check_tail(stats, err, cond, T, W, frac):
+    """ripe_position_error_tail's rows against the oracle's tail_statistics
+    on the same float32 rows: counts and the in-window fraction exact, sums
+    and shares within 1e-12 relative (double sums in another order)."""
+    got = stats.cpu().numpy()
+    for i, t in enumerate(T):
+        ref = ss.tail_statistics(err[i], int(t), W, cond=None if cond is None else cond[i], tail_frac=frac)
+        row = dict(zip(rp.TAIL_FIELDS, got[i]))
+        assert row["tail_positions"] == ref["tail_positions"] and row["positions"] == t, i
+        assert np.isclose(row["total"], float(np.asarray(err[i][:t], np.float64).sum()), rtol=1e-12, atol=0), i
+        for k in ("tail_share", "window_share", "tail_in_window", "ill_conditioned", "ill_conditioned_share"):
+            want = ref[k]
+            if want is None:
+                assert np.isnan(row[k]), (i, k, row[k])
+            elif k in ("tail_in_window", "ill_conditioned"):
+                assert row[k] == want, (i, k, row[k], want)
+            else:
+                assert abs(row[k] - want) <= 1e-12 * abs(want) + 1e-300, (i, k, row[k], want)
+
+
+@pytest.mark.parametrize("with_cond", [False, True])
+def test_tail_statistics_kernel_edge_rows(with_cond):
+    """Rows with many equal values (the tail ends inside a run of ties, some
+    of them in the window), -0.0 entries, all zeros, T = 0 and 1, a row of
+    70,000 positions, padding past T that must be ignored, and more rows
+    than one launch holds."""
+    rng = np.random.default_rng(20261204)
+    stride = 70016
+    T = [0, 1, 2, 7, 100, 333, 1024, 5000, 70000, 64, 64, 257] + list(rng.integers(0, 400, size=600))
+    rows = len(T)
+    err = np.full((rows, stride), 1e30, dtype=np.float32)  # padding: larger than anything inside T
+    for i, t in enumerate(T):
+        kind = i % 4
+        if kind == 0:
+            v = rng.integers(0, 5, size=t).astype(np.float32)           # ties everywhere
+        elif kind == 1:
+            v = rng.exponential(1.0, size=t).astype(np.float32) ** 4  # heavy tail
+        elif kind == 2:
+            v = np.zeros(t, dtype=np.float32)
+            v[::7] = -0.0
+        else:
+            v = np.full(t, 3.0, dtype=np.float32)
+            v[: t // 3] = 5.0                                          # the largest values first
+        err[i, :t] = v
+    cond = (rng.random((rows, stride)) * 2.0).astype(np.float32) if with_cond else None
+    dev_err = torch.from_numpy(err).to(DEV)
+    dev_cond = torch.from_numpy(cond).to(DEV) if with_cond else None
+    for W, frac in ((64, 0.01), (0, 0.3), (100000, 1.0), (5, 0.05)):
+        print(f"[case] tail rows={rows} W={W} frac={frac} cond={with_cond}", flush=True)
+        stats = torch.full((rows, rp.RIPE_TAIL_STATS), -1.0, dtype=torch.float64, device=DEV)
+        rp.ripe_position_error_tail(dev_err, T, W, stats, cond=dev_cond, tail_frac=frac)
+        torch.cuda.synchronize()
+        check_tail(stats, err, cond, T, W, frac)
+
+
+def test_tail_statistics_kernel_on_position_error_rows():
+    """The tail figures of ripe_position_error's own rows (c2's structure,
+    4 heads, both conventions) equal the oracle's on the same rows."""
+    for convention in ("workload", "pages"):
+        case = make_case("c2", layout="full", T_range=(333, 333), Hkv=4, Hq=4, convention=convention)
+        groups = case.groups_at(4)
+        planes = {4, case.R}
+        oc = oracle_cache(case, "full", planes=planes)
+        desc = make_desc(case, "full", max_groups=len(groups))
+        dev = Device(case)
+        err = torch.zeros((len(groups), case.t_max), dtype=torch.float32, device=DEV)
+        cond = torch.zeros_like(err)
+        ws = torch.zeros(rp.ripe_layout_bytes(desc, rp.RIPE_BYTES_POSERR_WORKSPACE), dtype=torch.uint8, device=DEV)
+        rp.ripe_position_error(desc, upload(olay.encode(oc)), case.seq_len, groups, case.n_rows, case.scale,
+                               dev.q, dev.kv_new, err, cond, None, None, ws)
+        T = [int(case.seq_len[g.seq]) for g in groups]
+        stats = torch.zeros((len(groups), rp.RIPE_TAIL_STATS), dtype=torch.float64, device=DEV)
+        rp.ripe_position_error_tail(err, T, case.W, stats, cond=cond)
+        torch.cuda.synchronize()
+        check_tail(stats, err.cpu().numpy(), cond.cpu().numpy(), T, case.W, 0.01)

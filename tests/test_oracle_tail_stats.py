@@ -1,8 +1,11 @@
-"""Host-side summary of the substitution-error rows (package side_stats):
-hand-worked arrays."""
+"""Pins of the oracle's tail figures of an error row (oracle/side_stats.py
+tail_statistics): hand-worked arrays, and a brute-force check of the tail
+selection (every subset of a small row)."""
+import itertools
+
 import numpy as np
 
-from self_speculative_verify_ripe_amd.side_stats import tail_statistics
+from oracle.side_stats import tail_statistics
 
 
 def test_hand_worked_row():
@@ -33,3 +36,24 @@ def test_ties_and_degenerate_rows():
     assert z["tail_share"] is None and z["window_share"] is None
     empty = tail_statistics(np.zeros(0), 0, 8)
     assert empty["tail_positions"] == 0 and empty["tail_in_window"] is None
+
+
+def test_tail_is_the_best_subset_brute_force():
+    """The tail of n positions carries the largest sum any n positions can,
+    and among subsets with that sum it is the lexicographically lowest one
+    (ties to the lower position): checked against every subset."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        T = int(rng.integers(1, 9))
+        e = rng.integers(0, 4, size=T).astype(np.float64)  # many ties
+        frac = float(rng.choice([0.01, 0.3, 0.5, 1.0]))
+        W = int(rng.integers(0, T + 1))
+        n = max(1, int(np.floor(frac * T)))
+        best = max(itertools.combinations(range(T), n), key=lambda c: (e[list(c)].sum(), [-j for j in c]))
+        s = tail_statistics(e, T, W, tail_frac=frac)
+        assert s["tail_positions"] == n
+        total = e.sum()
+        if total > 0:
+            assert np.isclose(s["tail_share"], e[list(best)].sum() / total)
+        w0 = max(0, T - W)
+        assert s["tail_in_window"] == np.mean([j >= w0 for j in best])
