@@ -56,7 +56,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // The largest workspace one verify launch uses: the header (with the merge
 // units' arrival words, zero before and after every call; a static array
 // starts zeroed) and kMaxItems partials of 32 query columns x (D + 2) floats
-// at the largest head dimension, D = 128.
+// at the largest head dimension, D = 128 (the size of an fp32 cache's
+// partial; a 16-bit cache's, in fp16, is smaller).
 // Calls are cut into launches of at most kMaxItems items, so every verify
 // call fits.  Each GPU the library runs on holds its own copy until the
 // process ends.

@@ -189,7 +189,7 @@ struct VerifyParams {
   void* out;
   float* lse;
   int8_t* plane_sel;
-  float* ws;             // split partials, [item][16 NB columns][D + 2]
+  float* ws;             // split partials, one per item (the verify kernel's PartLayout)
   unsigned long long* arrive;  // one arrival word per merge unit (fused merge)
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
