@@ -35,7 +35,7 @@ namespace {
 using namespace ripe;
 
 constexpr int64_t kMaxBytes = int64_t(1) << 50;   // sanity bound on any buffer size
-constexpr int64_t kMaxCommitItems = int64_t(1) << 30;  // commit work items per launch
+constexpr int64_t kMaxCommitTasks = int64_t(1) << 28;  // commit wavefront tasks per launch
 constexpr int kMaxCQ = 32;                        // query columns per verify work-group
 constexpr int kMaxSplit = 8192;                   // longest piece (positions)
 
@@ -961,28 +961,20 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
   const int We = ring_width(d);
   const size_t E = elem_bytes(d.dtype);
   const int64_t reg = region_elems(d);
-  const int64_t per_row_plane = int64_t(d.n_kv_heads) * (D / 8);  // items per (row, plane)
-
   struct Job {
     int b, j0, src0, n, plane_lo, n_planes, page;
   };
   std::vector<Job> jobs;
-  auto add_cut = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes, int page) {
-    // cut rows so that no job exceeds the per-launch item budget
-    const int64_t per_row = per_row_plane * n_planes;
-    const int max_rows = int(std::max<int64_t>(1, kMaxCommitItems / per_row));
-    for (int r0 = 0; r0 < n; r0 += max_rows) {
-      const int cnt = std::min(max_rows, n - r0);
-      jobs.push_back(Job{b, j0 + r0, src0 + r0, cnt, plane_lo, n_planes, page});
-    }
+  auto push = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes, int page) {
+    jobs.push_back(Job{b, j0, src0, n, plane_lo, n_planes, page});
   };
   // main-region rows of a paged cache: one job per page touched
   auto add = [&](int b, int j0, int src0, int n, int plane_lo, int n_planes) {
     const bool main_region = !(d.layout == RIPE_LAYOUT_RIPE && plane_lo < d.R);
-    if (table == nullptr || !main_region) return add_cut(b, j0, src0, n, plane_lo, n_planes, 0);
+    if (table == nullptr || !main_region) return push(b, j0, src0, n, plane_lo, n_planes, 0);
     for (int a = j0; a < j0 + n;) {
       const int e = std::min(j0 + n, (a / P + 1) * P);
-      add_cut(b, a, src0 + (a - j0), e - a, plane_lo, n_planes, table[b * nblk + a / P]);
+      push(b, a, src0 + (a - j0), e - a, plane_lo, n_planes, table[b * nblk + a / P]);
       a = e;
     }
   };
@@ -1054,15 +1046,17 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
     p.t_max = d.t_max;
     p.H = d.n_kv_heads;
     p.n_rows = n_rows;
-    int64_t items = 0, vtasks = 0;
+    int64_t tasks = 0, max_nt = 0;
     int nj = 0;
     taken.clear();
     for (; i < jobs.size() && nj < kMaxJobs; ++i) {
       const Job& jb = jobs[i];
       const Blocks k = blocks_of(jb);
-      const int64_t cnt = int64_t(jb.n) * jb.n_planes * per_row_plane;
-      const int64_t vt = int64_t(jb.n_planes) * d.n_kv_heads * (k.nblk0 + k.nblk1);
-      if (nj > 0 && (items + cnt > kMaxCommitItems || vtasks + vt > kMaxCommitItems)) break;
+      const int64_t nt = int64_t(jb.n_planes) * d.n_kv_heads * (k.nblk0 + k.nblk1);
+      // the grid has one row per job, as long as the largest: jobs of very
+      // different sizes go to separate launches
+      const int64_t mx = std::max(max_nt, nt);
+      if (nj > 0 && (tasks + nt > kMaxCommitTasks || mx * (nj + 1) > 2 * (tasks + nt) + (int64_t(1) << 16))) break;
       bool clash = false;
       for (int r = 0; r < 2 && !clash; ++r)
         for (int q = 0; q < (r ? k.nblk1 : k.nblk0) && !clash; ++q)
@@ -1071,8 +1065,7 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
       for (int r = 0; r < 2; ++r)
         for (int q = 0; q < (r ? k.nblk1 : k.nblk0); ++q) taken.insert(key(jb, k, (r ? k.blk1 : k.blk0) + q));
       CommitJob& cj = p.job[nj++];
-      cj.item0 = int32_t(items);
-      cj.vtask0 = int32_t(vtasks);
+      cj.n_tasks = int32_t(nt);
       cj.s0 = k.s0;
       cj.src0 = jb.src0;
       cj.n_rows = jb.n;
@@ -1085,12 +1078,11 @@ static ripe_status_t commit_impl(const ripe_desc_t* desc, void* cache, const int
       cj.nblk0 = k.nblk0;
       cj.blk1 = k.blk1;
       cj.nblk1 = k.nblk1;
-      items += cnt;
-      vtasks += vt;
+      tasks += nt;
+      max_nt = mx;
     }
     p.n_jobs = nj;
-    p.n_items = int32_t(items);
-    p.n_vtasks = int32_t(vtasks);
+    for (int j = 0; j < nj; ++j) p.max_tasks = std::max(p.max_tasks, p.job[j].n_tasks);
     launches.push_back(p);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);

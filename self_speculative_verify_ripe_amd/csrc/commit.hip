@@ -9,17 +9,19 @@
 // position W later reuses its slot.  FULL writes planes 1..R, DEEPEST plane
 // R.  LoopSpec summary (rit.work): rejected rows are simply not committed.
 //
-// K rows are contiguous per (position, head): one thread copies 8
-// consecutive head-dim elements (16 or 32 bytes).  V is stored transposed in
-// blocks of 8 slots ([D][8]: each head dimension's 8 values one 16- or
-// 32-byte run, a block 2 or 4 KB at D = 128), so a commit of a few
-// positions touches one or two blocks per (plane, head).  One wavefront per
-// (plane, head, block) rewrites the block's runs whole -- it reads a run
-// unless every slot of it is new, puts the new values in and writes the run
-// back; the other slots keep their bytes -- so the stores cover whole cache
-// lines.  (The cache lines a commit dirties, not the bytes it writes, set
-// what the write-back costs the verify calls that stream the cache next;
-// 32-slot blocks would make a commit of 4 positions dirty 4 times the lines.)
+// One wavefront per (plane, head, block of 8 slots) writes everything a
+// commit puts in that block.  K rows are contiguous per (position, head):
+// the wavefront copies the rows of the block's new slots, 16 bytes per lane.
+// V is stored transposed in blocks of 8 slots ([D][8]: each head
+// dimension's 8 values one 16- or 32-byte run, a block 2 or 4 KB at
+// D = 128), so a commit of a few positions touches one or two blocks per
+// (plane, head).  The wavefront rewrites the block's runs whole -- a lane
+// reads a run unless every slot of it is new, puts the new values in and
+// writes the run back; the other slots keep their bytes -- so the stores
+// cover whole cache lines.  (The cache lines a commit dirties, not the
+// bytes it writes, set what the write-back costs the verify calls that
+// stream the cache next; 32-slot blocks would make a commit of 4 positions
+// dirty 4 times the lines.)
 // The stores are non-temporal: the rows are read again only by later
 // calls, and lines left dirty in the caches would be written back while
 // those calls stream (c4 loop: the verify call after a commit 60.9 -> 58.8
@@ -45,58 +47,23 @@ __device__ inline size_t region_off(const CommitParams& p, const CommitJob& jb, 
   return (size_t(jb.b) * p.H + h) * size_t(p.t_max) * D;
 }
 
-__device__ inline int find_job(const CommitParams& p, int x, bool vtask) {
-  int lo = 0, hi = p.n_jobs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((vtask ? p.job[mid].vtask0 : p.job[mid].item0) <= x)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
-  const int kblocks = (p.n_items + 255) / 256;
+  // one wavefront per (job, plane, head, block of kVBlock slots): grid row
+  // y is job y (read with one argument load; a search over the job table
+  // cost the c4 commit 4 us), and the rows of shorter jobs end early
+  const CommitJob& jb = p.job[blockIdx.y];
+  int local = int(blockIdx.x) * 4 + int(threadIdx.x >> 6);
+  if (local >= jb.n_tasks) return;
+  const int lane = threadIdx.x & 63;
   const T* kv = static_cast<const T*>(p.kv_new);
   const size_t Hd = size_t(p.H) * D;
-  if (int(blockIdx.x) < kblocks) {
-    // ---- K: one thread per (row, plane, head, 8-element chunk)
-    const int item = blockIdx.x * 256 + threadIdx.x;
-    if (item >= p.n_items) return;
-    const CommitJob& jb = p.job[find_job(p, item, false)];
-    constexpr int CH = D / 8;
-    int local = item - jb.item0;
-    const int ch = local % CH;
-    local /= CH;
-    const int h = local % p.H;
-    local /= p.H;
-    const int pl = jb.plane_lo + local % jb.n_planes;  // 1-based plane
-    const int ri = local / jb.n_planes;
-    const int slot = jb.ring > 0 ? (jb.s0 + ri) % jb.ring : jb.s0 + ri;
-    const T* ks = kv + (size_t(pl - 1) * p.n_rows + jb.src0 + ri) * Hd + size_t(h) * D + ch * 8;
-    T* kd = static_cast<T*>(p.cache_k) + region_off(p, jb, pl, h, D) + size_t(slot) * D + ch * 8;
-    constexpr int NV = 8 * sizeof(T) / 16;  // 16-byte pieces per 8 elements
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-      __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(ks)[v], reinterpret_cast<u32x4*>(kd) + v);
-    return;
-  }
-  // ---- V: one wavefront per (plane, head, block); lane l rewrites the runs
-  // of head dimensions l, l + 64, ...
-  const int task = (int(blockIdx.x) - kblocks) * 4 + int(threadIdx.x >> 6);
-  if (task >= p.n_vtasks) return;
-  const int lane = threadIdx.x & 63;
-  const CommitJob& jb = p.job[find_job(p, task, true)];
-  int local = task - jb.vtask0;
   const int nb = jb.nblk0 + jb.nblk1;
   const int bi = local % nb;
   local /= nb;
   const int blk = bi < jb.nblk0 ? jb.blk0 + bi : jb.blk1 + (bi - jb.nblk0);
   const int h = local % p.H;
-  const int pl = jb.plane_lo + local / p.H;
+  const int pl = jb.plane_lo + local / p.H;                          // 1-based plane
   const int bs = blk * kVBlock;                                     // first slot of the block
   const int w = jb.ring > 0 ? min(kVBlock, jb.ring - bs) : kVBlock;  // its slots
   // row of slot s (or -1): main regions s0 + i, rings (s0 + i) mod We
@@ -105,12 +72,31 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
     if (jb.ring > 0 && i < 0) i += jb.ring;
     return (i >= 0 && i < jb.n_rows) ? i : -1;
   };
-  T* vb = static_cast<T*>(p.cache_v) + region_off(p, jb, pl, h, D) + size_t(bs) * D;
+  int n_new = 0;
+#pragma unroll
+  for (int s = 0; s < kVBlock; ++s) n_new += (s < w && row_of(bs + s) >= 0);
+  const size_t reg = region_off(p, jb, pl, h, D);
+
+  // ---- K: the rows of the block's new slots, 16 bytes per lane and step
+  constexpr int CPR = D * int(sizeof(T)) / 16;  // 16-byte chunks per row
+  const T* ksrc = kv + (size_t(pl - 1) * p.n_rows + jb.src0) * Hd + size_t(h) * D;
+  u32x4* const kdst = reinterpret_cast<u32x4*>(static_cast<T*>(p.cache_k) + reg + size_t(bs) * D);
+  for (int c = lane; c < n_new * CPR; c += 64) {
+    const int r = c / CPR, ch = c % CPR;
+    int slot = 0, seen = 0;  // the block's r-th new slot
+    for (int s = 0; s < w; ++s)
+      if (row_of(bs + s) >= 0 && seen++ == r) {
+        slot = s;
+        break;
+      }
+    const u32x4 x = reinterpret_cast<const u32x4*>(ksrc + size_t(row_of(bs + slot)) * Hd)[ch];
+    __builtin_nontemporal_store(x, kdst + size_t(slot) * CPR + ch);
+  }
+
+  // ---- V: lane l rewrites the runs of head dimensions l, l + 64, ...
+  T* vb = static_cast<T*>(p.cache_v) + reg + size_t(bs) * D;
   const T* vsrc = kv + (size_t(p.R + pl - 1) * p.n_rows + jb.src0) * Hd + size_t(h) * D;
   if (w == kVBlock) {
-    int n_new = 0;
-#pragma unroll
-    for (int s = 0; s < kVBlock; ++s) n_new += row_of(bs + s) >= 0;
     constexpr int NQ = kVBlock * sizeof(T) / 16;  // 16-byte pieces per run
 #pragma unroll
     for (int d = lane; d < D; d += 64) {
@@ -141,10 +127,10 @@ __global__ __launch_bounds__(256) void commit_rows(const CommitParams p) {
 
 template <typename T, int D>
 static hipError_t launch_commit_t(const CommitParams& p, hipStream_t stream) {
-  const int blocks = (p.n_items + 255) / 256 + (p.n_vtasks + 3) / 4;
-  if (blocks == 0) return hipSuccess;
+  const int blocks = (p.max_tasks + 3) / 4;
+  if (blocks == 0 || p.n_jobs == 0) return hipSuccess;
   void* args[] = {const_cast<CommitParams*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&commit_rows<T, D>), dim3(blocks), dim3(256),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&commit_rows<T, D>), dim3(blocks, p.n_jobs), dim3(256),
                          args, 0, stream);
 }
 

@@ -209,15 +209,14 @@ struct VerifyParams {
 
 constexpr int kVBlock = 8;  // positions per transposed V block [D][8]
 
-// Rows of one sequence written to one region (48 bytes).  Row i goes to slot
+// Rows of one sequence written to one region (44 bytes).  Row i goes to slot
 // s0 + i of the region (a position, a page slot), or for a RIPE ring to slot
-// (s0 + i) mod We.  Its V blocks (kVBlock slots each; a ring's last may be
-// narrower) are rewritten whole, one wavefront per (plane, head, block):
-// the blocks touched form one or two ranges [blk0, blk0 + nblk0) and
-// [blk1, blk1 + nblk1) that share no block.
+// (s0 + i) mod We.  One wavefront per (plane, head, block of kVBlock slots;
+// a ring's last may be narrower) writes the K rows of the block's new slots
+// and rewrites its V runs whole.  The blocks touched form one or two ranges
+// [blk0, blk0 + nblk0) and [blk1, blk1 + nblk1) that share no block.
 struct CommitJob {
-  int32_t item0;       // first K work item
-  int32_t vtask0;      // first V block task
+  int32_t n_tasks;     // its wavefront tasks: planes x heads x blocks
   int32_t s0;          // slot of the job's first row
   int32_t src0;        // kv_new row of the job's first row
   int32_t n_rows;
@@ -234,8 +233,8 @@ struct CommitParams {
   void* cache_v;
   const void* kv_new;
   uint64_t ring_off;
-  int32_t layout, R, We, t_max, H, n_rows, n_jobs, n_items;
-  int32_t n_vtasks;         // V block tasks (after the K items)
+  int32_t layout, R, We, t_max, H, n_rows, n_jobs;
+  int32_t max_tasks;        // the largest job's tasks
   int32_t page_len;         // paged cache: positions per page (0: unpaged)
   CommitJob job[kMaxJobs];  // a RIPE job with plane_lo < R writes the ring
 };
