@@ -104,8 +104,10 @@ int ring_width(const ripe_desc_t& d) {
 // trade-off between per-piece start-up and balance, unless full sequences
 // would then give more than about 1024 pieces per launch (longer pieces) or
 // fewer than about 448 (shorter pieces, down to 256 positions): a launch
-// runs best when its long pieces nearly fill the 512 resident work-group
-// slots of the device in one round, leaving some for the short items.
+// runs best when its pieces nearly fill the 512 resident work-group slots of
+// the device in one round, and a second round costs more than it balances
+// (measured per workload: shorter and longer pieces were slower for c2, c3,
+// c4 and c5 but for small margins at c3 960 and c5 FULL 544).
 int split_len(const ripe_desc_t& d) {
   if (d.split_len > 0) return d.split_len;
   const int64_t work = int64_t(d.batch) * d.n_kv_heads * d.t_max;  // positions of full sequences
