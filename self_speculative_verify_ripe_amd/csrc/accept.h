@@ -17,7 +17,9 @@ struct RowStat {
   int32_t arg;  // arg max, lowest index on ties
 };
 
-// Per-sequence progress between the launches (64 bytes).
+// Per-sequence progress between the launches (128 bytes).  It carries the
+// statistics of the rows a, c, m it names, so that the launches that follow
+// need not look them up before their first logit load.
 struct SeqState {
   int32_t stage;      // kStageDone / kStageFallback / kStageDraw
   int32_t kind;       // what the final draw draws from (see accept.hip)
@@ -26,8 +28,11 @@ struct SeqState {
   int32_t pad;
   double Wr, Wm;      // the fallback's residual masses
   double u;           // uniform of the final draw
-  double pad2;
+  double S[3];        // sums of rows ra, rc, rm (RowStat::S)
+  float M[3];         // their max logits
+  int32_t pad2[9];
 };
+static_assert(sizeof(SeqState) == 128, "SeqState layout");
 
 struct AcceptParams {
   const float* target;     // [B][2][k+1][V]
@@ -45,6 +50,8 @@ struct AcceptParams {
   double* sums;            // [B][split * kPartsPerSlice][2]: residual masses per part
   double* tiles;           // [B][n_tiles]: tile sums of the final draw's weights
   int32_t* last;           // [B][split * kPartsPerSlice]: last index with weight > 0 per part
+  double* ptot;            // [B][split * kPartsPerSlice]: each part's total weight (its tile sums
+                           // added in tile order)
   int32_t B, k, V;
   int32_t greedy;          // temperature == 0
   double inv_tau;          // 1 / temperature
@@ -53,7 +60,7 @@ struct AcceptParams {
 
 struct AcceptLayout {
   int32_t split, slice, n_tiles;
-  int64_t off_part, off_stats, off_state, off_sums, off_tiles, off_last, bytes;
+  int64_t off_part, off_stats, off_state, off_sums, off_tiles, off_last, off_ptot, bytes;
 };
 
 inline int64_t accept_align(int64_t x) { return (x + 255) / 256 * 256; }
@@ -76,6 +83,7 @@ inline AcceptLayout accept_layout(int64_t B, int64_t k, int64_t V) {
   L.off_sums = off;  off += accept_align(B * split * kPartsPerSlice * 2 * int64_t(sizeof(double)));
   L.off_tiles = off; off += accept_align(B * L.n_tiles * int64_t(sizeof(double)));
   L.off_last = off;  off += accept_align(B * split * kPartsPerSlice * int64_t(sizeof(int32_t)));
+  L.off_ptot = off;  off += accept_align(B * split * kPartsPerSlice * int64_t(sizeof(double)));
   L.bytes = off;
   return L;
 }

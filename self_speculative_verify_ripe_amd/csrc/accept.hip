@@ -14,8 +14,8 @@
 // (sequence, slice of the vocabulary) work-groups and the decisions run on
 // one work-group per sequence between them.
 //   accept_stats_kernel     per (row, slice): arg max (lowest index on ties),
-//                           max, and sum exp((z - max) / tau); rows no decision
-//                           can read are skipped
+//                           max, and sum exp((z - max) / tau) (a table-driven
+//                           exp, below); rows no decision can read are skipped
 //   accept_decide_kernel    per sequence: combines the slices into each row's
 //                           statistics; greedy decisions (final), or the
 //                           primary chain's speculative tests
@@ -24,8 +24,8 @@
 //   accept_fallback_kernel  per sequence: the fallback's tests
 //   accept_drawsum_kernel   per (sequence, quarter slice): sums of the final draw's
 //                           weights over tiles of 64 indices
-//   accept_pick_kernel      per sequence: the tile where the running sum
-//                           crosses u * total, then the index inside it
+//   accept_pick_kernel      per sequence: the part, then the tile, then the index
+//                           where the running sum crosses u * total
 // Probabilities, sums and decisions are in double; the logits are float.
 // Sums run in a fixed order for a given vocabulary size, so repeated calls
 // give the same result.
@@ -114,8 +114,6 @@ __device__ inline double prob_of(const Dist& d, double inv_tau, float z) {
   return exp((double(z) - d.M) * inv_tau) / d.S;
 }
 
-__device__ inline double prob(const Dist& d, double inv_tau, int t) { return prob_of(d, inv_tau, d.z[t]); }
-
 // The weights a final draw uses, as a function of the index.  With the
 // fallback's residual target r(t) = max(0, a - c) / Wr (a itself when Wr = 0)
 // and its draft distribution q'(t) = max(0, m - c) / Wm (0 when Wm = 0):
@@ -133,15 +131,6 @@ struct DrawSpec {
 
 enum Stage { kStageDone = 0, kStageFallback = 1, kStageDraw = 2 };
 
-__device__ inline double fallback_r(const DrawSpec& s, double inv_tau, int t) {
-  const double pa = prob(s.a, inv_tau, t);
-  return s.Wr > 0.0 ? fmax(pa - prob(s.c, inv_tau, t), 0.0) / s.Wr : pa;
-}
-
-__device__ inline double fallback_q(const DrawSpec& s, double inv_tau, int t) {
-  return s.Wm > 0.0 ? fmax(prob(s.m, inv_tau, t) - prob(s.c, inv_tau, t), 0.0) / s.Wm : 0.0;
-}
-
 // The weight of one index from its logits in rows a, c and m (rows a kind
 // does not use alias a, so every load is valid).
 __device__ inline double weight_of(const DrawSpec& s, double inv_tau, float za, float zc, float zm) {
@@ -152,7 +141,7 @@ __device__ inline double weight_of(const DrawSpec& s, double inv_tau, float za, 
       const double pa = prob_of(s.a, inv_tau, za);
       return s.Wr > 0.0 ? fmax(pa - prob_of(s.c, inv_tau, zc), 0.0) / s.Wr : pa;
     }
-    default: {  // kDrawRestart: fallback_r - fallback_q, with c's probability computed once
+    default: {  // kDrawRestart: max(0, r - q'), with c's probability computed once
       const double pa = prob_of(s.a, inv_tau, za), pc = prob_of(s.c, inv_tau, zc);
       const double r = s.Wr > 0.0 ? fmax(pa - pc, 0.0) / s.Wr : pa;
       const double q = s.Wm > 0.0 ? fmax(prob_of(s.m, inv_tau, zm) - pc, 0.0) / s.Wm : 0.0;
@@ -270,17 +259,28 @@ __device__ int wg_draw(const DrawSpec& s, double inv_tau, int V, double u) {
 __device__ inline bool in_vocab(int t, int V) { return t >= 0 && t < V; }
 
 
-__device__ inline Dist dist_of(const AcceptParams& p, int b, int r) {
-  const RowStat st = p.stats[size_t(b) * (4 * p.k + 2) + r];
-  return Dist{row_ptr(p, b, r), double(st.M), st.S};
+
+// The rows a, c, m of a state, with the statistics it carries.
+__device__ inline Dist dist_in(const AcceptParams& p, int b, const SeqState& s, int w) {
+  return Dist{row_ptr(p, b, w == 0 ? s.ra : (w == 1 ? s.rc : s.rm)), double(s.M[w]), s.S[w]};
+}
+
+// Copy the statistics of rows ra, rc, rm into the state (rows a state's kind
+// does not use are copied too and never read).
+__device__ inline void carry_rows(SeqState& s, const RowStat* st) {
+  const int r[3] = {s.ra, s.rc, s.rm};
+  for (int w = 0; w < 3; ++w) {
+    s.S[w] = st[r[w]].S;
+    s.M[w] = st[r[w]].M;
+  }
 }
 
 __device__ inline DrawSpec spec_of(const AcceptParams& p, int b, const SeqState& s) {
   DrawSpec d;
   d.kind = s.kind;
-  d.a = dist_of(p, b, s.ra);
-  d.c = s.kind == kDrawRow ? d.a : dist_of(p, b, s.rc);
-  d.m = (s.kind == kDrawRestart || s.kind == kDrawFallbackR) ? dist_of(p, b, s.rm) : d.a;
+  d.a = dist_in(p, b, s, 0);
+  d.c = s.kind == kDrawRow ? d.a : dist_in(p, b, s, 1);
+  d.m = (s.kind == kDrawRestart || s.kind == kDrawFallbackR) ? dist_in(p, b, s, 2) : d.a;
   d.Wr = s.Wr;
   d.Wm = s.Wm;
   return d;
@@ -294,6 +294,42 @@ __device__ inline bool row_unused(const AcceptParams& p, int r, bool fb) {
   const bool is_draft = r >= 2 * (k + 1);
   const int chain = is_draft ? (r - 2 * (k + 1)) / k : r / (k + 1);
   return r == target_row(k, 1, 0) || (chain == 1 && !fb) || (is_draft && p.greedy);
+}
+
+// ---------------------------------------------------------------------------
+// e^x for the row statistics
+// ---------------------------------------------------------------------------
+// One exp per logit is most of the row statistics' time: removing it cuts
+// the kernel by 40%, removing its loads by 7%, so the double-precision pipes
+// bound it, not memory.  A table shortens each exp.  With
+// N = rint(256 x / ln 2) = 256 n + j (0 <= j < 256), r = x - N ln 2 / 256
+// is taken in two steps (Cody and Waite's reduction: ln 2 / 256 split into a
+// head of 32 significant bits, so that N * head is exact, and the double
+// nearest the rest), and e^x = 2^n 2^(j/256) e^r: 2^(j/256) from a table
+// that each work-group fills in LDS with the library's exp2, e^r from its
+// Taylor series to degree 4 (|r| <= ln 2 / 512, so the truncation is below
+// 4e-17 relative), the power of two applied with ldexp, which also rounds
+// results below the normal range correctly.  About 12 double operations and
+// one LDS read per logit, against about 25 for the library's exp, within 2
+// units in the last place of it; x = 0 gives exactly 1.  x < -746 (e^x below
+// half the smallest subnormal) and x = -inf give 0; NaN stays NaN.
+constexpr int kExpTable = 256;
+constexpr double kLn2Head = 0x1.62e42feep-1;         // ln 2 to 32 significant bits
+constexpr double kLn2Rest = 1.9082149292705877e-10;  // ln 2 - kLn2Head, to double
+constexpr double kTableScale = 369.3299304675746;     // 256 / ln 2, to double
+
+__device__ inline void fill_exp_table(double* t) {  // every thread of the work-group, then a barrier
+  for (int j = threadIdx.x; j < kExpTable; j += kAcceptThreads) t[j] = exp2(double(j) / kExpTable);
+  __syncthreads();
+}
+
+__device__ inline double exp_tab(const double* t, double x) {
+  if (!(x >= -746.0)) return x != x ? x : 0.0;
+  const double nd = rint(x * kTableScale);
+  const int n = int(nd);
+  const double r = fma(-nd, kLn2Rest / kExpTable, fma(-nd, kLn2Head / kExpTable, x));
+  const double e = fma(fma(fma(fma(r, 1.0 / 24.0, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
+  return ldexp(t[n & (kExpTable - 1)] * e, n >> 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,6 +348,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_stats_kernel(const Acce
   int mi = 0x7fffffff;
   double s = 0.0;
   const bool sum = !p.greedy;
+  __shared__ double etab[kExpTable];
+  if (sum) fill_exp_table(etab);
   if (t1 - t0 <= kHeld * kAcceptThreads) {
     // the whole slice in registers: one read of the logits serves both passes
     float zv[kHeld];
@@ -325,7 +363,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_stats_kernel(const Acce
       const double M = mv;
 #pragma unroll
       for (int j = 0; j < kHeld; ++j)
-        if (t0 + int(threadIdx.x) + j * kAcceptThreads < t1) s += exp((double(zv[j]) - M) * p.inv_tau);
+        if (t0 + int(threadIdx.x) + j * kAcceptThreads < t1) s += exp_tab(etab, (double(zv[j]) - M) * p.inv_tau);
       s = wg_sum(s);
     }
   } else {
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_stats_kernel(const Acce
         for (int j = 0; j < kLoadBatch; ++j) zv[j] = load_or(z, t + j * kAcceptThreads, t1, 0.f);
 #pragma unroll
         for (int j = 0; j < kLoadBatch; ++j)
-          if (t + j * kAcceptThreads < t1) s += exp((double(zv[j]) - M) * p.inv_tau);
+          if (t + j * kAcceptThreads < t1) s += exp_tab(etab, (double(zv[j]) - M) * p.inv_tau);
       }
       s = wg_sum(s);
     }
@@ -358,68 +396,126 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_stats_kernel(const Acce
 // ---------------------------------------------------------------------------
 // 2. row statistics, greedy decisions, the primary chain's tests
 // ---------------------------------------------------------------------------
+constexpr int kMaxRows = 4 * 64 + 2;  // rows of one sequence at the largest k
+constexpr int kWaves = kAcceptThreads / 64;
+constexpr int kRowBatch = 4;          // rows whose slice statistics one wavefront loads together
+
+// The sequence's row statistics into out[rows] (LDS), for every row a
+// decision can read: the max and lowest arg max over the slices, and
+// S = sum_i S_i exp((M_i - M) / tau) by a fixed xor tree over the slices.
+// Lane i holds slice i (split <= 64); wavefront w takes rows w, w + kWaves, ...
+__device__ void combine_rows(const AcceptParams& p, int b, bool fb, RowStat* out) {
+  const int rows = 4 * p.k + 2, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const RowStat* base = p.part + size_t(b) * rows * p.split;
+  for (int r0 = wave; r0 < rows; r0 += kRowBatch * kWaves) {
+    RowStat st[kRowBatch];
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      const int r = r0 + j * kWaves;
+      const bool use = r < rows && lane < p.split && !row_unused(p, r, fb);
+      st[j] = use ? base[size_t(r) * p.split + lane] : RowStat{0.0, -INFINITY, 0x7fffffff};
+    }
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      const int r = r0 + j * kWaves;
+      if (r >= rows || row_unused(p, r, fb)) continue;  // the same for the whole wavefront
+      float M = st[j].M;
+      int arg = st[j].arg;
+      for (int off = 32; off > 0; off >>= 1) {  // better() is a total order: every lane ends equal
+        const float M2 = __shfl_xor(M, off);
+        const int a2 = __shfl_xor(arg, off);
+        better(M, arg, M2, a2);
+      }
+      double S = 0.0;
+      if (!p.greedy) S = wave_sum(st[j].M > -INFINITY ? st[j].S * exp((double(st[j].M) - double(M)) * p.inv_tau) : 0.0);
+      if (lane == 0) out[r] = RowStat{S, M, arg};
+    }
+  }
+}
+
+__device__ inline double uniform_of(uint32_t w) { return double(w) * (1.0 / 4294967296.0); }
+
 __global__ __launch_bounds__(kAcceptThreads) void accept_decide_kernel(const AcceptParams p) {
+  __shared__ RowStat s_st[kMaxRows];
+  __shared__ int s_acc[128];
   const int b = blockIdx.x;
   const int k = p.k, V = p.V;
   const int rows = 4 * k + 2;
   const bool fb = p.has_fb[b] != 0;
-  // combine the slices: max and arg max, S = sum_i s_i exp((m_i - M) / tau)
-  for (int r = threadIdx.x; r < rows; r += kAcceptThreads) {
-    if (row_unused(p, r, fb)) continue;
-    const RowStat* pr = p.part + (size_t(b) * rows + r) * p.split;
-    float M = -INFINITY;
-    int arg = 0x7fffffff;
-    for (int i = 0; i < p.split; ++i) better(M, arg, pr[i].M, pr[i].arg);
-    double S = 0.0;
-    if (!p.greedy)
-      for (int i = 0; i < p.split; ++i)
-        if (pr[i].M > -INFINITY) S += pr[i].S * exp((double(pr[i].M) - double(M)) * p.inv_tau);
-    p.stats[size_t(b) * rows + r] = RowStat{S, M, arg};
-  }
-  __syncthreads();  // (a work-group barrier also orders the global writes above)
-  const RowStat* st = p.stats + size_t(b) * rows;
   const int32_t* tok = p.tokens + size_t(b) * 2 * k;
-  // the primary chain's p_i(x_i) and q_i(x_i), one thread per position
-  __shared__ double s_pt[64], s_qt[64];
-  if (!p.greedy && int(threadIdx.x) < k) {
-    const int i = threadIdx.x, t = tok[i];
-    const bool ok = in_vocab(t, V);
-    s_pt[i] = ok ? prob(dist_of(p, b, target_row(k, 0, i)), p.inv_tau, t) : 0.0;
-    s_qt[i] = ok ? prob(dist_of(p, b, draft_row(k, 0, i)), p.inv_tau, t) : 0.0;
+  const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
+  // Every test runs on a thread of its own, its inputs loaded with the
+  // slices' statistics: thread i < k primary token i (its logits in the
+  // target and draft rows, its uniform); greedy calls also thread k + i,
+  // fallback token i.  Thread 0 then only reads the outcomes.
+  const int i = threadIdx.x;
+  int t = -1;
+  float zt = 0.f, zd = 0.f;
+  double u = 0.0;
+  if (i < k) {
+    t = tok[i];
+    if (!p.greedy) {
+      u = uniform_of(rw[i]);
+      if (in_vocab(t, V)) {
+        zt = row_ptr(p, b, target_row(k, 0, i))[t];
+        zd = row_ptr(p, b, draft_row(k, 0, i))[t];
+      }
+    }
+  } else if (p.greedy && i < 2 * k) {
+    t = tok[i];
   }
+  const double u_draw = p.greedy ? 0.0 : uniform_of(rw[2 * k]);
+  combine_rows(p, b, fb, s_st);
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  SeqState ss = {};
+  for (int r = threadIdx.x; r < rows; r += kAcceptThreads)
+    if (!row_unused(p, r, fb)) p.stats[size_t(b) * rows + r] = s_st[r];
   if (p.greedy) {
+    // primary token i: the arg max of target row i; the fallback's token 0
+    // is scored by the primary's target row 0, its token i >= 1 by its own
+    if (i < k) s_acc[i] = in_vocab(t, V) && t == s_st[target_row(k, 0, i)].arg;
+    if (i >= k && i < 2 * k) {
+      const int f = i - k;
+      s_acc[i] = in_vocab(t, V) && t == s_st[f == 0 ? target_row(k, 0, 0) : target_row(k, 1, f)].arg;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
     int j = 0, n, br, nx;
-    while (j < k && in_vocab(tok[j], V) && tok[j] == st[target_row(k, 0, j)].arg) ++j;
+    while (j < k && s_acc[j]) ++j;
     if (j == k || j > 0 || !fb) {
-      n = j; br = 0; nx = st[target_row(k, 0, j)].arg;
-    } else if (!(in_vocab(tok[k], V) && tok[k] == st[target_row(k, 0, 0)].arg)) {
-      n = 0; br = 0; nx = st[target_row(k, 0, 0)].arg;
+      n = j; br = 0; nx = s_st[target_row(k, 0, j)].arg;
+    } else if (!s_acc[k]) {
+      n = 0; br = 0; nx = s_st[target_row(k, 0, 0)].arg;
     } else {
       j = 1;
-      while (j < k && in_vocab(tok[k + j], V) && tok[k + j] == st[target_row(k, 1, j)].arg) ++j;
-      n = j; br = 1; nx = st[target_row(k, 1, j)].arg;
+      while (j < k && s_acc[k + j]) ++j;
+      n = j; br = 1; nx = s_st[target_row(k, 1, j)].arg;
     }
     p.n_accept[b] = n;
     p.branch[b] = br;
     p.next_token[b] = nx;
+    SeqState ss = {};
     ss.stage = kStageDone;
     p.state[b] = ss;
     return;
   }
-  const double it = p.inv_tau;
-  const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
-  auto uni = [&](int w) { return double(rw[w]) * (1.0 / 4294967296.0); };
-  // primary chain: accept t iff u q(t) < p(t)
-  int j = 0;
-  for (; j < k; ++j) {
-    if (!in_vocab(tok[j], V)) break;
-    if (!(uni(j) * s_qt[j] < s_pt[j])) break;
+  // primary chain: token i is accepted iff u q_i(t) < p_i(t)
+  if (i < k) {
+    bool acc = false;
+    if (in_vocab(t, V)) {
+      const RowStat& rt = s_st[target_row(k, 0, i)];
+      const RowStat& rd = s_st[draft_row(k, 0, i)];
+      const double pt = exp((double(zt) - double(rt.M)) * p.inv_tau) / rt.S;
+      const double qt = exp((double(zd) - double(rd.M)) * p.inv_tau) / rd.S;
+      acc = u * qt < pt;
+    }
+    s_acc[i] = acc;
   }
-  (void)it;
-  ss.u = uni(2 * k);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int j = 0;
+  while (j < k && s_acc[j]) ++j;
+  SeqState ss = {};
+  ss.u = u_draw;
   if (j == k) {
     ss.stage = kStageDraw; ss.kind = kDrawRow; ss.ra = target_row(k, 0, k); ss.n = k; ss.branch = 0;
   } else if (j > 0 || !fb) {
@@ -428,6 +524,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_decide_kernel(const Acc
   } else {
     ss.stage = kStageFallback; ss.ra = target_row(k, 0, 0); ss.rc = draft_row(k, 0, 0); ss.rm = draft_row(k, 1, 0);
   }
+  carry_rows(ss, s_st);
   p.state[b] = ss;
 }
 
@@ -440,7 +537,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_fbsum_kernel(const Acce
   const int b = blockIdx.x / n_parts;
   const SeqState ss = p.state[b];
   if (ss.stage != kStageFallback) return;
-  const Dist a = dist_of(p, b, ss.ra), c = dist_of(p, b, ss.rc), m = dist_of(p, b, ss.rm);
+  const Dist a = dist_in(p, b, ss, 0), c = dist_in(p, b, ss, 1), m = dist_in(p, b, ss, 2);
   const int per_part = (p.slice + kPartsPerSlice - 1) / kPartsPerSlice;
   const int t0 = part * per_part;
   const int t1 = min(p.V, t0 + per_part);
@@ -474,52 +571,93 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_fbsum_kernel(const Acce
 // ---------------------------------------------------------------------------
 __global__ void accept_fallback_kernel(const AcceptParams p) {
   const int b = blockIdx.x;
-  SeqState ss = p.state[b];
-  if (ss.stage != kStageFallback) return;
   const int k = p.k, V = p.V;
   const double it = p.inv_tau;
   const int32_t* tok = p.tokens + size_t(b) * 2 * k;
-  // the fallback chain's p'_i(y_i) and q'_i(y_i) for i >= 1, one lane per position
-  __shared__ double s_pt[64], s_qt[64];
-  if (threadIdx.x >= 1 && int(threadIdx.x) < k) {
-    const int i = threadIdx.x, t = tok[k + i];
-    const bool ok = in_vocab(t, V);
-    s_pt[i] = ok ? prob(dist_of(p, b, target_row(k, 1, i)), it, t) : 0.0;
-    s_qt[i] = ok ? prob(dist_of(p, b, draft_row(k, 1, i)), it, t) : 0.0;
+  const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
+  const RowStat* st = p.stats + size_t(b) * (4 * k + 2);
+  // the inputs of every test are loaded with the state (the rows involved
+  // are fixed): lane 0 the fallback's first token y, its uniform, its logits
+  // in rows a, c, m (the primary's first target and draft rows, the
+  // fallback's first draft row) and the statistics of the bonus row k;
+  // lane i in 1 .. k-1 the fallback chain's token i, its uniform, its rows'
+  // statistics and logits
+  __shared__ int s_acc[64];
+  __shared__ RowStat s_rt[65], s_rd[64];
+  SeqState ss = p.state[b];
+  const int i = threadIdx.x;
+  int y = -1;
+  double u = 0.0;
+  float z1 = 0.f, z2 = 0.f, z3 = 0.f;
+  RowStat rt = {}, rd = {};
+  if (i == 0) {
+    y = tok[k];
+    u = uniform_of(rw[k]);
+    rt = st[target_row(k, 1, k)];
+    if (in_vocab(y, V)) {
+      z1 = row_ptr(p, b, target_row(k, 0, 0))[y];
+      z2 = row_ptr(p, b, draft_row(k, 0, 0))[y];
+      z3 = row_ptr(p, b, draft_row(k, 1, 0))[y];
+    }
+  } else if (i < k) {
+    y = tok[k + i];
+    u = uniform_of(rw[k + i]);
+    rt = st[target_row(k, 1, i)];
+    rd = st[draft_row(k, 1, i)];
+    if (in_vocab(y, V)) {
+      z1 = row_ptr(p, b, target_row(k, 1, i))[y];
+      z2 = row_ptr(p, b, draft_row(k, 1, i))[y];
+    }
   }
-  // the residual masses: the parts' sums, lane i taking parts i, i + 64, ...
+  // the residual masses: the parts' sums, lane l taking parts l, l + 64, ...
   // in order, then a fixed xor tree over the lanes
   double Wr = 0.0, Wm = 0.0;
   const int n_parts = p.split * kPartsPerSlice;
-  for (int i = threadIdx.x; i < n_parts; i += 64) {
-    Wr += p.sums[(size_t(b) * n_parts + i) * 2];
-    Wm += p.sums[(size_t(b) * n_parts + i) * 2 + 1];
+  for (int q = threadIdx.x; q < n_parts; q += 64) {
+    Wr += p.sums[(size_t(b) * n_parts + q) * 2];
+    Wm += p.sums[(size_t(b) * n_parts + q) * 2 + 1];
   }
+  if (ss.stage != kStageFallback) return;
   Wr = wave_sum(Wr);
   Wm = wave_sum(Wm);
+  // lanes 1 .. k-1: the fallback chain's test at position i, u q'_i(y_i) < p'_i(y_i)
+  if (i == 0) s_rt[k] = rt;
+  if (i >= 1 && i < k) {
+    s_rt[i] = rt;
+    s_rd[i] = rd;
+    s_acc[i] = in_vocab(y, V) && u * (exp((double(z2) - double(rd.M)) * it) / rd.S) <
+                                     exp((double(z1) - double(rt.M)) * it) / rt.S;
+  }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
-  auto uni = [&](int w) { return double(rw[w]) * (1.0 / 4294967296.0); };
+  // the fallback's first token y: accepted iff u q'(y) < r(y), with the
+  // residual target r = max(0, p_a - p_c) / Wr (p_a when Wr = 0) and the
+  // fallback's draft distribution q' = max(0, p_m - p_c) / Wm (0 when Wm = 0)
   ss.Wr = Wr;
   ss.Wm = Wm;
   ss.kind = kDrawRestart;
-  const DrawSpec d = spec_of(p, b, ss);
-  const int y = tok[k];
-  const bool acc = in_vocab(y, V) && uni(k) * fallback_q(d, it, y) < fallback_r(d, it, y);
+  bool acc = false;
+  if (in_vocab(y, V)) {
+    const double pa = exp((double(z1) - double(ss.M[0])) * it) / ss.S[0];
+    const double pc = exp((double(z2) - double(ss.M[1])) * it) / ss.S[1];
+    const double pm = exp((double(z3) - double(ss.M[2])) * it) / ss.S[2];
+    const double r = Wr > 0.0 ? fmax(pa - pc, 0.0) / Wr : pa;
+    const double q = Wm > 0.0 ? fmax(pm - pc, 0.0) / Wm : 0.0;
+    acc = u * q < r;
+  }
   if (!acc) {
     ss.n = 0; ss.branch = 0;  // restart: draw from max(0, r - q')
   } else {
     int jj = 1;
-    for (; jj < k; ++jj) {
-      if (!in_vocab(tok[k + jj], V)) break;
-      if (!(uni(k + jj) * s_qt[jj] < s_pt[jj])) break;
-    }
+    while (jj < k && s_acc[jj]) ++jj;
     ss.n = jj; ss.branch = 1;
     if (jj == k) {
       ss.kind = kDrawRow; ss.ra = target_row(k, 1, k);
+      ss.S[0] = s_rt[k].S; ss.M[0] = s_rt[k].M;
     } else {
       ss.kind = kDrawResidual; ss.ra = target_row(k, 1, jj); ss.rc = draft_row(k, 1, jj);
+      ss.S[0] = s_rt[jj].S; ss.M[0] = s_rt[jj].M;
+      ss.S[1] = s_rd[jj].S; ss.M[1] = s_rd[jj].M;
     }
   }
   ss.stage = kStageDraw;
@@ -529,8 +667,10 @@ __global__ void accept_fallback_kernel(const AcceptParams p) {
 // ---------------------------------------------------------------------------
 // 5. tile sums of the final draw's weights, per quarter slice
 // ---------------------------------------------------------------------------
+constexpr int kMaxPartTiles = 1024;  // tiles per part at the largest vocabulary (2^24 over 64 slices)
 __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const AcceptParams p) {
   __shared__ int s_last;
+  __shared__ double s_ts[kMaxPartTiles];
   // kPartsPerSlice parts per slice, so that a small batch still fills the chip
   const int n_parts = p.split * kPartsPerSlice;
   const int part = blockIdx.x % n_parts;
@@ -565,39 +705,59 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const Ac
       const double w = t < p.V ? weight_of(d, p.inv_tau, za[j], zc[j], zm[j]) : 0.0;
       if (w > 0.0) last = t;
       const double ts = wave_sum(w);
-      if (lane == 0) p.tiles[size_t(b) * p.n_tiles + tile] = ts;
+      if (lane == 0) {
+        p.tiles[size_t(b) * p.n_tiles + tile] = ts;
+        s_ts[tile - tile0] = ts;
+      }
     }
   }
   atomicMax(&s_last, last);
   __syncthreads();
-  if (threadIdx.x == 0) p.last[size_t(b) * n_parts + part] = s_last;
+  if (threadIdx.x == 0) {
+    p.last[size_t(b) * n_parts + part] = s_last;
+    // the part's total: its tile sums added in tile order (the pick walks the
+    // crossing part's tiles in the same order from 0, so its running sums
+    // meet this total exactly)
+    double tot = 0.0;
+    for (int tile = tile0; tile < tile1; ++tile) tot += s_ts[tile - tile0];
+    p.ptot[size_t(b) * n_parts + part] = tot;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 6. the index where the running sum crosses u * total
 // ---------------------------------------------------------------------------
-constexpr int kPickBatch = 16;  // rows of 64 tile sums loaded together
+// The running sum is taken part by part (each part's total), then tile by
+// tile inside the crossing part, then index by index inside the crossing
+// tile; the part totals and the tiles inside a part are added in order from
+// 0, as the part totals were formed, so every level meets the next exactly.
+constexpr int kMaxParts = kAcceptMaxSplit * kPartsPerSlice;
 __global__ __launch_bounds__(kAcceptThreads) void accept_pick_kernel(const AcceptParams p) {
-  __shared__ double s_total;
+  __shared__ double s_v[kMaxPartTiles > kMaxParts ? kMaxPartTiles : kMaxParts];
+  __shared__ double s_total, s_base;
+  __shared__ int s_hit;
   const int b = blockIdx.x;
-  SeqState ss = p.state[b];
-  if (ss.stage != kStageDraw) return;
+  const int n_parts = p.split * kPartsPerSlice;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const double* tiles = p.tiles + size_t(b) * p.n_tiles;
-  if (wave == 0) {
-    // total of the tile sums, in tile order (16 rows of 64 loaded at a time)
-    double run = 0.0;
-    for (int base = 0; base < p.n_tiles; base += kPickBatch * 64) {
-      double ts[kPickBatch];
-#pragma unroll
-      for (int i = 0; i < kPickBatch; ++i) {
-        const int tile = base + i * 64 + lane;
-        ts[i] = tile < p.n_tiles ? tiles[tile] : 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < kPickBatch; ++i) run += __shfl(wave_inclusive_scan(ts[i]), 63);
+  // the part totals do not depend on the state: loaded with it
+  for (int q = threadIdx.x; q < n_parts; q += kAcceptThreads) s_v[q] = p.ptot[size_t(b) * n_parts + q];
+  SeqState ss = p.state[b];
+  __syncthreads();
+  if (ss.stage != kStageDraw) return;
+  const DrawSpec spec = spec_of(p, b, ss);
+  if (threadIdx.x == 0) {
+    double total = 0.0;
+    for (int q = 0; q < n_parts; ++q) total += s_v[q];
+    const double target = ss.u * total;
+    double base = 0.0;
+    int hit = -1;
+    for (int q = 0; q < n_parts && hit < 0; ++q) {
+      if (base + s_v[q] > target) hit = q;
+      else base += s_v[q];
     }
-    if (lane == 0) s_total = run;
+    s_total = total;
+    s_base = base;
+    s_hit = hit;
   }
   __syncthreads();
   const double total = s_total;
@@ -614,43 +774,45 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_pick_kernel(const Accep
     }
     return;
   }
-  if (wave != 0) return;
   const double target = ss.u * total;
-  double run = 0.0;
-  int hit = -1;
-  for (int base = 0; base < p.n_tiles && hit < 0; base += kPickBatch * 64) {
-    double ts[kPickBatch];
-#pragma unroll
-    for (int i = 0; i < kPickBatch; ++i) {
-      const int tile = base + i * 64 + lane;
-      ts[i] = tile < p.n_tiles ? tiles[tile] : 0.0;
-    }
-#pragma unroll
-    for (int i = 0; i < kPickBatch; ++i) {
-      if (hit >= 0) break;
-      const int i0 = base + i * 64;
-      const double incl = wave_inclusive_scan(ts[i]);
-      const unsigned long long over = __ballot(i0 + lane < p.n_tiles && run + incl > target);
-      if (over != 0ull) {
-        const int l = __ffsll(static_cast<long long>(over)) - 1;
-        hit = i0 + l;
-        run += __shfl(incl - ts[i], l);
-      } else {
-        run += __shfl(incl, 63);
-      }
-    }
-  }
+  const int part = s_hit;
   int result = -1;
-  if (hit >= 0) {
-    const DrawSpec d = spec_of(p, b, ss);
-    const int t = hit * kAcceptTile + lane;
-    const double w = t < p.V ? weight(d, p.inv_tau, t) : 0.0;
-    const double incl = run + wave_inclusive_scan(w);
-    const unsigned long long over = __ballot(t < p.V && incl > target);
-    if (over != 0ull) result = hit * kAcceptTile + __ffsll(static_cast<long long>(over)) - 1;
+  if (part >= 0) {
+    // the crossing part's tiles, in order from the part's start
+    const int per_part = (p.slice / kAcceptTile + kPartsPerSlice - 1) / kPartsPerSlice;
+    const int tile0 = part * per_part;
+    const int tile1 = min(p.n_tiles, tile0 + per_part);
+    __syncthreads();
+    for (int tile = tile0 + threadIdx.x; tile < tile1; tile += kAcceptThreads)
+      s_v[tile - tile0] = p.tiles[size_t(b) * p.n_tiles + tile];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const double base = s_base;
+      double pre = 0.0;
+      int hit = -1;
+      for (int tile = tile0; tile < tile1 && hit < 0; ++tile) {
+        if (base + (pre + s_v[tile - tile0]) > target) hit = tile;
+        else pre += s_v[tile - tile0];
+      }
+      s_hit = hit;
+      s_base = base + pre;
+    }
+    __syncthreads();
+    const int hit = s_hit;
+    if (wave == 0 && hit >= 0) {
+      const int t = hit * kAcceptTile + lane;
+      const double w = t < p.V ? weight(spec, p.inv_tau, t) : 0.0;
+      const double incl = s_base + wave_inclusive_scan(w);
+      const unsigned long long over = __ballot(t < p.V && incl > target);
+      const unsigned long long pos = __ballot(t < p.V && w > 0.0);
+      if (over != 0ull)
+        result = hit * kAcceptTile + __ffsll(static_cast<long long>(over)) - 1;
+      else if (pos != 0ull)  // rounding left no crossing in the tile: its last index with weight > 0
+        result = hit * kAcceptTile + 63 - __builtin_clzll(pos);
+    }
   }
+  if (wave != 0) return;
   if (result < 0) {  // rounding left no crossing: the last index with weight > 0
-    const int n_parts = p.split * kPartsPerSlice;
     for (int i = 0; i < n_parts; ++i) result = max(result, p.last[size_t(b) * n_parts + i]);
   }
   if (lane == 0) {

@@ -1182,6 +1182,7 @@ extern "C" ripe_status_t ripe_accept(const ripe_accept_desc_t* desc, const float
   p.sums = reinterpret_cast<double*>(ws + L.off_sums);
   p.tiles = reinterpret_cast<double*>(ws + L.off_tiles);
   p.last = reinterpret_cast<int32_t*>(ws + L.off_last);
+  p.ptot = reinterpret_cast<double*>(ws + L.off_ptot);
   p.split = L.split;
   p.slice = L.slice;
   p.n_tiles = L.n_tiles;
