@@ -46,7 +46,7 @@ struct AcceptParams {
   // workspace
   RowStat* part;           // [B][4k+2][split]: per-slice statistics
   RowStat* stats;          // [B][4k+2]
-  SeqState* state;         // [B]
+  SeqState* state;         // [2B]: after the primary chain's tests; [B + b]: after a fallback's
   double* sums;            // [B][split * kPartsPerSlice][2]: residual masses per part
   double* tiles;           // [B][n_tiles]: tile sums of the final draw's weights
   int32_t* last;           // [B][split * kPartsPerSlice]: last index with weight > 0 per part
@@ -79,7 +79,7 @@ inline AcceptLayout accept_layout(int64_t B, int64_t k, int64_t V) {
   int64_t off = 0;
   L.off_part = off;  off += accept_align(B * rows * split * int64_t(sizeof(RowStat)));
   L.off_stats = off; off += accept_align(B * rows * int64_t(sizeof(RowStat)));
-  L.off_state = off; off += accept_align(B * int64_t(sizeof(SeqState)));
+  L.off_state = off; off += accept_align(2 * B * int64_t(sizeof(SeqState)));
   L.off_sums = off;  off += accept_align(B * split * kPartsPerSlice * 2 * int64_t(sizeof(double)));
   L.off_tiles = off; off += accept_align(B * L.n_tiles * int64_t(sizeof(double)));
   L.off_last = off;  off += accept_align(B * split * kPartsPerSlice * int64_t(sizeof(int32_t)));

@@ -10,20 +10,23 @@
 // sampling keeps each output's probability under ordinary decoding.  The
 // rules are spelled out beside the declaration of ripe_accept.
 //
-// How: a short pipeline of launches; the per-index work is spread over
-// (sequence, slice of the vocabulary) work-groups and the decisions run on
-// one work-group per sequence between them.
+// How: four launches (two for greedy calls).  The per-index work is spread
+// over (sequence, slice of the vocabulary) work-groups; the decisions run on
+// one work-group per sequence, or again in every work-group of a sweep that
+// needs them, which costs less than a launch of their own.
 //   accept_stats_kernel     per (row, slice): arg max (lowest index on ties),
 //                           max, and sum exp((z - max) / tau) (a table-driven
 //                           exp, below); rows no decision can read are skipped
 //   accept_decide_kernel    per sequence: combines the slices into each row's
 //                           statistics; greedy decisions (final), or the
-//                           primary chain's speculative tests
-//   accept_fbsum_kernel     per (sequence, quarter slice), only after a first-token
-//                           rejection with a fallback: the residual masses
-//   accept_fallback_kernel  per sequence: the fallback's tests
-//   accept_drawsum_kernel   per (sequence, quarter slice): sums of the final draw's
-//                           weights over tiles of 64 indices
+//                           primary chain's speculative tests; and, sampling,
+//                           per (sequence with a fallback, quarter slice) the
+//                           fallback's residual masses, before the tests say
+//                           whether they are needed
+//   accept_drawsum_kernel   per (sequence, quarter slice): the fallback's tests
+//                           where the primary's first token was rejected, then
+//                           sums of the final draw's weights over tiles of 64
+//                           indices
 //   accept_pick_kernel      per sequence: the part, then the tile, then the index
 //                           where the running sum crosses u * total
 // Probabilities, sums and decisions are in double; the logits are float.
@@ -401,6 +404,22 @@ constexpr int kMaxRows = 4 * 64 + 2;  // rows of one sequence at the largest k
 constexpr int kWaves = kAcceptThreads / 64;
 constexpr int kRowBatch = 4;          // rows whose slice statistics one wavefront loads together
 
+// One row's statistics from its slices', across a wavefront (lane i holds
+// slice i; lanes past the slices hold {0, -inf, INT_MAX}); every lane
+// returns them.
+__device__ inline RowStat combine_one(const AcceptParams& p, const RowStat& st) {
+  float M = st.M;
+  int arg = st.arg;
+  for (int off = 32; off > 0; off >>= 1) {  // better() is a total order: every lane ends equal
+    const float M2 = __shfl_xor(M, off);
+    const int a2 = __shfl_xor(arg, off);
+    better(M, arg, M2, a2);
+  }
+  double S = 0.0;
+  if (!p.greedy) S = wave_sum(st.M > -INFINITY ? st.S * exp((double(st.M) - double(M)) * p.inv_tau) : 0.0);
+  return RowStat{S, M, arg};
+}
+
 // The sequence's row statistics into out[rows] (LDS), for every row a
 // decision can read: the max and lowest arg max over the slices, and
 // S = sum_i S_i exp((M_i - M) / tau) by a fixed xor tree over the slices.
@@ -420,23 +439,73 @@ __device__ void combine_rows(const AcceptParams& p, int b, bool fb, RowStat* out
     for (int j = 0; j < kRowBatch; ++j) {
       const int r = r0 + j * kWaves;
       if (r >= rows || row_unused(p, r, fb)) continue;  // the same for the whole wavefront
-      float M = st[j].M;
-      int arg = st[j].arg;
-      for (int off = 32; off > 0; off >>= 1) {  // better() is a total order: every lane ends equal
-        const float M2 = __shfl_xor(M, off);
-        const int a2 = __shfl_xor(arg, off);
-        better(M, arg, M2, a2);
-      }
-      double S = 0.0;
-      if (!p.greedy) S = wave_sum(st[j].M > -INFINITY ? st[j].S * exp((double(st[j].M) - double(M)) * p.inv_tau) : 0.0);
-      if (lane == 0) out[r] = RowStat{S, M, arg};
+      const RowStat c = combine_one(p, st[j]);
+      if (lane == 0) out[r] = c;
     }
   }
 }
 
 __device__ inline double uniform_of(uint32_t w) { return double(w) * (1.0 / 4294967296.0); }
 
+// ---------------------------------------------------------------------------
+// the fallback's residual masses, per quarter slice (in the decisions' launch)
+// ---------------------------------------------------------------------------
+// For every sequence with a fallback, before its primary chain is decided:
+// the rows involved are fixed (a, c: the primary's first target and draft
+// rows; m: the fallback's first draft row), and this part combines their
+// statistics itself, as the decisions do, so it needs nothing from them.  A
+// sequence whose first token is then accepted leaves its sums unread.
+__device__ void residual_part(const AcceptParams& p, int b, int part) {
+  __shared__ RowStat s_r[3];
+  const int k = p.k, rows = 4 * k + 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ra = target_row(k, 0, 0), rc = draft_row(k, 0, 0), rm = draft_row(k, 1, 0);
+  if (wave < 3) {
+    const int r = wave == 0 ? ra : (wave == 1 ? rc : rm);
+    const RowStat* base = p.part + (size_t(b) * rows + r) * p.split;
+    const RowStat c = combine_one(p, lane < p.split ? base[lane] : RowStat{0.0, -INFINITY, 0x7fffffff});
+    if (lane == 0) s_r[wave] = c;
+  }
+  __syncthreads();
+  const Dist a{row_ptr(p, b, ra), double(s_r[0].M), s_r[0].S};
+  const Dist c{row_ptr(p, b, rc), double(s_r[1].M), s_r[1].S};
+  const Dist m{row_ptr(p, b, rm), double(s_r[2].M), s_r[2].S};
+  const int n_parts = p.split * kPartsPerSlice;
+  const int per_part = (p.slice + kPartsPerSlice - 1) / kPartsPerSlice;
+  const int t0 = part * per_part;
+  const int t1 = min(p.V, t0 + per_part);
+  double wr = 0.0, wm = 0.0;
+  for (int t = t0 + threadIdx.x; t < t1; t += kLoadBatch * kAcceptThreads) {
+    float za[kLoadBatch], zc[kLoadBatch], zm[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      za[j] = load_or(a.z, t + j * kAcceptThreads, t1, 0.f);
+      zc[j] = load_or(c.z, t + j * kAcceptThreads, t1, 0.f);
+      zm[j] = load_or(m.z, t + j * kAcceptThreads, t1, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j)
+      if (t + j * kAcceptThreads < t1) {
+        const double pc = prob_of(c, p.inv_tau, zc[j]);
+        wr += fmax(prob_of(a, p.inv_tau, za[j]) - pc, 0.0);
+        wm += fmax(prob_of(m, p.inv_tau, zm[j]) - pc, 0.0);
+      }
+  }
+  wr = wg_sum(wr);
+  wm = wg_sum(wm);
+  if (threadIdx.x == 0) {
+    p.sums[(size_t(b) * n_parts + part) * 2] = wr;
+    p.sums[(size_t(b) * n_parts + part) * 2 + 1] = wm;
+  }
+}
+
 __global__ __launch_bounds__(kAcceptThreads) void accept_decide_kernel(const AcceptParams p) {
+  if (int(blockIdx.x) >= p.B) {  // (sampling) the residual-mass parts of sequences with a fallback
+    const int n_parts = p.split * kPartsPerSlice;
+    const int q = int(blockIdx.x) - p.B;
+    if (p.has_fb[q / n_parts] != 0) residual_part(p, q / n_parts, q % n_parts);
+    return;
+  }
   __shared__ RowStat s_st[kMaxRows];
   __shared__ int s_acc[128];
   const int b = blockIdx.x;
@@ -531,62 +600,26 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_decide_kernel(const Acc
 }
 
 // ---------------------------------------------------------------------------
-// 3. the fallback's residual masses, per quarter slice
+// the fallback chain's tests (in the draw sums' launch)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kAcceptThreads) void accept_fbsum_kernel(const AcceptParams p) {
-  const int n_parts = p.split * kPartsPerSlice;
-  const int part = blockIdx.x % n_parts;
-  const int b = blockIdx.x / n_parts;
-  const SeqState ss = p.state[b];
-  if (ss.stage != kStageFallback) return;
-  const Dist a = dist_in(p, b, ss, 0), c = dist_in(p, b, ss, 1), m = dist_in(p, b, ss, 2);
-  const int per_part = (p.slice + kPartsPerSlice - 1) / kPartsPerSlice;
-  const int t0 = part * per_part;
-  const int t1 = min(p.V, t0 + per_part);
-  double wr = 0.0, wm = 0.0;
-  for (int t = t0 + threadIdx.x; t < t1; t += kLoadBatch * kAcceptThreads) {
-    float za[kLoadBatch], zc[kLoadBatch], zm[kLoadBatch];
-#pragma unroll
-    for (int j = 0; j < kLoadBatch; ++j) {
-      za[j] = load_or(a.z, t + j * kAcceptThreads, t1, 0.f);
-      zc[j] = load_or(c.z, t + j * kAcceptThreads, t1, 0.f);
-      zm[j] = load_or(m.z, t + j * kAcceptThreads, t1, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < kLoadBatch; ++j)
-      if (t + j * kAcceptThreads < t1) {
-        const double pc = prob_of(c, p.inv_tau, zc[j]);
-        wr += fmax(prob_of(a, p.inv_tau, za[j]) - pc, 0.0);
-        wm += fmax(prob_of(m, p.inv_tau, zm[j]) - pc, 0.0);
-      }
-  }
-  wr = wg_sum(wr);
-  wm = wg_sum(wm);
-  if (threadIdx.x == 0) {
-    p.sums[(size_t(b) * n_parts + part) * 2] = wr;
-    p.sums[(size_t(b) * n_parts + part) * 2 + 1] = wm;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 4. the fallback chain's tests
-// ---------------------------------------------------------------------------
-__global__ void accept_fallback_kernel(const AcceptParams p) {
-  const int b = blockIdx.x;
+// Taken by every work-group of a sequence left at the fallback stage, the
+// same inputs and arithmetic in each; every thread returns the final state.
+__device__ SeqState fallback_decide(const AcceptParams& p, int b, SeqState ss) {
   const int k = p.k, V = p.V;
   const double it = p.inv_tau;
   const int32_t* tok = p.tokens + size_t(b) * 2 * k;
   const uint32_t* rw = p.rand + size_t(b) * (2 * k + 1);
   const RowStat* st = p.stats + size_t(b) * (4 * k + 2);
-  // the inputs of every test are loaded with the state (the rows involved
-  // are fixed): lane 0 the fallback's first token y, its uniform, its logits
-  // in rows a, c, m (the primary's first target and draft rows, the
-  // fallback's first draft row) and the statistics of the bonus row k;
-  // lane i in 1 .. k-1 the fallback chain's token i, its uniform, its rows'
-  // statistics and logits
+  // the inputs of every test are loaded together: thread 0 the fallback's
+  // first token y, its uniform, its logits in rows a, c, m (the primary's
+  // first target and draft rows, the fallback's first draft row) and the
+  // statistics of the bonus row k; thread i in 1 .. k-1 the fallback chain's
+  // token i, its uniform, its rows' statistics and logits; wavefront 0 the
+  // residual masses
   __shared__ int s_acc[64];
   __shared__ RowStat s_rt[65], s_rd[64];
-  SeqState ss = p.state[b];
+  __shared__ double s_w[2];
+  __shared__ SeqState s_ss;
   const int i = threadIdx.x;
   int y = -1;
   double u = 0.0;
@@ -611,18 +644,23 @@ __global__ void accept_fallback_kernel(const AcceptParams p) {
       z2 = row_ptr(p, b, draft_row(k, 1, i))[y];
     }
   }
-  // the residual masses: the parts' sums, lane l taking parts l, l + 64, ...
-  // in order, then a fixed xor tree over the lanes
-  double Wr = 0.0, Wm = 0.0;
-  const int n_parts = p.split * kPartsPerSlice;
-  for (int q = threadIdx.x; q < n_parts; q += 64) {
-    Wr += p.sums[(size_t(b) * n_parts + q) * 2];
-    Wm += p.sums[(size_t(b) * n_parts + q) * 2 + 1];
+  if (i < 64) {
+    // the residual masses: the parts' sums, lane l taking parts l, l + 64,
+    // ... in order, then a fixed xor tree over the lanes
+    double Wr = 0.0, Wm = 0.0;
+    const int n_parts = p.split * kPartsPerSlice;
+    for (int q = i; q < n_parts; q += 64) {
+      Wr += p.sums[(size_t(b) * n_parts + q) * 2];
+      Wm += p.sums[(size_t(b) * n_parts + q) * 2 + 1];
+    }
+    Wr = wave_sum(Wr);
+    Wm = wave_sum(Wm);
+    if (i == 0) {
+      s_w[0] = Wr;
+      s_w[1] = Wm;
+    }
   }
-  if (ss.stage != kStageFallback) return;
-  Wr = wave_sum(Wr);
-  Wm = wave_sum(Wm);
-  // lanes 1 .. k-1: the fallback chain's test at position i, u q'_i(y_i) < p'_i(y_i)
+  // threads 1 .. k-1: the fallback chain's test at position i, u q'_i(y_i) < p'_i(y_i)
   if (i == 0) s_rt[k] = rt;
   if (i >= 1 && i < k) {
     s_rt[i] = rt;
@@ -631,43 +669,47 @@ __global__ void accept_fallback_kernel(const AcceptParams p) {
                                      exp((double(z1) - double(rt.M)) * it) / rt.S;
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  // the fallback's first token y: accepted iff u q'(y) < r(y), with the
-  // residual target r = max(0, p_a - p_c) / Wr (p_a when Wr = 0) and the
-  // fallback's draft distribution q' = max(0, p_m - p_c) / Wm (0 when Wm = 0)
-  ss.Wr = Wr;
-  ss.Wm = Wm;
-  ss.kind = kDrawRestart;
-  bool acc = false;
-  if (in_vocab(y, V)) {
-    const double pa = exp((double(z1) - double(ss.M[0])) * it) / ss.S[0];
-    const double pc = exp((double(z2) - double(ss.M[1])) * it) / ss.S[1];
-    const double pm = exp((double(z3) - double(ss.M[2])) * it) / ss.S[2];
-    const double r = Wr > 0.0 ? fmax(pa - pc, 0.0) / Wr : pa;
-    const double q = Wm > 0.0 ? fmax(pm - pc, 0.0) / Wm : 0.0;
-    acc = u * q < r;
-  }
-  if (!acc) {
-    ss.n = 0; ss.branch = 0;  // restart: draw from max(0, r - q')
-  } else {
-    int jj = 1;
-    while (jj < k && s_acc[jj]) ++jj;
-    ss.n = jj; ss.branch = 1;
-    if (jj == k) {
-      ss.kind = kDrawRow; ss.ra = target_row(k, 1, k);
-      ss.S[0] = s_rt[k].S; ss.M[0] = s_rt[k].M;
-    } else {
-      ss.kind = kDrawResidual; ss.ra = target_row(k, 1, jj); ss.rc = draft_row(k, 1, jj);
-      ss.S[0] = s_rt[jj].S; ss.M[0] = s_rt[jj].M;
-      ss.S[1] = s_rd[jj].S; ss.M[1] = s_rd[jj].M;
+  if (i == 0) {
+    // the fallback's first token y: accepted iff u q'(y) < r(y), with the
+    // residual target r = max(0, p_a - p_c) / Wr (p_a when Wr = 0) and the
+    // fallback's draft distribution q' = max(0, p_m - p_c) / Wm (0 when Wm = 0)
+    const double Wr = s_w[0], Wm = s_w[1];
+    ss.Wr = Wr;
+    ss.Wm = Wm;
+    ss.kind = kDrawRestart;
+    bool acc = false;
+    if (in_vocab(y, V)) {
+      const double pa = exp((double(z1) - double(ss.M[0])) * it) / ss.S[0];
+      const double pc = exp((double(z2) - double(ss.M[1])) * it) / ss.S[1];
+      const double pm = exp((double(z3) - double(ss.M[2])) * it) / ss.S[2];
+      const double r = Wr > 0.0 ? fmax(pa - pc, 0.0) / Wr : pa;
+      const double q = Wm > 0.0 ? fmax(pm - pc, 0.0) / Wm : 0.0;
+      acc = u * q < r;
     }
+    if (!acc) {
+      ss.n = 0; ss.branch = 0;  // restart: draw from max(0, r - q')
+    } else {
+      int jj = 1;
+      while (jj < k && s_acc[jj]) ++jj;
+      ss.n = jj; ss.branch = 1;
+      if (jj == k) {
+        ss.kind = kDrawRow; ss.ra = target_row(k, 1, k);
+        ss.S[0] = s_rt[k].S; ss.M[0] = s_rt[k].M;
+      } else {
+        ss.kind = kDrawResidual; ss.ra = target_row(k, 1, jj); ss.rc = draft_row(k, 1, jj);
+        ss.S[0] = s_rt[jj].S; ss.M[0] = s_rt[jj].M;
+        ss.S[1] = s_rd[jj].S; ss.M[1] = s_rd[jj].M;
+      }
+    }
+    ss.stage = kStageDraw;
+    s_ss = ss;
   }
-  ss.stage = kStageDraw;
-  p.state[b] = ss;
+  __syncthreads();
+  return s_ss;
 }
 
 // ---------------------------------------------------------------------------
-// 5. tile sums of the final draw's weights, per quarter slice
+// 3. tile sums of the final draw's weights, per quarter slice
 // ---------------------------------------------------------------------------
 constexpr int kMaxPartTiles = 1024;  // tiles per part at the largest vocabulary (2^24 over 64 slices)
 __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const AcceptParams p) {
@@ -677,7 +719,13 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const Ac
   const int n_parts = p.split * kPartsPerSlice;
   const int part = blockIdx.x % n_parts;
   const int b = blockIdx.x / n_parts;
-  const SeqState ss = p.state[b];
+  SeqState ss = p.state[b];
+  if (ss.stage == kStageFallback) {
+    // the fallback's tests first; part 0 records the final state after the
+    // primary states, which the launch's other work-groups are still reading
+    ss = fallback_decide(p, b, ss);
+    if (part == 0 && threadIdx.x == 0) p.state[p.B + b] = ss;
+  }
   if (ss.stage != kStageDraw) return;
   const DrawSpec d = spec_of(p, b, ss);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -727,7 +775,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_drawsum_kernel(const Ac
 }
 
 // ---------------------------------------------------------------------------
-// 6. the index where the running sum crosses u * total
+// 4. the index where the running sum crosses u * total
 // ---------------------------------------------------------------------------
 // The running sum is taken part by part (each part's total), then tile by
 // tile inside the crossing part, then index by index inside the crossing
@@ -743,7 +791,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_pick_kernel(const Accep
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the part totals do not depend on the state: loaded with it
   for (int q = threadIdx.x; q < n_parts; q += kAcceptThreads) s_v[q] = p.ptot[size_t(b) * n_parts + q];
-  SeqState ss = p.state[b];
+  const SeqState s0 = p.state[b], s1 = p.state[p.B + b];  // (s1: the final state after a fallback)
+  SeqState ss = s0.stage == kStageFallback ? s1 : s0;
   __syncthreads();
   if (ss.stage != kStageDraw) return;
   const DrawSpec spec = spec_of(p, b, ss);
@@ -828,20 +877,20 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
   if (p.B <= 0) return hipSuccess;
   void* args[] = {const_cast<AcceptParams*>(&p)};
   const int rows = 4 * p.k + 2;
+  const int parts = p.B * p.split * kPartsPerSlice;
   struct Launch {
     const void* fn;
-    int grid, block;
+    int grid;
   };
-  const Launch all[] = {
-      {reinterpret_cast<const void*>(&accept_stats_kernel), p.B * rows * p.split, kAcceptThreads},
-      {reinterpret_cast<const void*>(&accept_decide_kernel), p.B, kAcceptThreads},
-      {reinterpret_cast<const void*>(&accept_fbsum_kernel), p.B * p.split * kPartsPerSlice, kAcceptThreads},
-      {reinterpret_cast<const void*>(&accept_fallback_kernel), p.B, 64},
-      {reinterpret_cast<const void*>(&accept_drawsum_kernel), p.B * p.split * kPartsPerSlice, kAcceptThreads},
-      {reinterpret_cast<const void*>(&accept_pick_kernel), p.B, kAcceptThreads}};
-  const int n = p.greedy ? 2 : 6;  // greedy decisions are final after the second
+  // greedy decisions are final after the second launch; sampling runs the
+  // residual-mass parts in the second launch's grid after its B sequences
+  const Launch all[] = {{reinterpret_cast<const void*>(&accept_stats_kernel), p.B * rows * p.split},
+                        {reinterpret_cast<const void*>(&accept_decide_kernel), p.greedy ? p.B : p.B + parts},
+                        {reinterpret_cast<const void*>(&accept_drawsum_kernel), parts},
+                        {reinterpret_cast<const void*>(&accept_pick_kernel), p.B}};
+  const int n = p.greedy ? 2 : 4;
   for (int i = 0; i < n; ++i) {
-    const hipError_t e = hipLaunchKernel(all[i].fn, dim3(all[i].grid), dim3(all[i].block), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(all[i].fn, dim3(all[i].grid), dim3(kAcceptThreads), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
