@@ -33,6 +33,7 @@
 // 16x16 MFMAs, lane l holds A row / B column l%16 and the k-slots of lane
 // group l/16; the accumulator lane l holds column l%16, rows 4*(l/16)+j.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 
 #include "plan.h"
@@ -426,31 +427,102 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   const SeqRec sr = p.seq[tab.piece[it.r0].s];
   const int Wb = min(p.We, sr.T);
 
-  // ---- query columns of this lane ---------------------------------------
-  // Straight-line on purpose: every lane loads from a valid address and
-  // padding columns are zeroed by selects, with no loads under divergent
-  // control flow.  The column's group, row and depth are kept to resolve each
-  // run's visibility.
-  int cgi[NB], crow[NB], cdep[NB];
-  u32x4 qf[NB][KC];
-  auto setup_columns = [&]() {
+  // ---- query columns --------------------------------------------------
+  // The group records are read with wave-uniform indices (the first kG
+  // together) and each lane selects its own: a record read with a per-lane
+  // index would be a vector load, and waiting for it waits for every vector
+  // load issued before it.  col_info(cols, ...) finds, for N columns of the
+  // chunk at once, the group (-1 for a padding column), the offset within
+  // the group's columns, the group's first draft row and its depth; a padding
+  // column gets the first group's row_start and depth.
+  constexpr int kG = 4;
+  GroupRec gr[kG];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = cc * CQ + ln + 16 * nb;
-      int row = 0, hh = 0;
-      const int gi = column_group(p, sr, col, row, hh);
-      const bool valid = gi >= 0;
-      const GroupRec& g = p.grp[valid ? gi : sr.g_begin];
-      const T* qp = static_cast<const T*>(p.q) + (size_t(g.row_start + row) * p.Hq + size_t(h) * p.G + hh) * D;
+  for (int i = 0; i < kG; ++i) gr[i] = p.grp[sr.g_begin + min(i, sr.g_count - 1)];
+  auto col_info = [&](const auto& col, auto& gi, auto& cofs, auto& crs, auto& dep) {
+    constexpr int N = int(std::extent<std::remove_reference_t<decltype(col)>>::value);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 v = ld16(qp + c * 4 * VEC + lg * VEC);
-        qf[nb][c] = valid ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-      cgi[nb] = gi;
-      crow[nb] = row;
-      cdep[nb] = g.depth;
+    for (int j = 0; j < N; ++j) {
+      gi[j] = -1;
+      cofs[j] = 0;
+      crs[j] = gr[0].row_start;
+      dep[j] = gr[0].depth;
     }
+    int off = 0;
+    auto take = [&](const GroupRec& g, int gidx, bool live) {
+      const int nc = live ? g.n_rows * p.G : 0;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const bool in = gi[j] < 0 && col[j] >= off && col[j] < off + nc;
+        gi[j] = in ? gidx : gi[j];
+        cofs[j] = in ? col[j] - off : cofs[j];
+        crs[j] = in ? g.row_start : crs[j];
+        dep[j] = in ? int(g.depth) : dep[j];
+      }
+      off += nc;
+    };
+    // no branch on the group count: every record load stays ahead of the
+    // first use
+#pragma unroll
+    for (int i = 0; i < kG; ++i) take(gr[i], sr.g_begin + i, i < sr.g_count);
+    for (int i = kG; i < sr.g_count; ++i) take(p.grp[sr.g_begin + i], sr.g_begin + i, true);
+  };
+  // This lane's MFMA columns ln + 16 nb: group, row and depth, kept to resolve
+  // each run's visibility.  A padding column's runs are all invisible
+  // (run_hi gives it 0), so every one of its scores is replaced by -inf
+  // before use and it adds nothing; the MFMA keeps columns apart, so its
+  // query values (the first group's first row) never reach another column.
+  int cgi[NB], crow[NB], cdep[NB];
+  auto setup_columns = [&]() {
+    int col[NB], cofs[NB], crs[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) col[nb] = cc * CQ + ln + 16 * nb;
+    col_info(col, cgi, cofs, crs, cdep);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) crow[nb] = cofs[nb] / p.G;
+  };
+  // The chunk's query rows are read once per work-group: thread t loads the
+  // 16-byte pieces t, t + 256, ... of the [CQ][D] chunk (column-major over
+  // pieces), which go through LDS to every wavefront's MFMA operands.  Four
+  // wavefronts loading the whole chunk each put 4x the bytes in flight at the
+  // start of the call, when the first work-group on a compute unit already
+  // holds the second one's requests back.
+  constexpr int QROW = D * E;                    // bytes of one query row
+  constexpr int QPR = QROW / 16;                 // 16-byte pieces per row
+  constexpr int QPT = (CQ * QPR + kThreads - 1) / kThreads;  // pieces per thread
+  constexpr int QLDS = QROW + 16;                // LDS row stride (padded against bank conflicts)
+  static_assert(CQ * QLDS <= verify_lds_bytes<T, D, NB>(), "query chunk must fit the LDS");
+  u32x4 qpiece[QPT];
+  auto load_q_pieces = [&]() {
+    int col[QPT], gi[QPT], cofs[QPT], crs[QPT], dep[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) col[j] = cc * CQ + min((int(threadIdx.x) + j * kThreads) / QPR, CQ - 1);
+    col_info(col, gi, cofs, crs, dep);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int row = cofs[j] / p.G;
+      const int hh = cofs[j] - row * p.G;
+      const int pc = (int(threadIdx.x) + j * kThreads) % QPR;
+      const char* qp = static_cast<const char*>(p.q) +
+                       ((size_t(crs[j] + row) * p.Hq + size_t(h) * p.G + hh) * D) * E + size_t(pc) * 16;
+      qpiece[j] = ld16(qp);
+    }
+  };
+  u32x4 qf[NB][KC];
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int i = int(threadIdx.x) + j * kThreads;
+      if (i < CQ * QPR)
+        *reinterpret_cast<u32x4*>(lds_raw + (i / QPR) * QLDS + (i % QPR) * 16) = qpiece[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        qf[nb][c] = *reinterpret_cast<const u32x4*>(lds_raw + (ln + 16 * nb) * QLDS + (c * 4 * VEC + lg * VEC) * E);
+    __syncthreads();  // the region is the draft rows' staging area afterwards
   };
   // Run-local end of what each column sees in run `pc` (0: nothing).
   auto run_hi = [&](const Piece& pc, int (&hi)[NB]) {
@@ -613,13 +685,24 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   if (have) {
     make_ctx(it.r0, cur);
     have = advance(cur, st);
+  } else {  // no streamed run: resources of no bytes (every load returns zeros)
+    cur.krs = cur.vrs = make_rsrc(p.cache_k, 0);
+    cur.r = it.r0;
+    cur.ns = cur.len = cur.c0 = 0;
+    cur.vlim = 1 << 30;
+    cur.depth = 1;
+    cur.ring = cur.per_step = false;
   }
-  if (!have) setup_columns();
+  // The query pieces go out first, then the first step's K and V (loads of a
+  // wavefront with no step address nothing: past a resource's end they
+  // return zeros without touching memory), then the query chunk is staged
+  // through LDS while K and V are in flight.
+  load_q_pieces();
+  load_k(cur, st, have, kf);
+  load_v(cur, st, have, vf);
+  stage_q();
+  setup_columns();
   if (have) {
-    // the first step's loads go out before the query setup
-    load_k(cur, st, true, kf);
-    load_v(cur, st, true, vf);
-    setup_columns();
     run_hi(tab.piece[cur.r], cur.hi);
     for (;;) {
       floatx4 sacc[2][NB];
