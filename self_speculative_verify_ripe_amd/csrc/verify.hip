@@ -417,7 +417,10 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
 
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  const uint32_t wge = tab.wg[blockIdx.x];
+  // the 16-bit entry read through its aligned 32-bit word: a scalar load
+  // (a 16-bit read is a vector load, and the first wait would cover it)
+  const uint32_t wge =
+      (reinterpret_cast<const uint32_t*>(tab.wg)[blockIdx.x >> 1] >> (16 * (blockIdx.x & 1))) & 0xFFFFu;
   if (wge == kWgEmpty) return;  // a grid position with no item (XCD placement)
   const Item it = tab.item[wge];
   const int h = it.h;
