@@ -446,6 +446,34 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     return res
 
 
+def library_read(nbytes: int, reps: int = 40, buffers: int = 4):
+    """Context for the roofline: one library reduction (torch.sum with fp32
+    accumulation) streaming a contiguous bf16 buffer of `nbytes` -- one verify
+    call's algorithmic bytes -- rotating over `buffers` buffers so that
+    consecutive launches do not hit the last-level cache: the rate at which a
+    general-purpose library kernel reads the same bytes in one launch.  It is
+    a reference point, not a bound, and not part of the verify path."""
+    import torch
+    n = nbytes // 2
+    bufs = [torch.ones(n, dtype=torch.bfloat16, device="cuda") for _ in range(buffers)]
+    for i in range(2 * buffers):
+        bufs[i % buffers].sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        bufs[i % buffers].sum(dtype=torch.float32)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return {"op": "torch.sum(dtype=float32) over a contiguous bf16 buffer of the call's algorithmic bytes, "
+                  f"{buffers} buffers in rotation, {reps} launches",
+            "bytes": int(n * 2), "us": round(us, 2), "GB/s": round(n * 2 / us / 1e3, 1),
+            "frac": round(n * 2 / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def graph_replay(one_step_verify_calls, n_calls, steps):
     """One step's verify calls (fixed lengths) captured into a HIP graph
     (torch.cuda.CUDAGraph) and replayed: mean call time from HIP events, and
@@ -668,6 +696,10 @@ def main():
     }
     if "graph" in r:
         result["graph_replay"] = r["graph"]
+    if not args.no_extra:
+        lr = library_read(r["alg_bytes_per_call"])
+        lr["verify_call_over_library_read"] = round(r["avg_call_us"] / lr["us"], 3)
+        result["roofline"]["library_read"] = lr
     if not args.no_extra:
         extra = {}
         for name, lay in EXTRA_WORKLOADS:
