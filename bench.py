@@ -241,7 +241,7 @@ def counted_traffic(workload: str):
 
 
 def run_workload(name, layout_override, steps, warmup, split_len, layers, depths_arg,
-                 copy_calibration_mib=0, graph=False, page_len=0):
+                 copy_calibration_mib=0, graph=False, page_len=0, floor=False):
     import torch
     import self_speculative_verify_ripe_amd as rp
     from workloads import device_kv_rows
@@ -436,6 +436,9 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
         "step_working_set_bytes": int(step_set),
         "cache_resident": bool(step_set < LLC_BYTES),
     }
+    if floor and layout == "ripe" and case.dtype == "bf16" and D == 128 and not page_len:
+        res["read_floor"] = read_floor(caches, cache_bytes, seq_len, W, B, Hkv, t_max, split_len,
+                                       res["avg_call_us"])
     if graph:
         res["graph"] = graph_replay(one_step_verify_calls=lambda st: [
             rp.ripe_verify_attn(desc, caches[layer], seq_len, packed_sets[gi], n_rows, 1.0, q, kv_new, out,
@@ -444,6 +447,111 @@ def run_workload(name, layout_override, steps, warmup, split_len, layers, depths
     del caches, q, kv_new, out, lse, ws
     torch.cuda.empty_cache()
     return res
+
+
+def default_split(B, Hkv, t_max):
+    """The library's default split length for a descriptor (its rule, restated)."""
+    if B * Hkv >= 448:
+        return 8192
+    work = B * Hkv * t_max
+    s = max(1024, -(-work // 1024))
+    s = min(s, max(256, -(-work // 448)))
+    s = -(-s // 32) * 32
+    return min(max(s, 256), 8192)
+
+
+def floor_pieces(seq_len, W, B, Hkv, S, n_xcd=8, cus_per_xcd=32):
+    """The deep-plane pieces of one RIPE verify call below depth R in the
+    planner's grid order: each sequence's [0, T - W) cut into near-equal
+    pieces of at most S positions (multiples of 32 but the last), the last
+    one extended by the W window positions (the ring's bytes, read here from
+    the deep plane); the pieces of one (sequence, KV head) on one XCD, the
+    units spread over the XCDs by their steps, largest first, and each XCD's
+    pieces paired largest with smallest on its compute units.  Rows of
+    (b, h, c0, len); len 0 marks an empty grid slot."""
+    units = []
+    for b in range(B):
+        T = int(seq_len[b])
+        Wb = min(W, T)
+        deep = T - Wb
+        cuts = []
+        if deep > 0:
+            n = -(-deep // S)
+            pl = -(-(-(-deep // n)) // 32) * 32
+            cuts = [[c0, min(pl, deep - c0)] for c0 in range(0, deep, pl)]
+        if cuts:
+            cuts[-1][1] += Wb
+        elif T > 0:
+            cuts = [[0, T]]
+        for h in range(Hkv):
+            units.append([(b, h, c0, ln) for c0, ln in cuts])
+    steps = lambda it: -(-it[3] // 32)
+    cost = [sum(steps(i) for i in u) for u in units]
+    load, per_xcd = [0] * n_xcd, [[] for _ in range(n_xcd)]
+    for u in sorted(range(len(units)), key=lambda u: -cost[u]):
+        x = min(range(n_xcd), key=lambda k: load[k])
+        load[x] += cost[u]
+        per_xcd[x] += units[u]
+    rows = max(len(v) for v in per_xcd)
+    grid = [(0, 0, 0, 0)] * (rows * n_xcd)
+    for x in range(n_xcd):
+        v = sorted(per_xcd[x], key=lambda it: -steps(it))
+        nx = len(v)
+        if cus_per_xcd < nx <= 2 * cus_per_xcd:
+            P, Sx = nx - cus_per_xcd, 2 * cus_per_xcd - nx
+            for k in range(P):
+                grid[x + n_xcd * k] = v[Sx + k]
+                grid[x + n_xcd * (cus_per_xcd + k)] = v[nx - 1 - k]
+            for k in range(Sx):
+                grid[x + n_xcd * (P + k)] = v[k]
+        else:
+            for k in range(nx):
+                grid[x + n_xcd * k] = v[k]
+    return np.array(grid, dtype=np.int32)
+
+
+def read_floor(caches, cache_bytes, seq_len, W, B, Hkv, t_max, split_len, call_us, reps=40):
+    """Roofline context: the same byte ranges as one verify call (the deep
+    plane's pieces and window bytes, in the same grid order, two 4-wavefront
+    work-groups per compute unit) read by a kernel that only reads them
+    (measure/read_floor.hip), back to back over the layers' caches."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "self_speculative_verify_ripe_amd", "measure", "libripe_readfloor.so"))
+    lib.ripe_read_floor.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 2
+    lib.ripe_read_floor.restype = ctypes.c_int
+    S = split_len or default_split(B, Hkv, t_max)
+    grid = floor_pieces(seq_len, W, B, Hkv, S)
+    live = grid[:, 3] > 0
+    assert np.all(grid[live, 0] < B) and np.all(grid[live, 1] < Hkv) and np.all(grid[:, 2] >= 0) \
+        and np.all(grid[:, 2] + grid[:, 3] <= t_max), "read-floor pieces outside the cache"
+    items = torch.from_numpy(grid).cuda()
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    lds = 68608  # the bf16 D = 128 verify kernel's LDS per work-group
+    def launch(i):
+        base = caches[i % len(caches)].data_ptr()
+        rc = lib.ripe_read_floor(base, base + cache_bytes // 2, items.data_ptr(), len(grid), Hkv, t_max, 128,
+                                 lds, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ripe_read_floor failed ({rc})")
+    for i in range(2 * len(caches)):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = int(grid[:, 3].astype(np.int64).sum()) * 2 * 128 * 2  # K and V rows, bf16
+    return {"what": "a read-only kernel over the call's deep-plane pieces (window bytes read from the deep plane) "
+                    "in the planner's grid order, with the verify kernel's load pattern, cache policy, "
+                    "work-group shape and LDS footprint; back-to-back launches over the layers' caches",
+            "pieces": int(live.sum()), "split_len": S, "bytes": nbytes, "us": round(us, 2),
+            "GB/s": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "verify_call_over_floor": round(call_us / us, 3)}
 
 
 def library_read(nbytes: int, reps: int = 40, buffers: int = 4):
@@ -659,7 +767,7 @@ def main():
         return
     r = run_workload(args.workload, args.layout, args.steps, args.warmup, args.split_len,
                      args.layers, args.depths, args.copy_calibration, graph=not args.no_extra,
-                     page_len=args.page_len)
+                     page_len=args.page_len, floor=not args.no_extra)
     workload_key = f"{args.workload}-{r['layout']}" if not args.workload.startswith("c5") \
         else args.workload
     traffic = counted_traffic(workload_key) if args.split_len == 0 and args.layers is None \
@@ -700,6 +808,8 @@ def main():
         lr = library_read(r["alg_bytes_per_call"])
         lr["verify_call_over_library_read"] = round(r["avg_call_us"] / lr["us"], 3)
         result["roofline"]["library_read"] = lr
+    if "read_floor" in r:
+        result["roofline"]["read_floor"] = r["read_floor"]
     if not args.no_extra:
         extra = {}
         for name, lay in EXTRA_WORKLOADS:

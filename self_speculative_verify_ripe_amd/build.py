@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libripe.so")
+# bench.py's read-floor context: its own library, never loaded by the binding
+FLOOR_SRC = os.path.join(PKG, "measure", "read_floor.hip")
+FLOOR_LIB = os.path.join(PKG, "measure", "libripe_readfloor.so")
 SOURCES = ("api.hip", "verify.hip", "commit.hip", "accept.hip", "side_stats.hip")
 ARCH = os.environ.get("RIPE_OFFLOAD_ARCH", "gfx950")
 
@@ -26,13 +29,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libripe.so (always recompiles)."""
-    tmp = LIB + ".tmp"
+def _compile(sources, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, "-o", tmp]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += list(sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +44,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libripe.so, and the bench's read-floor
+    library beside it (always recompiles)."""
+    _compile([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    _compile([FLOOR_SRC], FLOOR_LIB, verbose)
     return LIB
 
 
