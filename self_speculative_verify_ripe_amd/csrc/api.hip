@@ -636,6 +636,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
         p.gorig[p.n_grp] = uint16_t(sc.order[g0 + k]);
         ++p.n_grp;
       }
+      for (int k = 0; k < 2; ++k) sr.g01[k] = p.grp[sr.g_begin + std::min(k, gc - 1)];
       const int pbase = p.n_pieces;
       for (int k = 0; k < n_piece; ++k) {
         Piece pc = sc.pieces[k];
@@ -665,7 +666,7 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
             it.part = uint16_t(sr.part0 + unit * n_split + k);
             it.h = uint16_t(h + hh);
             it.cc = uint16_t(cc);
-            it.steps = uint16_t(pr.steps);
+            it.s = uint16_t(p.n_seq);
           }
           Unit& un = cur->u.unit[p.n_units + unit];
           un.part = sr.part0 + unit * n_split;
@@ -699,10 +700,10 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     lp.part_bytes = kWsHeader + int64_t(lp.p.n_wg) * CQ * (D + 2) * 4;
     Item* items = lp.t.item;
     const int n = lp.p.n_wg;
-    // an item's cost: its streamed steps and its draft-row steps
+    // an item's cost: the 32-position steps of its streamed and draft-row runs
     auto cost_of = [&](const Item& it) {
-      int c = it.steps;
-      for (int r = it.r0 + it.n_stream; r < it.r0 + it.n_run; ++r) c += (lp.t.piece[r].len + kStep - 1) / kStep;
+      int c = 0;
+      for (int r = it.r0; r < it.r0 + it.n_run; ++r) c += (lp.t.piece[r].len + kStep - 1) / kStep;
       return c;
     };
     int max_steps = 0;

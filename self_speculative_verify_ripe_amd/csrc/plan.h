@@ -57,6 +57,13 @@ constexpr int64_t kWsHeader = kWsArrive + 8 * int64_t(kMaxItems);  // partials
 // each group's depth (kind 4, one segment per distinct depth).
 enum SegKind { kSegPlane = 0, kSegRing = 1, kSegDraft = 2, kSegParentDeep = 3, kSegParentWin = 4 };
 
+struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
+  int32_t row_start;
+  uint16_t n_rows;
+  uint8_t depth;
+  uint8_t seq;         // launch-local sequence index
+};
+
 struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   int32_t T;           // committed prefix length
   int32_t part0;       // first split partial slot of its units
@@ -76,6 +83,9 @@ struct SeqRec {        // one sequence (or a KV-head range of it) in a launch
   uint16_t nd;         // its rows below the window (read at plane R)
   uint16_t hole;       // oldest ring slots not read (now before the window)
   uint16_t ring_base;  // ring slot of the oldest window position
+  // copies of its first two group records (the rest: VerifyParams::grp), so
+  // that a sequence of at most two groups needs no record load after this one
+  GroupRec g01[2];
 };
 
 // Where the window falls for a sequence with committed length T, ring width
@@ -109,12 +119,7 @@ RIPE_HD inline InFlight in_flight(int layout, int We, int T, int kp) {
   return f;
 }
 
-struct GroupRec {      // one group of a launch (8 bytes), sorted by sequence
-  int32_t row_start;
-  uint16_t n_rows;
-  uint8_t depth;
-  uint8_t seq;         // launch-local sequence index
-};
+
 
 // A run: positions of one segment of one sequence (12 bytes).
 struct Piece {
@@ -129,7 +134,9 @@ struct Piece {
 // One verify work item (12 bytes): runs [r0, r0 + n_stream) streamed from
 // the cache (prefix planes, rings), then runs [r0 + n_stream, r0 + n_run)
 // read from the draft tensors (draft rows, parent rows), for KV head h and
-// query-column chunk cc, written to split partial slot `part`.
+// query-column chunk cc of launch-local sequence s, written to split
+// partial slot `part`.  (s is here so that the sequence record loads beside
+// the first run's, not after it.)
 struct Item {
   uint16_t r0;
   uint8_t n_stream;
@@ -137,7 +144,7 @@ struct Item {
   uint16_t part;
   uint16_t h;
   uint16_t cc;
-  uint16_t steps;      // 32-position steps of its stream runs
+  uint16_t s;          // launch-local sequence (its SeqRec)
 };
 
 // Runs, work items and work-groups of one launch.  wg[] maps each

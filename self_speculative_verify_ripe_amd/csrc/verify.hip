@@ -427,21 +427,22 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   const int cc = it.cc;
   const int r_draft = it.r0 + it.n_stream;  // first draft-row run
   const int r_end = it.r0 + it.n_run;
-  const SeqRec sr = p.seq[tab.piece[it.r0].s];
+  const SeqRec sr = p.seq[it.s];
   const int Wb = min(p.We, sr.T);
 
   // ---- query columns --------------------------------------------------
-  // The group records are read with wave-uniform indices (the first kG
-  // together) and each lane selects its own: a record read with a per-lane
-  // index would be a vector load, and waiting for it waits for every vector
-  // load issued before it.  col_info(cols, ...) finds, for N columns of the
-  // chunk at once, the group (-1 for a padding column), the offset within
-  // the group's columns, the group's first draft row and its depth; a padding
-  // column gets the first group's row_start and depth.
-  constexpr int kG = 4;
+  // The sequence's first two group records come with its sequence record;
+  // any further ones are read with wave-uniform indices.  Each lane selects
+  // its own: a record read with a per-lane index would be a vector load, and
+  // waiting for it waits for every vector load issued before it.
+  // col_info(cols, ...) finds, for N columns of the chunk at once, the group
+  // (-1 for a padding column), the offset within the group's columns, the
+  // group's first draft row and its depth; a padding column gets the first
+  // group's row_start and depth.
+  constexpr int kG = 2;
   GroupRec gr[kG];
 #pragma unroll
-  for (int i = 0; i < kG; ++i) gr[i] = p.grp[sr.g_begin + min(i, sr.g_count - 1)];
+  for (int i = 0; i < kG; ++i) gr[i] = sr.g01[i];
   auto col_info = [&](const auto& col, auto& gi, auto& cofs, auto& crs, auto& dep) {
     constexpr int N = int(std::extent<std::remove_reference_t<decltype(col)>>::value);
 #pragma unroll
