@@ -258,6 +258,7 @@ struct VerifyScratch {
   std::vector<Item> items;
   std::vector<int> cost, by_size;
   std::vector<WgCost> wgs;
+  std::vector<uint16_t> grid;  // grid position -> sorted item (kWgEmpty: none)
   std::vector<int64_t> unit_cost;
   std::vector<int> item_unit, unit_order, unit_xcd;
   std::vector<uint16_t> xcd_items[kXcds];
@@ -730,7 +731,8 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
     const int cus_x = n_cu / kXcds;
     bool fused = n_cu > 0 && n_cu % kXcds == 0 && per_cu == 2;
     for (int s = 0; s < lp.p.n_seq && fused; ++s) fused = lp.p.seq[s].n_split <= kFuseSplits;
-    uint16_t* wg = lp.t.wg;
+    sc.grid.assign(size_t(kMaxItems) + 512, kWgEmpty);
+    uint16_t* wg = sc.grid.data();
     if (fused) {
       const int nu = lp.p.n_units;
       sc.unit_cost.assign(nu, 0);
@@ -795,6 +797,9 @@ static ripe_status_t verify_impl(const ripe_desc_t* desc, const void* cache, con
       }
       lp.p.n_blocks = N;
     }
+    // the items in grid order, so that a work-group's first argument read
+    // is its own item (sc.items holds them sorted, as wg indexes them)
+    for (int j = 0; j < lp.p.n_blocks; ++j) items[j] = wg[j] == kWgEmpty ? Item{} : sc.items[wg[j]];
   }
   sc.key_desc = d;
   sc.key_rows = n_rows;

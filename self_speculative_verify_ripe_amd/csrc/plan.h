@@ -146,6 +146,8 @@ struct Item {
   uint16_t cc;
   uint16_t s;          // launch-local sequence (its SeqRec)
 };
+static_assert(sizeof(Item) == 12 && offsetof(Item, part) == 4 && offsetof(Item, cc) == 8,
+              "the verify kernel reads an item as three 32-bit words");
 
 // Runs, work items and work-groups of one launch.  wg[] maps each
 // work-group of the grid to its item, or to none (kWgEmpty); see the
@@ -154,8 +156,9 @@ constexpr uint16_t kWgEmpty = 0xFFFF;
 
 struct ItemTable {
   Piece piece[kMaxPieces];
-  Item item[kMaxItems];
-  uint16_t wg[kMaxItems + 512];
+  // in grid order: work-group j runs item[j]; an item with no runs marks a
+  // grid position with no work (XCD placement leaves gaps)
+  Item item[kMaxItems + 512];
   // paged caches: prefix-plane piece i starts in page pages[i] (read with the
   // piece itself); a piece spanning pages continues in pages[kMaxPieces +
   // pref[i]], pages[kMaxPieces + pref[i] + 1], ...

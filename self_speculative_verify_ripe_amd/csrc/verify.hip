@@ -417,12 +417,25 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[verify_lds_bytes<T, D, NB>()];
 
   // ---- this work item (host-planned; wave-uniform) ----------------------
-  // the 16-bit entry read through its aligned 32-bit word: a scalar load
-  // (a 16-bit read is a vector load, and the first wait would cover it)
-  const uint32_t wge =
-      (reinterpret_cast<const uint32_t*>(tab.wg)[blockIdx.x >> 1] >> (16 * (blockIdx.x & 1))) & 0xFFFFu;
-  if (wge == kWgEmpty) return;  // a grid position with no item (XCD placement)
-  const Item it = tab.item[wge];
+  // The items are in grid order: the first argument read is this item, as
+  // three 32-bit words (scalar loads; its 16-bit fields read one by one
+  // would be vector loads).
+  Item it;
+  {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&tab.item[blockIdx.x]);
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    // all three before the empty-slot test: sunk below it, the third would
+    // be a dependent read of its own
+    asm volatile("" ::"s"(w0), "s"(w1), "s"(w2));
+    it.r0 = uint16_t(w0);
+    it.n_stream = uint8_t(w0 >> 16);
+    it.n_run = uint8_t(w0 >> 24);
+    it.part = uint16_t(w1);
+    it.h = uint16_t(w1 >> 16);
+    it.cc = uint16_t(w2);
+    it.s = uint16_t(w2 >> 16);
+  }
+  if (it.n_run == 0) return;  // a grid position with no item (XCD placement)
   const int h = it.h;
   const int cc = it.cc;
   const int r_draft = it.r0 + it.n_stream;  // first draft-row run
