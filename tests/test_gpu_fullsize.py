@@ -177,3 +177,23 @@ def test_c5_full_size_sampled(layout):
     sl = case.seq_len.astype(np.int32)
     for r in depths:
         run_and_check(case, desc, cache, oc, case.groups_at(r), sample, sl, f"c5 {layout} r={r}")
+
+
+def test_whole_segment_rule_past_the_longest_piece():
+    """At least 448 (sequence, KV head) pairs keep each segment whole up to the
+    longest piece (8192 positions); longer sequences split into two pieces,
+    so their units merge again (B = 56, Hkv = 8: 448 units; T in [8200,
+    8600]; RIPE at depths 1 and R, DEEPEST at depth 4), sampled sequences
+    against the oracle."""
+    for layout, depths in (("ripe", (1, 8)), ("deepest", (4,))):
+        case = make_case("c5", layout=layout, B=56, T_range=(8200, 8600), R=8, D=64)
+        assert case.B * case.Hkv >= 448
+        t_max = t_max_of(case)
+        desc = bench_desc(case, layout, t_max)
+        sample = {0, int(np.argmax(case.seq_len)), case.B - 1}
+        cache, oc = fill(case, layout, desc, t_max, sample)
+        sl = case.seq_len.astype(np.int32)
+        for r in depths:
+            run_and_check(case, desc, cache, oc, case.groups_at(r), sample, sl, f"whole-segment {layout} r={r}")
+        del cache
+        torch.cuda.empty_cache()
