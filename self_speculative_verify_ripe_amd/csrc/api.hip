@@ -230,7 +230,7 @@ struct LaunchPlan {
 // once they have grown to the call sizes in use).
 struct WgCost {
   int work;        // 32-position steps streamed by the work-group
-  uint16_t entry;  // its ItemTable::wg entry
+  uint16_t entry;  // its index among the sorted items
 };
 
 // Compute units of the current device (0 if the runtime cannot say).

@@ -149,9 +149,10 @@ struct Item {
 static_assert(sizeof(Item) == 12 && offsetof(Item, part) == 4 && offsetof(Item, cc) == 8,
               "the verify kernel reads an item as three 32-bit words");
 
-// Runs, work items and work-groups of one launch.  wg[] maps each
-// work-group of the grid to its item, or to none (kWgEmpty); see the
-// planner for the placement order.
+// Runs, work items and work-groups of one launch.  The items are stored in
+// grid order (work-group j runs item[j]; see the planner for the placement
+// order); the planner marks a grid position with no item kWgEmpty while it
+// places them, and stores it as an item with no runs.
 constexpr uint16_t kWgEmpty = 0xFFFF;
 
 struct ItemTable {
@@ -203,7 +204,7 @@ struct VerifyParams {
   unsigned long long* arrive;  // one arrival word per merge unit (fused merge)
   uint64_t ring_off;     // elements from a region's start to its ring (RIPE)
   int32_t layout, R, We, t_max, H, Hq, G, n_rows, n_seq, n_wg, n_units, n_grp, n_pieces;
-  int32_t n_blocks;      // verify work-groups (entries of ItemTable::wg)
+  int32_t n_blocks;      // verify work-groups (grid-ordered entries of ItemTable::item)
   float scale_log2;      // softmax scale * log2(e)
   SeqRec seq[kMaxSeq];
   GroupRec grp[kMaxGroups];
