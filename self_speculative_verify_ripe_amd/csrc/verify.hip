@@ -767,7 +767,11 @@ void verify_attn_kernel(const VerifyParams p, const ItemTable tab) {
     for (int r = r_draft; r < r_end; ++r) {
       const Piece pc = tab.piece[r];
       const int ns = ceil_div(pc.len, kStep);
-      int st = wave;
+      // a run's first step goes to the last wavefront: the streamed runs
+      // give their steps beyond a multiple of 4 to the first ones.  The start
+      // is the same for every draft run, so a group's result does not depend
+      // on the other groups of its launch.
+      int st = (wave + 1) & (kWaves - 1);
       if (st < ns) {
         int hi[NB];
         run_hi(pc, hi);
